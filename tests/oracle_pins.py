@@ -1,0 +1,332 @@
+"""Pins for the float64 oracle: checks against facts fixed outside the oracle.
+
+Each pin returns the largest error it saw (0 is perfect) and a tolerance, so
+the same pins serve the plain tests and the planted-mistake tests, which
+mutate the oracle and require that some pin fails.
+
+Sources of truth used here, none of which is the oracle's own code path:
+  * closed forms of the definitions (zero weight, one dominant logit, k tied
+    logits, zero-weight gradient);
+  * invariants of softmax, entropy and the tanh cap;
+  * torch float64 library routines on the CPU (logsumexp, cross_entropy with
+    ignore_index and reductions, Categorical.entropy, autograd);
+  * central finite differences of the oracle's forward.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle.flce_oracle as O
+
+TOL_CLOSED = 1e-10
+TOL_LIB = 1e-9
+TOL_FD = 1e-6
+
+
+def _rand_case(seed, N=5, H=6, V=9, wstd=0.7, ignore_rows=(), c=0.0):
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((N, H))
+    w = rng.standard_normal((H, V)) * wstd
+    y = rng.integers(0, V, size=N).astype(np.int64)
+    for r in ignore_rows:
+        y[r] = -100
+    return h, w, y, c
+
+
+# ---------------------------------------------------------------- closed forms
+
+def pin_zero_weight_forward():
+    """W = 0: every logit is 0, so lse = entropy = ln V and logprob = -ln V."""
+    err = 0.0
+    for V in (7, 4096, 32000):
+        h = np.random.default_rng(V).standard_normal((3, 2))
+        w = np.zeros((2, V))
+        y = np.array([0, V - 1, V // 2])
+        out = O.forward(h, w, y)
+        lnV = math.log(V)
+        err = max(err, np.abs(out["lse"] - lnV).max(), np.abs(out["entropy"] - lnV).max(),
+                  np.abs(out["logprob"] + lnV).max())
+    return err, TOL_CLOSED
+
+
+def pin_dominant_logit():
+    """One logit L, the other V-1 at 0: lse = ln(e^L + V - 1),
+    entropy = lse - L e^L / (e^L + V - 1), logprob = L - lse at the label,
+    -lse elsewhere."""
+    err = 0.0
+    for V, L, j in ((11, 3.0, 4), (1000, 9.5, 0), (50, 40.0, 49)):
+        w = np.zeros((1, V))
+        w[0, j] = L
+        h = np.ones((2, 1))
+        y = np.array([j, (j + 1) % V])
+        out = O.forward(h, w, y)
+        den = math.exp(L) + V - 1
+        lse = math.log(den)
+        ent = lse - L * math.exp(L) / den
+        err = max(err, abs(out["lse"][0] - lse) / max(1, lse), abs(out["entropy"][0] - ent),
+                  abs(out["logprob"][0] - (L - lse)), abs(out["logprob"][1] + lse))
+    return err, TOL_CLOSED
+
+
+def pin_k_tied():
+    """k logits at L, the rest 0: lse = ln(k e^L + V - k); entropy tends to
+    ln k as L grows (the exact form is checked)."""
+    err = 0.0
+    for V, k, L in ((20, 3, 2.0), (4096, 17, 60.0), (300, 300, 1.5)):
+        w = np.zeros((1, V))
+        w[0, :k] = L
+        h = np.ones((1, 1))
+        out = O.forward(h, w, np.array([0]))
+        den = k * math.exp(L) + (V - k)
+        lse = math.log(den)
+        ent = lse - k * L * math.exp(L) / den
+        err = max(err, abs(out["lse"][0] - lse) / max(1, lse), abs(out["entropy"][0] - ent))
+        if L >= 60:
+            err = max(err, abs(out["entropy"][0] - math.log(k)))
+    return err, TOL_CLOSED
+
+
+def pin_zero_weight_grads():
+    """W = 0: p = 1/V and z' = S = 0, so the entropy term vanishes,
+    dH = 0 and dW[k, j] = sum_i h_ik g_i ([j == y_i] - 1/V)."""
+    rng = np.random.default_rng(5)
+    N, H, V = 6, 4, 10
+    h = rng.standard_normal((N, H))
+    w = np.zeros((H, V))
+    y = rng.integers(0, V, size=N)
+    y[2] = -100
+    g = rng.standard_normal(N)
+    e = rng.standard_normal(N)
+    dh, dw = O.backward(h, w, y, grad_logprob=g, grad_entropy=e)
+    ref = np.zeros((H, V))
+    for i in range(N):
+        if y[i] == -100:
+            continue
+        t = -np.full(V, 1.0 / V)
+        t[y[i]] += 1.0
+        ref += np.outer(h[i], g[i] * t)
+    return max(np.abs(dh).max(), np.abs(dw - ref).max()), TOL_CLOSED
+
+
+# ---------------------------------------------------------------- invariants
+
+def pin_invariants():
+    """0 <= entropy <= ln V, logprob <= 0, lse >= max z', ignored rows 0."""
+    worst = 0.0
+    for seed, c in ((1, 0.0), (2, 3.0)):
+        h, w, y, _ = _rand_case(seed, N=40, H=16, V=33, wstd=1.5, ignore_rows=(3, 7), c=c)
+        out = O.forward(h, w, y, softcap_c=c)
+        zc = O.softcap(h @ w, c)
+        valid = y != -100
+        lnV = math.log(33)
+        ent = out["entropy"][valid]
+        worst = max(worst, max(0.0, -ent.min()), max(0.0, ent.max() - lnV),
+                    max(0.0, out["logprob"].max()),
+                    max(0.0, (zc.max(axis=1) - out["lse"])[valid].max()),
+                    np.abs(out["lse"][~valid]).max(), np.abs(out["entropy"][~valid]).max(),
+                    np.abs(out["logprob"][~valid]).max())
+    return worst, 1e-12
+
+
+def pin_softcap_bounds():
+    """|z'| < c; the cap is odd; z' ~ z - z^3/(3c^2) for small z; a huge c
+    leaves logits unchanged; large logits saturate lse below c + ln V."""
+    z = np.linspace(-200, 200, 4001)
+    c = 30.0
+    zc = O.softcap(z, c)
+    err = max(0.0, np.abs(zc).max() - c)
+    err = max(err, np.abs(zc + O.softcap(-z, c)).max())
+    zs = np.linspace(-0.3, 0.3, 61)
+    err = max(err, np.abs(O.softcap(zs, c) - (zs - zs ** 3 / (3 * c * c))).max())
+    h, w, y, _ = _rand_case(9, N=4, H=6, V=9, wstd=1.0)
+    a = O.forward(h, w, y, softcap_c=1e6)
+    b = O.forward(h, w, y, softcap_c=0.0)
+    err = max(err, np.abs(a["lse"] - b["lse"]).max(), np.abs(a["entropy"] - b["entropy"]).max())
+    h, w, y, _ = _rand_case(10, N=4, H=6, V=9, wstd=100.0)
+    o = O.forward(h, w, y, softcap_c=2.0)
+    err = max(err, max(0.0, (o["lse"] - (2.0 + math.log(9))).max()))
+    return err, 1e-9
+
+
+def pin_softcap_derivative():
+    """softcap_grad(softcap(z)) equals the central difference of softcap."""
+    z = np.linspace(-90, 90, 721)
+    c, step = 30.0, 1e-5
+    fd = (O.softcap(z + step, c) - O.softcap(z - step, c)) / (2 * step)
+    return np.abs(O.softcap_grad(O.softcap(z, c), c) - fd).max(), 1e-8
+
+
+def pin_mean_empty():
+    """reduction='mean' with every token ignored: means and gradients are 0."""
+    h, w, y, _ = _rand_case(11, N=4)
+    y[:] = -100
+    out = O.forward(h, w, y, reduction="mean")
+    dh, dw = O.backward(h, w, y, reduction="mean", grad_logprob=[1.0], grad_entropy=[1.0])
+    return max(abs(out["logprob_mean"]), abs(out["entropy_mean"]), np.abs(dh).max(),
+               np.abs(dw).max()), 0.0
+
+
+def pin_dz_row_sums():
+    """Without a cap each row of dlogits sums to 0, so each row of dW sums to
+    0 over the vocabulary."""
+    h, w, y, _ = _rand_case(12, N=7, H=5, V=11, ignore_rows=(1,))
+    g = np.random.default_rng(1).standard_normal(7)
+    e = np.random.default_rng(2).standard_normal(7)
+    _, dw = O.backward(h, w, y, grad_logprob=g, grad_entropy=e)
+    return np.abs(dw.sum(axis=1)).max(), 1e-12
+
+
+# ---------------------------------------------------------------- library
+
+def _torch_forward(h, w, y, c, ii=-100):
+    z = torch.as_tensor(h, dtype=torch.float64) @ torch.as_tensor(w, dtype=torch.float64)
+    if c > 0:
+        z = c * torch.tanh(z / c)
+    yt = torch.as_tensor(y)
+    lse = torch.logsumexp(z, dim=-1)
+    lp = -F.cross_entropy(z, yt, ignore_index=ii, reduction="none")
+    ent = torch.distributions.Categorical(logits=z).entropy()
+    return z, lse, lp, ent
+
+
+def pin_library_forward():
+    """lse vs torch.logsumexp, logprob vs -F.cross_entropy (ignore_index,
+    'none' and 'mean'), entropy vs Categorical(logits).entropy()."""
+    err = 0.0
+    for seed, c in ((20, 0.0), (21, 2.5)):
+        h, w, y, _ = _rand_case(seed, N=12, H=8, V=15, wstd=1.2, ignore_rows=(0, 5), c=c)
+        out = O.forward(h, w, y, softcap_c=c, reduction="mean")
+        _, lse, lp, ent = _torch_forward(h, w, y, c)
+        valid = y != -100
+        err = max(err, np.abs(out["lse"][valid] - lse.numpy()[valid]).max(),
+                  np.abs(out["logprob"] - lp.numpy()).max(),
+                  np.abs(out["entropy"][valid] - ent.numpy()[valid]).max())
+        zt = torch.as_tensor(O.softcap(h @ w, c))
+        mean_ce = F.cross_entropy(zt, torch.as_tensor(y), ignore_index=-100, reduction="mean")
+        err = max(err, abs(out["logprob_mean"] + mean_ce.item()),
+                  abs(out["entropy_mean"] - ent.numpy()[valid].mean()))
+    return err, TOL_LIB
+
+
+def pin_library_grads():
+    """Oracle gradients vs torch autograd (float64) of the same objective."""
+    err = 0.0
+    for seed, c, red in ((30, 0.0, "none"), (31, 2.0, "none"), (32, 0.0, "mean"), (33, 3.0, "mean")):
+        h, w, y, _ = _rand_case(seed, N=6, H=5, V=8, wstd=1.0, ignore_rows=(2,), c=c)
+        rng = np.random.default_rng(seed + 100)
+        if red == "none":
+            g = rng.standard_normal(6)
+            e = rng.standard_normal(6)
+        else:
+            g = np.array([0.7])
+            e = np.array([-1.3])
+        ht = torch.tensor(h, requires_grad=True)
+        wt = torch.tensor(w, requires_grad=True)
+        z = ht @ wt
+        if c > 0:
+            z = c * torch.tanh(z / c)
+        yt = torch.as_tensor(y)
+        valid = yt != -100
+        lp = -F.cross_entropy(z, yt, ignore_index=-100, reduction="none")
+        ent = torch.distributions.Categorical(logits=z).entropy() * valid
+        if red == "none":
+            loss = (torch.as_tensor(g) * lp).sum() + (torch.as_tensor(e) * ent).sum()
+        else:
+            n = valid.sum()
+            loss = g[0] * lp.sum() / n + e[0] * ent.sum() / n
+        loss.backward()
+        dh, dw = O.backward(h, w, y, softcap_c=c, reduction=red, grad_logprob=g, grad_entropy=e)
+        scale = max(np.abs(ht.grad.numpy()).max(), np.abs(wt.grad.numpy()).max())
+        err = max(err, np.abs(dh - ht.grad.numpy()).max() / scale,
+                  np.abs(dw - wt.grad.numpy()).max() / scale)
+    return err, TOL_LIB
+
+
+# ---------------------------------------------------------------- finite differences
+
+def _objective(h, w, y, c, red, g, e):
+    out = O.forward(h, w, y, softcap_c=c, reduction=red)
+    if red == "none":
+        return float((g * out["logprob"]).sum() + (e * out["entropy"]).sum())
+    return g[0] * out["logprob_mean"] + e[0] * out["entropy_mean"]
+
+
+def pin_finite_differences():
+    """Central differences (float64, step 1e-6) of the forward objective
+    g.logprob + e.entropy vs the oracle's backward, for none/mean, cap off/on,
+    with an ignored token."""
+    worst = 0.0
+    step = 1e-6
+    for seed, c, red in ((40, 0.0, "none"), (41, 2.0, "none"), (42, 0.0, "mean"), (43, 1.5, "mean")):
+        h, w, y, _ = _rand_case(seed, N=4, H=3, V=6, wstd=1.0, ignore_rows=(1,), c=c)
+        rng = np.random.default_rng(seed + 7)
+        if red == "none":
+            g = rng.standard_normal(4)
+            e = rng.standard_normal(4)
+        else:
+            g = np.array([1.1])
+            e = np.array([-0.8])
+        dh, dw = O.backward(h, w, y, softcap_c=c, reduction=red, grad_logprob=g, grad_entropy=e)
+        fdh = np.zeros_like(h)
+        fdw = np.zeros_like(w)
+        for arr, out in ((h, fdh), (w, fdw)):
+            for idx in np.ndindex(arr.shape):
+                old = arr[idx]
+                arr[idx] = old + step
+                fp = _objective(h, w, y, c, red, g, e)
+                arr[idx] = old - step
+                fm = _objective(h, w, y, c, red, g, e)
+                arr[idx] = old
+                out[idx] = (fp - fm) / (2 * step)
+        scale = max(np.abs(fdh).max(), np.abs(fdw).max())
+        worst = max(worst, np.abs(dh - fdh).max() / scale, np.abs(dw - fdw).max() / scale)
+    return worst, TOL_FD
+
+
+def pin_sampled_helpers():
+    """dhidden_rows / dweight_columns agree with the full backward (they are
+    the same definition restricted to rows / columns)."""
+    h, w, y, _ = _rand_case(50, N=9, H=4, V=13, ignore_rows=(4,), c=2.0)
+    g = np.array([0.9])
+    e = np.array([0.4])
+    dh, dw = O.backward(h, w, y, softcap_c=2.0, reduction="mean", grad_logprob=g, grad_entropy=e)
+    rows = np.array([0, 4, 8])
+    cols = np.array([1, 12])
+    a = O.dhidden_rows(h, w, y, rows, softcap_c=2.0, reduction="mean", grad_logprob=g, grad_entropy=e)
+    b = O.dweight_columns(h, w, y, cols, softcap_c=2.0, reduction="mean", grad_logprob=g,
+                          grad_entropy=e, row_block=4)
+    return max(np.abs(a - dh[rows]).max(), np.abs(b - dw[:, cols]).max()), 1e-12
+
+
+ALL_PINS = [
+    pin_zero_weight_forward,
+    pin_dominant_logit,
+    pin_k_tied,
+    pin_zero_weight_grads,
+    pin_invariants,
+    pin_softcap_bounds,
+    pin_softcap_derivative,
+    pin_mean_empty,
+    pin_dz_row_sums,
+    pin_library_forward,
+    pin_library_grads,
+    pin_finite_differences,
+    pin_sampled_helpers,
+]
+
+
+def failing_pins():
+    """Names of the pins whose error exceeds their tolerance (or that raise)."""
+    bad = []
+    for pin in ALL_PINS:
+        try:
+            err, tol = pin()
+            if not (err <= tol):
+                bad.append(pin.__name__)
+        except Exception:  # a mutated oracle may also break shapes
+            bad.append(pin.__name__)
+    return bad
