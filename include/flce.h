@@ -1,0 +1,160 @@
+/*
+ * flce.h -- fused linear cross-entropy + entropy for the LM output head, on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (all from the pages on fusing the LM head with
+ * cross-entropy and entropy):
+ *
+ *   z   = hidden[N,H] x weight[H,V]                       (logits, never stored)
+ *   z'  = c * tanh(z / c) if softcap c > 0, else z          (Gemma2 cap)
+ *   lse_i     = log sum_j exp(z'_ij)
+ *   logprob_i = z'_{i,y_i} - lse_i                          (minus the cross-entropy)
+ *   entropy_i = lse_i - sum_j p_ij z'_ij,  p_ij = exp(z'_ij - lse_i)
+ *
+ * and the gradients of  sum_i gbar_i logprob_i + ebar_i entropy_i  with respect
+ * to hidden and weight.
+ *
+ * Sources: verl pull request #462 (memory-efficient linear_cross_entropy),
+ * sections "Equivalent compute logic" (the definition above, and that logprobs
+ * are the negated cross-entropy) and "API" (hidden is [num_tokens,
+ * hidden_size], weight is [hidden_size, vocab_size], labels are integer token
+ * ids, a `reduction` argument); Liger-Kernel pull request #551 "[Verl] Add
+ * entropy loss to cross_entropy_loss and fused_linear_cross_entropy_loss"
+ * (Summary: both outputs without materialising the logits; review thread: the
+ * mean divides by the number of non-ignored tokens); Liger-Kernel pull
+ * request #435 "Fix LigerCrossEntropyLoss Reduction Behavior for 'None' Mode"
+ * (Summary: reduction "none" returns the per-example vector; "Why we pass
+ * gradient to output.backward()": a per-element upstream gradient for
+ * non-scalar outputs); Liger-Kernel issue #127 "[feat] FusedLinearCrossEntropy
+ * support for Gemma2" (proposal: an optional softcap applied after the head
+ * matmul; discussion: tanh cap, gradients of hidden and weight by the chain
+ * rule).
+ *
+ * Readings where those pages are silent:
+ *   - A token whose label equals ignore_index gets lse = logprob = entropy = 0
+ *     and no gradient, and is not counted by the mean.
+ *   - reduction MEAN reduces both outputs over the n non-ignored tokens (n = 0
+ *     gives 0); the per-token vectors are written under both reductions.
+ *   - A label that is neither ignore_index nor in [0, V) is treated as ignored
+ *     and counted in the workspace status word (see flce_get_status).
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are HIP device pointers; the caller owns every
+ *     buffer, including the workspace. The library allocates no device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *     device work is enqueued on it; no call synchronises the device except
+ *     flce_get_status and flce_profile_read, which say so.
+ *   - Matrices are dense and row-major. bf16 means IEEE bfloat16 bits (uint16).
+ *   - Alignment: hidden, weight, grad_hidden, grad_weight and the workspace
+ *     must be 16-byte aligned, and H and V must be multiples of 8
+ *     (FLCE_ERR_MISALIGNED otherwise). N, H and V need no other multiple.
+ *   - Argument errors are detected on the host before anything is enqueued;
+ *     then nothing is launched and no output is touched. A failed launch
+ *     returns FLCE_ERR_HIP. No C++ exception crosses this interface.
+ *   - Concurrent calls on different streams need distinct workspaces.
+ */
+#ifndef FLCE_H
+#define FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLCE_OK = 0,
+  FLCE_ERR_NULL_POINTER = 1,      /* a required pointer is NULL */
+  FLCE_ERR_BAD_SHAPE = 2,         /* N < 0, H < 1, V < 1, or a size beyond the limits below */
+  FLCE_ERR_BAD_REDUCTION = 3,     /* reduction not FLCE_REDUCTION_NONE / _MEAN */
+  FLCE_ERR_MISALIGNED = 4,        /* see "Alignment" above */
+  FLCE_ERR_WORKSPACE_TOO_SMALL = 5,
+  FLCE_ERR_BAD_SOFTCAP = 6,       /* softcap is NaN or infinite */
+  FLCE_ERR_HIP = 7,               /* a HIP runtime call or kernel launch failed */
+  FLCE_ERR_INVALID_LABEL = 8      /* reported only by flce_get_status */
+} flce_status_t;
+
+enum { FLCE_REDUCTION_NONE = 0, FLCE_REDUCTION_MEAN = 1 };
+
+/* Size limits: N < 2^31, H <= 2^20, V <= 2^22 (FLCE_ERR_BAD_SHAPE beyond). */
+
+/* Workspace bytes needed by flce_forward (*fwd_bytes) and flce_backward
+ * (*bwd_bytes) for this shape. Host only; either out-pointer may be NULL.
+ * The forward size is about 16 * N * ceil(V/256) bytes (one partial softmax
+ * state per token and 256-wide vocabulary tile). The backward size holds a
+ * bounded bf16 slice of the logit gradient (N x Vc with 2*N*Vc <= 512 MiB
+ * unless Vc is at its floor of 2048 columns; independent of V) and, when that
+ * slice does not cover the whole vocabulary, an fp32 accumulator of N*H*4
+ * bytes. */
+flce_status_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int reduction,
+                                  size_t* fwd_bytes, size_t* bwd_bytes);
+
+/* Forward.
+ *   hidden   device bf16 [N,H]        weight  device bf16 [H,V]
+ *   labels   device int64 [N]         ignore_index: label value that marks a skipped token
+ *   softcap  c > 0 caps logits as c*tanh(z/c); c <= 0 disables the cap
+ *   lse, logprob, entropy   device fp32 [N] outputs (always written).
+ *                           Keep lse and entropy for flce_backward.
+ *   logprob_mean, entropy_mean  device fp32 [1] outputs; required when
+ *                           reduction == FLCE_REDUCTION_MEAN, ignored otherwise.
+ *   workspace  device scratch of at least the forward size from
+ *              flce_workspace_size; its first 256 bytes hold the status word.
+ */
+flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t* labels,
+                           int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                           float softcap, int reduction,
+                           float* lse, float* logprob, float* entropy,
+                           float* logprob_mean, float* entropy_mean,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward: writes grad_hidden = dL/dhidden (device bf16 [N,H]) and
+ * grad_weight = dL/dweight (device bf16 [H,V]) for
+ *   L = sum_i gbar_i logprob_i + ebar_i entropy_i.
+ * hidden, weight, labels, N, H, V, ignore_index, softcap and reduction must be
+ * those of the matching flce_forward; lse and entropy are its outputs.
+ *   reduction NONE: grad_logprob, grad_entropy are device fp32 [N]
+ *                   (gbar_i = grad_logprob[i]).
+ *   reduction MEAN: they are device fp32 [1], the gradients of the two means
+ *                   (gbar_i = grad_logprob[0] / n on non-ignored tokens).
+ * Either gradient pointer may be NULL, meaning zero. Ignored tokens get zero
+ * rows in grad_hidden. The logit gradient is recomputed, not stored by the
+ * forward.
+ */
+flce_status_t flce_backward(const void* hidden, const void* weight, const int64_t* labels,
+                            int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                            float softcap, int reduction,
+                            const float* lse, const float* entropy,
+                            const float* grad_logprob, const float* grad_entropy,
+                            void* grad_hidden, void* grad_weight,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Reads the status word that the last flce_forward / flce_backward on this
+ * workspace left, after synchronising `stream`. *invalid_labels (may be NULL)
+ * receives the number of labels that were neither ignore_index nor in [0, V);
+ * returns FLCE_ERR_INVALID_LABEL if that number is not 0, else FLCE_OK. */
+flce_status_t flce_get_status(const void* workspace, int64_t* invalid_labels, void* stream);
+
+/* Static English text for a status code. */
+const char* flce_status_string(flce_status_t status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int flce_version(void);
+
+/* Measurement hooks. When enabled, every kernel the library launches is
+ * bracketed by a pair of hipEvents recorded on the launch stream; the host
+ * side keeps one table per kernel kind. Host state, not thread-safe; meant for
+ * benchmarks. */
+flce_status_t flce_profile_enable(int enable);
+flce_status_t flce_profile_reset(void);
+/* Number of kernel kinds in the table. */
+int flce_profile_kinds(void);
+/* Synchronises the recorded events, then returns the name, the number of
+ * launches and the summed duration (ms) of kernel kind `kind`. */
+flce_status_t flce_profile_read(int kind, const char** name, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H */

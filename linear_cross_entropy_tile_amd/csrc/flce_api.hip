@@ -1,0 +1,474 @@
+// Host side of libflce: argument checks, the launch plan, the workspace
+// layout, kernel launches and the optional per-kernel event timing.
+// Declarations and their documentation: include/flce.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "flce.h"
+#include "flce_kernels.hpp"
+
+namespace {
+
+using namespace flce;
+
+constexpr size_t kAlign = 256;
+constexpr size_t kHeaderBytes = 256;
+constexpr int64_t kMaxN = ((int64_t)1 << 31) - 1;
+constexpr int64_t kMaxH = (int64_t)1 << 20;   // keeps every 32-bit buffer offset below 2^31
+constexpr int64_t kMaxV = (int64_t)1 << 22;
+constexpr int64_t kMaxVc = (int64_t)1 << 18;
+constexpr int kNumCUs = 256;                              // MI355X
+constexpr size_t kDefaultDBudget = (size_t)512 << 20;     // bytes of the bf16 logit-gradient slice
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---- the plan: every size the kernels and the workspace depend on ----------
+struct Plan {
+  int64_t N, H, V;
+  int TB, VT;          // token blocks, vocabulary tiles (256 wide)
+  int64_t Vc;          // backward chunk capacity (multiple of 256)
+  int nchunks;
+  int HT, VTc;         // hidden tiles, vocabulary tiles per chunk
+  int dw_splits;       // split over tokens of the dW contraction
+  int64_t dw_kper;     // tokens per dW split
+  // forward workspace
+  size_t f_lab, f_part, f_zlab, f_bsum, f_total;
+  // backward workspace
+  size_t b_lab, b_coef, b_D, b_acc, b_part, b_total;
+};
+
+size_t env_size(const char* name, size_t dflt) {
+  const char* s = std::getenv(name);
+  if (s == nullptr || *s == 0) return dflt;
+  char* end = nullptr;
+  const unsigned long long v = std::strtoull(s, &end, 10);
+  return (end != s && v > 0) ? (size_t)v : dflt;
+}
+
+Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
+  Plan p{};
+  p.N = N;
+  p.H = H;
+  p.V = V;
+  p.TB = (int)ceil_div(N, kTile);
+  p.VT = (int)ceil_div(V, kTile);
+  // Backward: vocabulary chunk so the bf16 slice D[N, Vc] stays within budget.
+  // FLCE_D_BUDGET (bytes) overrides the budget, for tests and tuning only; the
+  // 2048-column floor applies to the default budget.
+  const size_t budget = env_size("FLCE_D_BUDGET", 0);
+  const int64_t vfull = (int64_t)p.VT * kTile;
+  const size_t bud = budget > 0 ? budget : kDefaultDBudget;
+  int64_t vc = N > 0 ? (int64_t)(bud / (2 * (size_t)N)) / kTile * kTile : vfull;
+  if (vc < (budget > 0 ? kTile : 2048)) vc = budget > 0 ? kTile : 2048;
+  if (vc > kMaxVc) vc = kMaxVc;
+  if (vc > vfull) vc = vfull;
+  p.Vc = vc;
+  p.nchunks = (int)ceil_div(V, vc);
+  p.HT = (int)ceil_div(H, kTile);
+  p.VTc = (int)(vc / kTile);
+  // dW: split the token reduction when there are too few output tiles.
+  const int64_t tiles = (int64_t)p.HT * p.VTc;
+  int sp = 1;
+  if (tiles < kNumCUs) {
+    sp = (int)(kNumCUs / tiles);
+    const int64_t maxsp = N / 1024;  // keep >= 1024 tokens per split
+    if (sp > maxsp) sp = (int)(maxsp > 1 ? maxsp : 1);
+  }
+  p.dw_splits = sp;
+  p.dw_kper = sp > 1 ? ceil_div(ceil_div(N, sp), kBK) * kBK : (N > 0 ? N : 1);
+  if (sp > 1) p.dw_splits = (int)ceil_div(N, p.dw_kper);
+
+  size_t off = kHeaderBytes;
+  p.f_lab = off;
+  off = align_up(off + 4 * (size_t)N);
+  p.f_part = off;
+  off = align_up(off + 16 * (size_t)p.VT * (size_t)N);
+  p.f_zlab = off;
+  off = align_up(off + 4 * (size_t)N);
+  p.f_bsum = off;
+  off = align_up(off + (reduction == FLCE_REDUCTION_MEAN ? 16 * (size_t)ceil_div(N, 256) : 0));
+  p.f_total = off;
+
+  off = kHeaderBytes;
+  p.b_lab = off;
+  off = align_up(off + 4 * (size_t)N);
+  p.b_coef = off;
+  off = align_up(off + 16 * (size_t)N);
+  p.b_D = off;
+  off = align_up(off + 2 * (size_t)N * (size_t)p.Vc);
+  p.b_acc = off;
+  off = align_up(off + (p.nchunks > 1 ? 4 * (size_t)N * (size_t)H : 0));
+  p.b_part = off;
+  off = align_up(off + (p.dw_splits > 1 ? 4 * (size_t)p.dw_splits * (size_t)H * (size_t)p.Vc : 0));
+  p.b_total = off;
+  return p;
+}
+
+flce_status_t check_shape(int64_t N, int64_t H, int64_t V) {
+  if (N < 0 || H < 1 || V < 1) return FLCE_ERR_BAD_SHAPE;
+  if (N > kMaxN || H > kMaxH || V > kMaxV) return FLCE_ERR_BAD_SHAPE;
+  if (H % 8 != 0 || V % 8 != 0) return FLCE_ERR_MISALIGNED;
+  return FLCE_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---- kernel timing hooks --------------------------------------------------------
+enum Kind {
+  K_FWD_PREP, K_FWD_TILE, K_FWD_COMBINE, K_FWD_MEAN, K_BWD_PREP, K_BWD_DLOGITS, K_BWD_DX,
+  K_BWD_DW, K_DW_REDUCE, K_FILL, K_NUM
+};
+const char* kKindNames[K_NUM] = {"fwd_prep", "fwd_tile", "fwd_combine", "fwd_mean", "bwd_prep",
+                                 "bwd_dlogits", "bwd_dx", "bwd_dw", "dw_reduce", "fill_zero"};
+
+struct Pending {
+  int kind;
+  hipEvent_t a, b;
+};
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;
+  int64_t launches[K_NUM] = {};
+  double ms[K_NUM] = {};
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  void drain() {
+    for (auto& p : pending) {
+      float t = 0.f;
+      if (hipEventSynchronize(p.b) == hipSuccess && hipEventElapsedTime(&t, p.a, p.b) == hipSuccess) {
+        launches[p.kind] += 1;
+        ms[p.kind] += t;
+      }
+      pool.push_back(p.a);
+      pool.push_back(p.b);
+    }
+    pending.clear();
+  }
+};
+Profiler& prof() {
+  static Profiler* p = new Profiler();
+  return *p;
+}
+
+// Launches through `fn` on `st`, bracketed by events when timing is on.
+template <class F>
+flce_status_t launch(int kind, hipStream_t st, F fn) {
+  Profiler& P = prof();
+  hipEvent_t a = nullptr, b = nullptr;
+  const bool timed = P.on;
+  if (timed) {
+    std::lock_guard<std::mutex> g(P.mu);
+    a = P.get();
+    b = P.get();
+    if (a != nullptr) (void)hipEventRecord(a, st);
+  }
+  fn();
+  if (hipGetLastError() != hipSuccess) return FLCE_ERR_HIP;
+  if (timed && a != nullptr && b != nullptr) {
+    (void)hipEventRecord(b, st);
+    std::lock_guard<std::mutex> g(P.mu);
+    P.pending.push_back({kind, a, b});
+  }
+  return FLCE_OK;
+}
+
+#define FLCE_TRY(x)                    \
+  do {                                 \
+    const flce_status_t _s = (x);      \
+    if (_s != FLCE_OK) return _s;      \
+  } while (0)
+
+char* wsp(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+flce_status_t zero_fill(void* p, size_t bytes, hipStream_t st) {
+  const int64_t n32 = (int64_t)(bytes / 4);
+  if (n32 == 0) return FLCE_OK;
+  const int blocks = (int)(n32 / 256 + 1 < 4096 ? n32 / 256 + 1 : 4096);
+  return launch(K_FILL, st, [&] {
+    fill_zero_kernel<<<blocks, 256, 0, st>>>(static_cast<uint32_t*>(p), n32);
+  });
+}
+
+}  // namespace
+
+extern "C" {
+
+flce_status_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int reduction,
+                                  size_t* fwd_bytes, size_t* bwd_bytes) {
+  FLCE_TRY(check_shape(N, H, V));
+  if (reduction != FLCE_REDUCTION_NONE && reduction != FLCE_REDUCTION_MEAN)
+    return FLCE_ERR_BAD_REDUCTION;
+  const Plan p = make_plan(N, H, V, reduction);
+  if (fwd_bytes) *fwd_bytes = p.f_total;
+  if (bwd_bytes) *bwd_bytes = p.b_total;
+  return FLCE_OK;
+}
+
+flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t* labels,
+                           int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                           float softcap, int reduction, float* lse, float* logprob,
+                           float* entropy, float* logprob_mean, float* entropy_mean,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  FLCE_TRY(check_shape(N, H, V));
+  if (reduction != FLCE_REDUCTION_NONE && reduction != FLCE_REDUCTION_MEAN)
+    return FLCE_ERR_BAD_REDUCTION;
+  if (!std::isfinite(softcap)) return FLCE_ERR_BAD_SOFTCAP;
+  const bool mean = reduction == FLCE_REDUCTION_MEAN;
+  if (workspace == nullptr) return FLCE_ERR_NULL_POINTER;
+  if (mean && (logprob_mean == nullptr || entropy_mean == nullptr)) return FLCE_ERR_NULL_POINTER;
+  if (N > 0 && (hidden == nullptr || weight == nullptr || labels == nullptr || lse == nullptr ||
+                logprob == nullptr || entropy == nullptr))
+    return FLCE_ERR_NULL_POINTER;
+  if (!aligned16(hidden) || !aligned16(weight) || !aligned16(workspace)) return FLCE_ERR_MISALIGNED;
+  const Plan p = make_plan(N, H, V, reduction);
+  if (workspace_bytes < p.f_total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  int32_t* header = reinterpret_cast<int32_t*>(workspace);
+  int32_t* lab32 = reinterpret_cast<int32_t*>(wsp(workspace, p.f_lab));
+  float4* part = reinterpret_cast<float4*>(wsp(workspace, p.f_part));
+  float* zlab = reinterpret_cast<float*>(wsp(workspace, p.f_zlab));
+  double2* bsum = mean ? reinterpret_cast<double2*>(wsp(workspace, p.f_bsum)) : nullptr;
+
+  FLCE_TRY(launch(K_FWD_PREP, st, [&] {
+    fwd_prep_kernel<<<1, 1024, 0, st>>>(labels, N, V, ignore_index, lab32, header);
+  }));
+  if (N > 0) {
+    FwdTileArgs a{};
+    a.hidden = static_cast<const uint16_t*>(hidden);
+    a.weight = static_cast<const uint16_t*>(weight);
+    a.lab = lab32;
+    a.N = N;
+    a.H = H;
+    a.V = V;
+    a.VT = p.VT;
+    a.TB = p.TB;
+    a.cap = softcap > 0.f ? softcap : 0.f;
+    a.cap_k = softcap > 0.f ? 2.f * kLog2e / softcap : 0.f;
+    a.part = part;
+    a.zlab = zlab;
+    const int grid = p.TB * p.VT;
+    FLCE_TRY(launch(K_FWD_TILE, st, [&] {
+      if (softcap > 0.f)
+        fwd_tile_kernel<true><<<grid, kThreads, 0, st>>>(a);
+      else
+        fwd_tile_kernel<false><<<grid, kThreads, 0, st>>>(a);
+    }));
+    const int nb = (int)ceil_div(N, 256);
+    FLCE_TRY(launch(K_FWD_COMBINE, st, [&] {
+      fwd_combine_kernel<<<nb, 256, 0, st>>>(part, p.VT, zlab, lab32, N, lse, logprob, entropy,
+                                             bsum);
+    }));
+  }
+  if (mean) {
+    const int nb = (int)ceil_div(N, 256);
+    FLCE_TRY(launch(K_FWD_MEAN, st, [&] {
+      fwd_mean_kernel<<<1, 256, 0, st>>>(bsum, nb, header, logprob_mean, entropy_mean);
+    }));
+  }
+  return FLCE_OK;
+}
+
+flce_status_t flce_backward(const void* hidden, const void* weight, const int64_t* labels,
+                            int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                            float softcap, int reduction, const float* lse,
+                            const float* entropy, const float* grad_logprob,
+                            const float* grad_entropy, void* grad_hidden, void* grad_weight,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  FLCE_TRY(check_shape(N, H, V));
+  if (reduction != FLCE_REDUCTION_NONE && reduction != FLCE_REDUCTION_MEAN)
+    return FLCE_ERR_BAD_REDUCTION;
+  if (!std::isfinite(softcap)) return FLCE_ERR_BAD_SOFTCAP;
+  const bool mean = reduction == FLCE_REDUCTION_MEAN;
+  if (workspace == nullptr || weight == nullptr || grad_weight == nullptr)
+    return FLCE_ERR_NULL_POINTER;
+  if (N > 0 && (hidden == nullptr || labels == nullptr || lse == nullptr || entropy == nullptr ||
+                grad_hidden == nullptr))
+    return FLCE_ERR_NULL_POINTER;
+  if (!aligned16(hidden) || !aligned16(weight) || !aligned16(grad_hidden) ||
+      !aligned16(grad_weight) || !aligned16(workspace))
+    return FLCE_ERR_MISALIGNED;
+  const Plan p = make_plan(N, H, V, reduction);
+  if (workspace_bytes < p.b_total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  if (N == 0) return zero_fill(grad_weight, 2 * (size_t)H * (size_t)V, st);
+
+  int32_t* header = reinterpret_cast<int32_t*>(workspace);
+  int32_t* lab32 = reinterpret_cast<int32_t*>(wsp(workspace, p.b_lab));
+  float4* coef = reinterpret_cast<float4*>(wsp(workspace, p.b_coef));
+  uint16_t* D = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_D));
+  float* acc = reinterpret_cast<float*>(wsp(workspace, p.b_acc));
+  float* part = reinterpret_cast<float*>(wsp(workspace, p.b_part));
+
+  FLCE_TRY(launch(K_BWD_PREP, st, [&] {
+    bwd_prep_kernel<<<1, 1024, 0, st>>>(labels, N, V, ignore_index, mean ? 1 : 0, lse, entropy,
+                                        grad_logprob, grad_entropy, coef, lab32, header);
+  }));
+
+  const bool capped = softcap > 0.f;
+  for (int c = 0; c < p.nchunks; ++c) {
+    const int64_t v0 = (int64_t)c * p.Vc;
+    const int64_t vc = V - v0 < p.Vc ? V - v0 : p.Vc;
+    const int vtc = (int)ceil_div(vc, kTile);
+
+    DlogitsArgs d{};
+    d.hidden = static_cast<const uint16_t*>(hidden);
+    d.weight = static_cast<const uint16_t*>(weight);
+    d.coef = coef;
+    d.lab = lab32;
+    d.N = N;
+    d.H = H;
+    d.V = V;
+    d.v0 = v0;
+    d.vc = vc;
+    d.ldd = p.Vc;
+    d.VTc = vtc;
+    d.TB = p.TB;
+    d.cap = capped ? softcap : 0.f;
+    d.cap_k = capped ? 2.f * kLog2e / softcap : 0.f;
+    d.inv_cap = capped ? 1.f / softcap : 0.f;
+    d.D = D;
+    FLCE_TRY(launch(K_BWD_DLOGITS, st, [&] {
+      if (capped)
+        bwd_dlogits_kernel<true><<<vtc * p.TB, kThreads, 0, st>>>(d);
+      else
+        bwd_dlogits_kernel<false><<<vtc * p.TB, kThreads, 0, st>>>(d);
+    }));
+
+    DxArgs x{};
+    x.D = D;
+    x.weight = static_cast<const uint16_t*>(weight);
+    x.N = N;
+    x.H = H;
+    x.V = V;
+    x.v0 = v0;
+    x.vc = vc;
+    x.ldd = p.Vc;
+    x.TB = p.TB;
+    x.HT = p.HT;
+    x.acc = acc;
+    x.gh = static_cast<uint16_t*>(grad_hidden);
+    const int mode =
+        p.nchunks == 1 ? DX_ONLY : (c == 0 ? DX_FIRST : (c == p.nchunks - 1 ? DX_LAST : DX_MID));
+    const int gx = p.TB * p.HT;
+    FLCE_TRY(launch(K_BWD_DX, st, [&] {
+      switch (mode) {
+        case DX_ONLY: bwd_dx_kernel<DX_ONLY><<<gx, kThreads, 0, st>>>(x); break;
+        case DX_FIRST: bwd_dx_kernel<DX_FIRST><<<gx, kThreads, 0, st>>>(x); break;
+        case DX_MID: bwd_dx_kernel<DX_MID><<<gx, kThreads, 0, st>>>(x); break;
+        default: bwd_dx_kernel<DX_LAST><<<gx, kThreads, 0, st>>>(x); break;
+      }
+    }));
+
+    DwArgs w{};
+    w.hidden = static_cast<const uint16_t*>(hidden);
+    w.D = D;
+    w.N = N;
+    w.H = H;
+    w.V = V;
+    w.v0 = v0;
+    w.vc = vc;
+    w.ldd = p.Vc;
+    w.HT = p.HT;
+    w.VTc = vtc;
+    w.splits = p.dw_splits;
+    w.kper = p.dw_kper;
+    w.gw = static_cast<uint16_t*>(grad_weight);
+    w.part = part;
+    const int gw = p.HT * vtc * p.dw_splits;
+    FLCE_TRY(launch(K_BWD_DW, st, [&] {
+      if (p.dw_splits > 1)
+        bwd_dw_kernel<true><<<gw, kThreads, 0, st>>>(w);
+      else
+        bwd_dw_kernel<false><<<gw, kThreads, 0, st>>>(w);
+    }));
+    if (p.dw_splits > 1) {
+      const int64_t n = H * vc;
+      const int blocks = (int)(ceil_div(n, 256) < 8192 ? ceil_div(n, 256) : 8192);
+      FLCE_TRY(launch(K_DW_REDUCE, st, [&] {
+        dw_reduce_kernel<<<blocks, 256, 0, st>>>(part, p.dw_splits, H, vc, p.Vc, V, v0,
+                                                 static_cast<uint16_t*>(grad_weight));
+      }));
+    }
+  }
+  return FLCE_OK;
+}
+
+flce_status_t flce_get_status(const void* workspace, int64_t* invalid_labels, void* stream) {
+  if (workspace == nullptr) return FLCE_ERR_NULL_POINTER;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t h[2] = {0, 0};
+  if (hipMemcpyAsync(h, workspace, sizeof(h), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return FLCE_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return FLCE_ERR_HIP;
+  if (invalid_labels) *invalid_labels = h[0];
+  return h[0] != 0 ? FLCE_ERR_INVALID_LABEL : FLCE_OK;
+}
+
+const char* flce_status_string(flce_status_t s) {
+  switch (s) {
+    case FLCE_OK: return "ok";
+    case FLCE_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case FLCE_ERR_BAD_SHAPE: return "bad shape (need N >= 0, H >= 1, V >= 1 within limits)";
+    case FLCE_ERR_BAD_REDUCTION: return "reduction must be NONE (0) or MEAN (1)";
+    case FLCE_ERR_MISALIGNED: return "pointers must be 16-byte aligned and H, V multiples of 8";
+    case FLCE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than flce_workspace_size";
+    case FLCE_ERR_BAD_SOFTCAP: return "softcap must be finite";
+    case FLCE_ERR_HIP: return "HIP runtime error or failed kernel launch";
+    case FLCE_ERR_INVALID_LABEL: return "labels outside [0, V) that are not ignore_index";
+  }
+  return "unknown status";
+}
+
+int flce_version(void) { return 100; }
+
+flce_status_t flce_profile_enable(int enable) {
+  Profiler& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  P.on = enable != 0;
+  return FLCE_OK;
+}
+
+flce_status_t flce_profile_reset(void) {
+  Profiler& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  P.drain();
+  for (int k = 0; k < K_NUM; ++k) {
+    P.launches[k] = 0;
+    P.ms[k] = 0.0;
+  }
+  return FLCE_OK;
+}
+
+int flce_profile_kinds(void) { return K_NUM; }
+
+flce_status_t flce_profile_read(int kind, const char** name, int64_t* launches, double* total_ms) {
+  if (kind < 0 || kind >= K_NUM) return FLCE_ERR_BAD_SHAPE;
+  Profiler& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  P.drain();
+  if (name) *name = kKindNames[kind];
+  if (launches) *launches = P.launches[kind];
+  if (total_ms) *total_ms = P.ms[kind];
+  return FLCE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,273 @@
+"""ctypes binding for libflce.so (declared in include/flce.h).
+
+Two layers, both argument marshalling only:
+
+* ``flce_workspace_size``, ``flce_forward``, ``flce_backward``,
+  ``flce_get_status``, ... : one Python function per C entry point, same name,
+  same arguments (device pointers and streams as integers). A non-OK status
+  raises ``FlceError``.
+* ``forward`` / ``backward``: take torch CUDA tensors, check dtypes and
+  layouts, allocate outputs and the workspace with torch (so torch's caching
+  allocator owns all memory), and call the C entry points on torch's current
+  stream. No arithmetic of the head happens here.
+
+The library is loaded on first use. There is no fallback: if libflce.so is
+missing or the device is not a GPU, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "FlceError", "lib", "LIB_PATH",
+    "FLCE_REDUCTION_NONE", "FLCE_REDUCTION_MEAN",
+    "flce_workspace_size", "flce_forward", "flce_backward", "flce_get_status",
+    "flce_status_string", "flce_version", "flce_profile_enable", "flce_profile_reset",
+    "flce_profile_kinds", "flce_profile_read", "profile_table",
+    "forward", "backward", "workspace_bytes",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflce.so")
+
+FLCE_REDUCTION_NONE = 0
+FLCE_REDUCTION_MEAN = 1
+_REDUCTIONS = {"none": FLCE_REDUCTION_NONE, "mean": FLCE_REDUCTION_MEAN}
+
+STATUS_NAMES = {
+    0: "FLCE_OK", 1: "FLCE_ERR_NULL_POINTER", 2: "FLCE_ERR_BAD_SHAPE",
+    3: "FLCE_ERR_BAD_REDUCTION", 4: "FLCE_ERR_MISALIGNED",
+    5: "FLCE_ERR_WORKSPACE_TOO_SMALL", 6: "FLCE_ERR_BAD_SOFTCAP", 7: "FLCE_ERR_HIP",
+    8: "FLCE_ERR_INVALID_LABEL",
+}
+
+# Every exported symbol with its (restype, argtypes).
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SIG = {
+    "flce_workspace_size": (ctypes.c_int, [_I64, _I64, _I64, ctypes.c_int,
+                                           ctypes.POINTER(ctypes.c_size_t),
+                                           ctypes.POINTER(ctypes.c_size_t)]),
+    "flce_forward": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
+                                    ctypes.c_int, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "flce_backward": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
+                                     ctypes.c_int, _P, _P, _P, _P, _P, _P, _P,
+                                     ctypes.c_size_t, _P]),
+    "flce_get_status": (ctypes.c_int, [_P, ctypes.POINTER(_I64), _P]),
+    "flce_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "flce_version": (ctypes.c_int, []),
+    "flce_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+    "flce_profile_reset": (ctypes.c_int, []),
+    "flce_profile_kinds": (ctypes.c_int, []),
+    "flce_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                         ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]),
+}
+
+
+class FlceError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = STATUS_NAMES.get(status, str(status))
+        try:
+            text = lib().flce_status_string(status).decode()
+        except Exception:  # pragma: no cover - library itself unavailable
+            text = ""
+        super().__init__(f"{where}: {name} ({text})")
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded libflce.so (loads it on first call)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "or python -m linear_cross_entropy_tile_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIG.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise FlceError(status, where)
+
+
+# ---------------------------------------------------------------- C entry points
+
+def flce_workspace_size(N: int, H: int, V: int, reduction: int):
+    f = ctypes.c_size_t(0)
+    b = ctypes.c_size_t(0)
+    _check(lib().flce_workspace_size(N, H, V, reduction, ctypes.byref(f), ctypes.byref(b)),
+           "flce_workspace_size")
+    return f.value, b.value
+
+
+def flce_forward(hidden, weight, labels, N, H, V, ignore_index, softcap, reduction,
+                 lse, logprob, entropy, logprob_mean, entropy_mean, workspace,
+                 workspace_bytes, stream):
+    _check(lib().flce_forward(hidden, weight, labels, N, H, V, ignore_index, softcap, reduction,
+                              lse, logprob, entropy, logprob_mean, entropy_mean, workspace,
+                              workspace_bytes, stream), "flce_forward")
+
+
+def flce_backward(hidden, weight, labels, N, H, V, ignore_index, softcap, reduction,
+                  lse, entropy, grad_logprob, grad_entropy, grad_hidden, grad_weight,
+                  workspace, workspace_bytes, stream):
+    _check(lib().flce_backward(hidden, weight, labels, N, H, V, ignore_index, softcap,
+                               reduction, lse, entropy, grad_logprob, grad_entropy,
+                               grad_hidden, grad_weight, workspace, workspace_bytes, stream),
+           "flce_backward")
+
+
+def flce_get_status(workspace, stream) -> int:
+    """Number of invalid labels the last call on this workspace saw (syncs)."""
+    n = _I64(0)
+    st = lib().flce_get_status(workspace, ctypes.byref(n), stream)
+    if st not in (0, 8):
+        _check(st, "flce_get_status")
+    return n.value
+
+
+def flce_status_string(status: int) -> str:
+    return lib().flce_status_string(status).decode()
+
+
+def flce_version() -> int:
+    return lib().flce_version()
+
+
+def flce_profile_enable(enable: bool) -> None:
+    _check(lib().flce_profile_enable(1 if enable else 0), "flce_profile_enable")
+
+
+def flce_profile_reset() -> None:
+    _check(lib().flce_profile_reset(), "flce_profile_reset")
+
+
+def flce_profile_kinds() -> int:
+    return lib().flce_profile_kinds()
+
+
+def flce_profile_read(kind: int):
+    name = ctypes.c_char_p()
+    n = _I64(0)
+    ms = ctypes.c_double(0.0)
+    _check(lib().flce_profile_read(kind, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms)),
+           "flce_profile_read")
+    return name.value.decode(), n.value, ms.value
+
+
+def profile_table() -> dict:
+    """{kernel kind: (launches, total ms)} for kinds launched at least once."""
+    out = {}
+    for k in range(flce_profile_kinds()):
+        name, n, ms = flce_profile_read(k)
+        if n:
+            out[name] = (n, ms)
+    return out
+
+
+# ---------------------------------------------------------------- torch marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _require(t, dtype, ndim, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+
+
+def workspace_bytes(N: int, H: int, V: int, reduction: str = "none"):
+    return flce_workspace_size(N, H, V, _REDUCTIONS[reduction])
+
+
+def forward(hidden, weight, labels, ignore_index: int = -100, softcap: float = 0.0,
+            reduction: str = "none", workspace=None) -> dict:
+    """lse, logprob, entropy [N] (fp32) and, under "mean", the two means.
+
+    hidden: bf16 [N,H]; weight: bf16 [H,V]; labels: int64 [N].
+    """
+    torch = _torch()
+    _require(hidden, torch.bfloat16, 2, "hidden")
+    _require(weight, torch.bfloat16, 2, "weight")
+    _require(labels, torch.int64, 1, "labels")
+    N, H = hidden.shape
+    V = weight.shape[1]
+    if weight.shape[0] != H or labels.shape[0] != N:
+        raise ValueError("shape mismatch among hidden [N,H], weight [H,V], labels [N]")
+    red = _REDUCTIONS[reduction]
+    fbytes, _ = flce_workspace_size(N, H, V, red)
+    if workspace is None:
+        workspace = torch.empty(max(fbytes, 256), dtype=torch.uint8, device=hidden.device)
+    dev = hidden.device
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    lp = torch.empty(N, dtype=torch.float32, device=dev)
+    ent = torch.empty(N, dtype=torch.float32, device=dev)
+    out = {"lse": lse, "logprob": lp, "entropy": ent, "workspace": workspace}
+    lpm = entm = None
+    if red == FLCE_REDUCTION_MEAN:
+        lpm = torch.empty(1, dtype=torch.float32, device=dev)
+        entm = torch.empty(1, dtype=torch.float32, device=dev)
+        out["logprob_mean"] = lpm
+        out["entropy_mean"] = entm
+    flce_forward(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), N, H, V,
+                 int(ignore_index), float(softcap), red, lse.data_ptr(), lp.data_ptr(),
+                 ent.data_ptr(), lpm.data_ptr() if lpm is not None else None,
+                 entm.data_ptr() if entm is not None else None, workspace.data_ptr(),
+                 workspace.numel(), _stream())
+    return out
+
+
+def backward(hidden, weight, labels, lse, entropy, grad_logprob=None, grad_entropy=None,
+             ignore_index: int = -100, softcap: float = 0.0, reduction: str = "none",
+             workspace=None):
+    """(grad_hidden bf16 [N,H], grad_weight bf16 [H,V]).
+
+    grad_logprob / grad_entropy: fp32 [N] under "none", fp32 [1] under "mean",
+    or None for zero.
+    """
+    torch = _torch()
+    _require(hidden, torch.bfloat16, 2, "hidden")
+    _require(weight, torch.bfloat16, 2, "weight")
+    _require(labels, torch.int64, 1, "labels")
+    _require(lse, torch.float32, 1, "lse")
+    _require(entropy, torch.float32, 1, "entropy")
+    N, H = hidden.shape
+    V = weight.shape[1]
+    red = _REDUCTIONS[reduction]
+    want = N if red == FLCE_REDUCTION_NONE else 1
+    for g, name in ((grad_logprob, "grad_logprob"), (grad_entropy, "grad_entropy")):
+        if g is not None:
+            _require(g, torch.float32, 1, name)
+            if g.shape[0] != want:
+                raise ValueError(f"{name} must have {want} element(s) under '{reduction}'")
+    _, bbytes = flce_workspace_size(N, H, V, red)
+    if workspace is None or workspace.numel() < bbytes:
+        workspace = torch.empty(max(bbytes, 256), dtype=torch.uint8, device=hidden.device)
+    gh = torch.empty((N, H), dtype=torch.bfloat16, device=hidden.device)
+    gw = torch.empty((H, V), dtype=torch.bfloat16, device=hidden.device)
+    flce_backward(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), N, H, V,
+                  int(ignore_index), float(softcap), red, lse.data_ptr(), entropy.data_ptr(),
+                  grad_logprob.data_ptr() if grad_logprob is not None else None,
+                  grad_entropy.data_ptr() if grad_entropy is not None else None,
+                  gh.data_ptr(), gw.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                  _stream())
+    return gh, gw

@@ -92,6 +92,10 @@ WORKLOADS = {
     "zero_weight": Workload("zero_weight", 200, 256, 3000, seed=204,
                             weight_zero=True, grad_logprob=("normal",),
                             grad_entropy=("normal",)),
+    # Few output tiles of dW and many tokens: the token reduction is split.
+    "dw_split": Workload("dw_split", 4096, 256, 2048, seed=205, weight_std=0.1,
+                         ignore="fraction", ignore_fraction=0.05,
+                         grad_logprob=("normal",), grad_entropy=("normal",)),
 }
 
 

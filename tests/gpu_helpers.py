@@ -1,0 +1,69 @@
+"""Shared helpers of the GPU tests: upload seeded inputs, run the library
+through its C ABI (via the ctypes binding), and compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from linear_cross_entropy_tile_amd import flce, workloads as W
+
+# Tolerances: per-token statistics within 2e-3 absolute or 1e-3 relative;
+# gradients within 1e-2 relative L2 error.
+STAT_ABS = 2e-3
+STAT_REL = 1e-3
+GRAD_REL_L2 = 1e-2
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def upload(x: dict) -> dict:
+    d = dev()
+    out = {
+        "hidden": torch.from_numpy(x["hidden"].view(np.int16)).view(torch.bfloat16).to(d),
+        "weight": torch.from_numpy(x["weight"].view(np.int16)).view(torch.bfloat16).to(d),
+        "labels": torch.from_numpy(x["labels"]).to(d),
+    }
+    for k in ("grad_logprob", "grad_entropy"):
+        out[k] = torch.from_numpy(x[k]).to(d) if x[k] is not None else None
+    return out
+
+
+def run(wl: W.Workload, t: dict, backward: bool = True) -> dict:
+    """Forward (+ backward) through the library; returns CPU numpy arrays."""
+    out = flce.forward(t["hidden"], t["weight"], t["labels"], ignore_index=wl.ignore_index,
+                       softcap=wl.softcap, reduction=wl.reduction)
+    res = {}
+    if backward:
+        gh, gw = flce.backward(t["hidden"], t["weight"], t["labels"], out["lse"], out["entropy"],
+                               t["grad_logprob"], t["grad_entropy"], ignore_index=wl.ignore_index,
+                               softcap=wl.softcap, reduction=wl.reduction)
+        torch.cuda.synchronize()
+        res["grad_hidden"] = gh.float().cpu().numpy()
+        res["grad_weight"] = gw.float().cpu().numpy()
+    torch.cuda.synchronize()
+    for k in ("lse", "logprob", "entropy", "logprob_mean", "entropy_mean"):
+        if k in out:
+            res[k] = out[k].cpu().numpy()
+    res["invalid_labels"] = flce.flce_get_status(out["workspace"].data_ptr(),
+                                                 torch.cuda.current_stream().cuda_stream)
+    return res
+
+
+def stat_err(got, want):
+    """Largest violation ratio of |got - want| <= max(STAT_ABS, STAT_REL |want|)."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    tol = np.maximum(STAT_ABS, STAT_REL * np.abs(want))
+    return float((np.abs(got - want) / tol).max()) if got.size else 0.0
+
+
+def rel_l2(got, want):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    den = np.linalg.norm(want)
+    num = np.linalg.norm(got - want)
+    if den == 0.0:
+        return float(num)
+    return float(num / den)
