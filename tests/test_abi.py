@@ -1,0 +1,122 @@
+"""The C ABI on the CPU: libflce.so loads, exports every function that
+include/flce.h declares, and rejects bad arguments on the host with the
+documented status codes (no device work is involved on these paths)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from linear_cross_entropy_tile_amd import flce
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flce.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flce_[a-z_]+)\s*\(", text)))
+
+
+def _exported():
+    out = subprocess.run(["nm", "-D", "--defined-only", flce.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    return {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+
+
+def test_library_loads():
+    assert flce.flce_version() >= 100
+
+
+def test_exports_match_header():
+    decl = _declared()
+    assert len(decl) >= 10, decl
+    exp = _exported()
+    missing = [d for d in decl if d not in exp]
+    assert not missing, f"declared but not exported: {missing}"
+    extra = sorted(e for e in exp if e.startswith("flce_") and e not in decl)
+    assert not extra, f"exported but not declared: {extra}"
+    assert set(flce._SIG) == set(decl), "binding and header disagree"
+
+
+def test_status_strings():
+    for code in range(9):
+        assert flce.flce_status_string(code)
+    assert "unknown" in flce.flce_status_string(99)
+
+
+# Host-side validation: none of these calls reaches the device. Pointer values
+# are dummies (16-byte aligned) that are never dereferenced.
+A = 0x1000
+BIG = 1 << 40
+
+
+def _fwd(**kw):
+    args = dict(hidden=A, weight=A, labels=A, N=4, H=8, V=8, ii=-100, cap=0.0, red=0,
+                lse=A, lp=A, ent=A, lpm=None, entm=None, ws=A, wsb=BIG, st=None)
+    args.update(kw)
+    return flce.lib().flce_forward(args["hidden"], args["weight"], args["labels"], args["N"],
+                                   args["H"], args["V"], args["ii"], args["cap"], args["red"],
+                                   args["lse"], args["lp"], args["ent"], args["lpm"],
+                                   args["entm"], args["ws"], args["wsb"], args["st"])
+
+
+def _bwd(**kw):
+    args = dict(hidden=A, weight=A, labels=A, N=4, H=8, V=8, ii=-100, cap=0.0, red=0,
+                lse=A, ent=A, g=A, e=A, gh=A, gw=A, ws=A, wsb=BIG, st=None)
+    args.update(kw)
+    return flce.lib().flce_backward(args["hidden"], args["weight"], args["labels"], args["N"],
+                                    args["H"], args["V"], args["ii"], args["cap"], args["red"],
+                                    args["lse"], args["ent"], args["g"], args["e"], args["gh"],
+                                    args["gw"], args["ws"], args["wsb"], args["st"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=None), 1), (dict(weight=None), 1), (dict(labels=None), 1), (dict(lse=None), 1),
+    (dict(ws=None), 1), (dict(red=1), 1),                      # mean needs the mean outputs
+    (dict(N=-1), 2), (dict(H=0), 2), (dict(V=0), 2), (dict(H=(1 << 20) + 8), 2),
+    (dict(V=(1 << 22) + 8), 2),
+    (dict(red=2), 3), (dict(red=-1), 3),
+    (dict(H=12), 4), (dict(V=1001), 4), (dict(hidden=A + 2), 4), (dict(weight=A + 8), 4),
+    (dict(ws=A + 4), 4),
+    (dict(wsb=16), 5),
+    (dict(cap=float("nan")), 6), (dict(cap=float("inf")), 6),
+])
+def test_forward_rejects(kw, code):
+    assert _fwd(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(weight=None), 1), (dict(gw=None), 1), (dict(gh=None), 1), (dict(lse=None), 1),
+    (dict(ent=None), 1), (dict(ws=None), 1),
+    (dict(N=-3), 2), (dict(H=-8), 2),
+    (dict(red=7), 3),
+    (dict(gh=A + 2), 4), (dict(gw=A + 2), 4), (dict(V=12), 4),
+    (dict(wsb=100), 5),
+    (dict(cap=float("-inf")), 6),
+])
+def test_backward_rejects(kw, code):
+    assert _bwd(**kw) == code
+
+
+def test_workspace_size():
+    f, b = flce.flce_workspace_size(8192, 4096, 128256, 0)
+    # 16 B per (token, 256-wide vocabulary tile) of forward partials.
+    assert f >= 16 * 8192 * 501
+    # bounded logit-gradient slice + fp32 dHidden accumulator; far below N*V*2.
+    assert b < 2 * 8192 * 128256 and b >= 8192 * 4096 * 4
+    f1, b1 = flce.flce_workspace_size(0, 64, 64, 1)
+    assert f1 >= 256 and b1 >= 256
+    with pytest.raises(flce.FlceError):
+        flce.flce_workspace_size(4, 7, 8, 0)
+
+
+def test_profile_hooks_host_only():
+    flce.flce_profile_reset()
+    assert flce.flce_profile_kinds() >= 8
+    name, n, ms = flce.flce_profile_read(1)
+    assert name == "fwd_tile" and n == 0 and ms == 0.0
+    with pytest.raises(flce.FlceError):
+        flce.flce_profile_read(99)
