@@ -77,7 +77,7 @@ typedef enum {
 
 enum { FLCE_REDUCTION_NONE = 0, FLCE_REDUCTION_MEAN = 1 };
 
-/* Size limits: N < 2^31, H <= 2^20, V <= 2^22 (FLCE_ERR_BAD_SHAPE beyond). */
+/* Size limits: N <= 2^21, H <= 2^20, V <= 2^22 (FLCE_ERR_BAD_SHAPE beyond). */
 
 /* Workspace bytes needed by flce_forward (*fwd_bytes) and flce_backward
  * (*bwd_bytes) for this shape. Host only; either out-pointer may be NULL.

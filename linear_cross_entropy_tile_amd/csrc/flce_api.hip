@@ -19,8 +19,8 @@ using namespace flce;
 
 constexpr size_t kAlign = 256;
 constexpr size_t kHeaderBytes = 256;
-constexpr int64_t kMaxN = ((int64_t)1 << 31) - 1;
-constexpr int64_t kMaxH = (int64_t)1 << 20;   // keeps every 32-bit buffer offset below 2^31
+constexpr int64_t kMaxN = (int64_t)1 << 21;   // keeps every 32-bit buffer offset below 2^31
+constexpr int64_t kMaxH = (int64_t)1 << 20;
 constexpr int64_t kMaxV = (int64_t)1 << 22;
 constexpr int64_t kMaxVc = (int64_t)1 << 18;
 constexpr int kNumCUs = 256;                              // MI355X
@@ -38,10 +38,11 @@ struct Plan {
   int HT, VTc;         // hidden tiles, vocabulary tiles per chunk
   int dw_splits;       // split over tokens of the dW contraction
   int64_t dw_kper;     // tokens per dW split
+  int64_t ldt;         // row stride of hidden^T and of the logit-gradient slice (N rounded to 8)
   // forward workspace
-  size_t f_lab, f_part, f_zlab, f_bsum, f_total;
+  size_t f_lab, f_part, f_zlab, f_bsum, f_xt, f_total;
   // backward workspace
-  size_t b_lab, b_coef, b_D, b_acc, b_part, b_total;
+  size_t b_lab, b_coef, b_xt, b_D, b_acc, b_part, b_total;
 };
 
 size_t env_size(const char* name, size_t dflt) {
@@ -68,6 +69,10 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   int64_t vc = N > 0 ? (int64_t)(bud / (2 * (size_t)N)) / kTile * kTile : vfull;
   if (vc < (budget > 0 ? kTile : 2048)) vc = budget > 0 ? kTile : 2048;
   if (vc > kMaxVc) vc = kMaxVc;
+  // The slice's byte offsets are 32-bit: 2 * Vc * ldt < 2^31.
+  const int64_t ldt8 = ceil_div(N > 0 ? N : 1, 8) * 8;
+  const int64_t vcap = ((((int64_t)1 << 30) - 1) / ldt8) / kTile * kTile;
+  if (vc > vcap) vc = vcap > kTile ? vcap : kTile;
   if (vc > vfull) vc = vfull;
   p.Vc = vc;
   p.nchunks = (int)ceil_div(V, vc);
@@ -84,6 +89,7 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   p.dw_splits = sp;
   p.dw_kper = sp > 1 ? ceil_div(ceil_div(N, sp), kBK) * kBK : (N > 0 ? N : 1);
   if (sp > 1) p.dw_splits = (int)ceil_div(N, p.dw_kper);
+  p.ldt = ceil_div(N > 0 ? N : 1, 8) * 8;
 
   size_t off = kHeaderBytes;
   p.f_lab = off;
@@ -94,6 +100,8 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   off = align_up(off + 4 * (size_t)N);
   p.f_bsum = off;
   off = align_up(off + (reduction == FLCE_REDUCTION_MEAN ? 16 * (size_t)ceil_div(N, 256) : 0));
+  p.f_xt = off;
+  off = align_up(off + 2 * (size_t)H * (size_t)p.ldt);
   p.f_total = off;
 
   off = kHeaderBytes;
@@ -101,8 +109,10 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   off = align_up(off + 4 * (size_t)N);
   p.b_coef = off;
   off = align_up(off + 16 * (size_t)N);
+  p.b_xt = off;
+  off = align_up(off + 2 * (size_t)H * (size_t)p.ldt);
   p.b_D = off;
-  off = align_up(off + 2 * (size_t)N * (size_t)p.Vc);
+  off = align_up(off + 2 * (size_t)p.ldt * (size_t)p.Vc);
   p.b_acc = off;
   off = align_up(off + (p.nchunks > 1 ? 4 * (size_t)N * (size_t)H : 0));
   p.b_part = off;
@@ -123,10 +133,11 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // ---- kernel timing hooks --------------------------------------------------------
 enum Kind {
   K_FWD_PREP, K_FWD_TILE, K_FWD_COMBINE, K_FWD_MEAN, K_BWD_PREP, K_BWD_DLOGITS, K_BWD_DX,
-  K_BWD_DW, K_DW_REDUCE, K_FILL, K_NUM
+  K_BWD_DW, K_DW_REDUCE, K_FILL, K_TRANSPOSE, K_NUM
 };
 const char* kKindNames[K_NUM] = {"fwd_prep", "fwd_tile", "fwd_combine", "fwd_mean", "bwd_prep",
-                                 "bwd_dlogits", "bwd_dx", "bwd_dw", "dw_reduce", "fill_zero"};
+                                 "bwd_dlogits", "bwd_dx", "bwd_dw", "dw_reduce", "fill_zero",
+                                 "transpose"};
 
 struct Pending {
   int kind;
@@ -206,6 +217,15 @@ flce_status_t zero_fill(void* p, size_t bytes, hipStream_t st) {
   });
 }
 
+// hidden [N,H] -> hidden^T [H, ldt] (zero columns past N).
+flce_status_t transpose_hidden(const void* hidden, const Plan& p, uint16_t* xt, hipStream_t st) {
+  const dim3 grid((unsigned)ceil_div(p.H, 64), (unsigned)ceil_div(p.ldt, 64));
+  return launch(K_TRANSPOSE, st, [&] {
+    transpose_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(hidden), p.N, p.H, p.ldt,
+                                           xt);
+  });
+}
+
 }  // namespace
 
 extern "C" {
@@ -251,13 +271,16 @@ flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t
     fwd_prep_kernel<<<1, 1024, 0, st>>>(labels, N, V, ignore_index, lab32, header);
   }));
   if (N > 0) {
+    uint16_t* xt = reinterpret_cast<uint16_t*>(wsp(workspace, p.f_xt));
+    FLCE_TRY(transpose_hidden(hidden, p, xt, st));
     FwdTileArgs a{};
-    a.hidden = static_cast<const uint16_t*>(hidden);
     a.weight = static_cast<const uint16_t*>(weight);
+    a.xt = xt;
     a.lab = lab32;
     a.N = N;
     a.H = H;
     a.V = V;
+    a.ldt = p.ldt;
     a.VT = p.VT;
     a.TB = p.TB;
     a.cap = softcap > 0.f ? softcap : 0.f;
@@ -314,6 +337,7 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
   int32_t* header = reinterpret_cast<int32_t*>(workspace);
   int32_t* lab32 = reinterpret_cast<int32_t*>(wsp(workspace, p.b_lab));
   float4* coef = reinterpret_cast<float4*>(wsp(workspace, p.b_coef));
+  uint16_t* xt = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_xt));
   uint16_t* D = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_D));
   float* acc = reinterpret_cast<float*>(wsp(workspace, p.b_acc));
   float* part = reinterpret_cast<float*>(wsp(workspace, p.b_part));
@@ -323,6 +347,7 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
                                         grad_logprob, grad_entropy, coef, lab32, header);
   }));
 
+  FLCE_TRY(transpose_hidden(hidden, p, xt, st));
   const bool capped = softcap > 0.f;
   for (int c = 0; c < p.nchunks; ++c) {
     const int64_t v0 = (int64_t)c * p.Vc;
@@ -330,22 +355,22 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
     const int vtc = (int)ceil_div(vc, kTile);
 
     DlogitsArgs d{};
-    d.hidden = static_cast<const uint16_t*>(hidden);
     d.weight = static_cast<const uint16_t*>(weight);
+    d.xt = xt;
     d.coef = coef;
     d.lab = lab32;
     d.N = N;
     d.H = H;
     d.V = V;
+    d.ldt = p.ldt;
     d.v0 = v0;
     d.vc = vc;
-    d.ldd = p.Vc;
     d.VTc = vtc;
     d.TB = p.TB;
     d.cap = capped ? softcap : 0.f;
     d.cap_k = capped ? 2.f * kLog2e / softcap : 0.f;
     d.inv_cap = capped ? 1.f / softcap : 0.f;
-    d.D = D;
+    d.dt = D;
     FLCE_TRY(launch(K_BWD_DLOGITS, st, [&] {
       if (capped)
         bwd_dlogits_kernel<true><<<vtc * p.TB, kThreads, 0, st>>>(d);
@@ -354,14 +379,14 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
     }));
 
     DxArgs x{};
-    x.D = D;
+    x.dt = D;
     x.weight = static_cast<const uint16_t*>(weight);
     x.N = N;
     x.H = H;
     x.V = V;
     x.v0 = v0;
     x.vc = vc;
-    x.ldd = p.Vc;
+    x.ldt = p.ldt;
     x.TB = p.TB;
     x.HT = p.HT;
     x.acc = acc;
@@ -380,13 +405,14 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
 
     DwArgs w{};
     w.hidden = static_cast<const uint16_t*>(hidden);
-    w.D = D;
+    w.dt = D;
     w.N = N;
     w.H = H;
     w.V = V;
     w.v0 = v0;
     w.vc = vc;
-    w.ldd = p.Vc;
+    w.ldt = p.ldt;
+    w.ldp = p.Vc;
     w.HT = p.HT;
     w.VTc = vtc;
     w.splits = p.dw_splits;

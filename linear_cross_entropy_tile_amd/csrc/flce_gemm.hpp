@@ -1,23 +1,29 @@
-// Block-tile bf16 GEMM core for gfx950 (CDNA4), used by every kernel of the
+// Block-tile bf16 GEMM core for gfx950 (CDNA4), shared by every kernel of the
 // fused linear cross-entropy head.
 //
-// A block of 256 threads (4 wave64s, one per SIMD) owns a 256 x 256 output
-// tile C[m][n] = sum_k A[m][k] * B[n][k]. Both operands are staged through LDS
-// in the same K-contiguous layout, 64 K-elements per stage, two stages
-// (128 KiB of LDS). Each wave computes a 128 x 128 sub-tile with
-// v_mfma_f32_32x32x16_bf16 (4 x 4 blocks of 32 x 32, fp32 accumulators).
+// A block of 512 threads (8 wave64s, two per SIMD) owns a 256 x 256 output
+// tile C[m][n] = sum_k A[m][k] * B[n][k], fp32 accumulators. Wave w computes
+// rows [128*(w&1), +128) x cols [64*(w>>1), +64) with
+// v_mfma_f32_32x32x16_bf16 (4 x 2 blocks of 32 x 32, 128 accumulators per
+// lane), so two waves share each SIMD and hide each other's stalls.
 //
-// Operands in global memory come in two layouts:
+// Operands move global -> LDS by direct DMA (buffer_load_dwordx4 ... lds): no
+// staging registers and no LDS store instructions. Four LDS stages of 32 K
+// values (16 KiB per operand each, 128 KiB in all) keep three K slices in
+// flight while one is consumed; every stage is a separate __shared__ array so
+// the compiler can tell a stage being read from the ones being filled.
+//
+// Two global layouts per operand:
 //   KMAJOR  element (r, k) at ptr[r * ld + k]   (K contiguous)
 //   RMAJOR  element (r, k) at ptr[k * ld + r]   (rows contiguous)
-// KMAJOR tiles are copied to LDS as 16-byte chunks. RMAJOR tiles are loaded as
-// 8 x 8 element blocks (eight 16-byte row segments) and transposed in
-// registers before the LDS store, so the MFMA operand reads are always one
-// 16-byte LDS read per lane.
+// KMAJOR stages are stored row-major in LDS and read with ds_read_b128;
+// RMAJOR stages are stored K-row-major and read with the gfx950 transposing
+// read ds_read_b64_tr_b16, which hands each lane 4 consecutive K values of one
+// tile row. Both LDS layouts are XOR-swizzled so the DMA writes and the
+// fragment reads are free of bank conflicts.
 //
-// LDS tile layout: row r (0..255) holds 64 bf16 = eight 16-byte chunks; chunk
-// c is stored at position c ^ (r & 7). Eight consecutive rows reading the same
-// logical chunk therefore touch eight distinct 16-byte bank groups.
+// All global loads go through raw buffer resources: out-of-range offsets
+// (tails in rows and K) read as zero, also into LDS.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,15 +32,21 @@
 namespace flce {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int kTile = 256;                    // M and N extent of a block tile
-constexpr int kBK = 64;                       // K extent of one LDS stage
-constexpr int kThreads = 256;                 // 4 waves of 64
-constexpr int kStageElems = kTile * kBK;      // elements per operand per stage
-constexpr int kLdsElems = 4 * kStageElems;    // 2 stages x 2 operands (128 KiB)
+constexpr int kTile = 256;                          // M and N extent of a block tile
+constexpr int kBK = 32;                             // K per LDS stage
+constexpr int kStages = 4;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStageBytes = kTile * kBK * 2;        // 16 KiB per operand per stage
+constexpr int kDmaBlocks = kStageBytes / 1024 / kWaves;  // 1 KiB DMA blocks per wave
 
 enum { KMAJOR = 0, RMAJOR = 1 };
 
@@ -43,6 +55,8 @@ struct Operand {
   int64_t ld;           // leading dimension, elements
   int64_t rows;         // valid rows; rows >= this read as zero
 };
+
+// ---- block numbering ------------------------------------------------------------
 
 // Hardware dispatches workgroup p to XCD p % 8. Renumber so that logical ids
 // [x*q + min(x,rem), ...) run on XCD x: consecutive logical ids share an XCD
@@ -66,21 +80,13 @@ __device__ __forceinline__ void group_map(int L, int rows, int cols, int g, int&
   c = w / gr;
 }
 
-// ---- global -> registers ---------------------------------------------------
-//
-// Loads go through raw buffer resources: a 32-bit byte offset per lane, and the
-// hardware returns zeros for any offset at or past the resource's size. Tails
-// (rows past `rows`, K past `kend`) are handled that way, with no branches.
+// ---- buffer resources, waits, barriers -------------------------------------------
 
 constexpr uint32_t kOOB = 0x80000000u;  // an offset past every resource's size
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0x7FFFFFFFll ? 0x7FFFFFFFu : (uint32_t)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
-}
-
-__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
@@ -92,178 +98,277 @@ __device__ __forceinline__ void buf_store_u16(uint32_t v, __amdgpu_buffer_rsrc_t
   __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, voff, 0, 0);
 }
 
-// KMAJOR: 2048 chunks of 8 elements per tile; thread t takes row t/8 + 32q,
-// chunk t%8, for q = 0..7. The resource starts at row r0 and ends at `rows`.
-__device__ __forceinline__ void load_kmajor(const Operand& op, int64_t r0, int64_t k0,
-                                            int64_t kend, u32x4_t (&buf)[8]) {
-  const int t = threadIdx.x;
-  const int rowb = t >> 3, kc = t & 7;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(op.ptr + r0 * op.ld, (op.rows - r0) * op.ld * 2);
-  const bool kok = k0 + kc * 8 < kend;
-  const uint32_t base = (uint32_t)((rowb * op.ld + k0 + kc * 8) * 2);
-  const uint32_t step = (uint32_t)(32 * op.ld * 2);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) buf[q] = buf_load16(rs, kok ? base + q * step : kOOB);
+// Keeps the compiler from hoisting work that depends on `x` out of a loop.
+template <class T>
+__device__ __forceinline__ void opaque(T& x) {
+  __asm__ volatile("" : "+v"(x));
 }
 
-// RMAJOR: thread t owns the 8 x 8 block (rows 8*(t>>3).., k 8*(t&7)..). The
-// resource starts at K row k0 and ends at kend. rows must be a multiple of 8
-// so a block is either fully valid or not.
-__device__ __forceinline__ void load_rmajor(const Operand& op, int64_t r0, int64_t k0,
-                                            int64_t kend, u32x4_t (&buf)[8]) {
-  const int t = threadIdx.x;
-  const int rb = t >> 3, kb = t & 7;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(op.ptr + k0 * op.ld, (kend - k0) * op.ld * 2);
-  const bool rok = r0 + rb * 8 < op.rows;
-  const uint32_t base = (uint32_t)(((int64_t)kb * 8 * op.ld + r0 + rb * 8) * 2);
-  const uint32_t step = (uint32_t)(op.ld * 2);
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) buf[kk] = buf_load16(rs, rok ? base + kk * step : kOOB);
+// s_waitcnt on vmcnt only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+}
+// A block barrier that does not drain outstanding global loads (unlike
+// __syncthreads, which waits for every one of them): the stages still in
+// flight stay in flight.
+__device__ __forceinline__ void block_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// ---- LDS layouts of one operand stage (256 tile rows x 32 K) ------------------
+
+// KMAJOR: tile row r is 64 bytes (four 16-byte chunks of 8 K values); chunk c
+// sits at position c ^ ((r >> 2) & 3). Sixteen consecutive rows reading one
+// logical chunk hit sixteen distinct 16-byte bank groups.
+__device__ __forceinline__ int kmaj_byte(int r, int c) {
+  return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+}
+// RMAJOR: K row k is 512 bytes (all 256 tile rows); the 64-byte segment of
+// tile rows [32s, 32s+32) sits at position s ^ (k & 3), so the four K rows a
+// transposing read touches land in four distinct bank groups.
+__device__ __forceinline__ int rmaj_byte(int k, int m) {
+  return k * 512 + ((((m >> 5) ^ (k & 3))) << 6) + (m & 31) * 2;
+}
+
+// ---- global -> LDS DMA of one operand stage -------------------------------------
 
 template <int L>
-__device__ __forceinline__ void load_tile(const Operand& op, int64_t r0, int64_t k0, int64_t kend,
-                                          u32x4_t (&buf)[8]) {
-  if constexpr (L == KMAJOR) load_kmajor(op, r0, k0, kend, buf);
-  else load_rmajor(op, r0, k0, kend, buf);
-}
+struct Dma;
 
-// ---- registers -> LDS --------------------------------------------------------
-
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * kBK + ((chunk ^ (row & 7)) << 3);
-}
-
-__device__ __forceinline__ void store_kmajor(uint16_t* lds, const u32x4_t (&buf)[8]) {
-  const int t = threadIdx.x;
+// KMAJOR: a 1 KiB DMA block is 16 tile rows x 64 bytes; lane l fetches the
+// logical chunk whose swizzled position is l % 4 of row l / 4. The resource
+// starts at the tile's first row and ends at `rows`.
+template <>
+struct Dma<KMAJOR> {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t off[kDmaBlocks];
+  int c8[kDmaBlocks];
+  __device__ __forceinline__ void init(const Operand& op, int64_t r0) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    rs = make_rsrc(op.ptr + r0 * op.ld, (op.rows - r0) * op.ld * 2);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int c = t + q * kThreads;
-    const int row = c >> 3, kc = c & 7;
-    *reinterpret_cast<u32x4_t*>(lds + lds_off(row, kc)) = buf[q];
-  }
-}
-
-// buf[kk] holds rows 8*rb .. 8*rb+7 (two per dword) at k = 8*kb + kk. Row j of
-// the block gets dword q = (k 2q, k 2q+1) = (buf[2q] elem j, buf[2q+1] elem j).
-__device__ __forceinline__ void store_rmajor(uint16_t* lds, const u32x4_t (&buf)[8]) {
-  const int t = threadIdx.x;
-  const int rb = t >> 3, kb = t & 7;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    u32x4_t o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = buf[2 * q][j >> 1];
-      const uint32_t hi = buf[2 * q + 1][j >> 1];
-      o[q] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+    for (int q = 0; q < kDmaBlocks; ++q) {
+      const int r = (w * kDmaBlocks + q) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((r >> 2) & 3);
+      off[q] = (uint32_t)((r * op.ld + c * 8) * 2);
+      c8[q] = c * 8;
     }
-    const int row = rb * 8 + j;
-    *reinterpret_cast<u32x4_t*>(lds + lds_off(row, kb)) = o;
   }
-}
-
-template <int L>
-__device__ __forceinline__ void store_tile(uint16_t* lds, const u32x4_t (&buf)[8]) {
-  if constexpr (L == KMAJOR) store_kmajor(lds, buf);
-  else store_rmajor(lds, buf);
-}
-
-// ---- MFMA on one LDS stage ---------------------------------------------------
-
-// Wave (wm, wn) multiplies rows [wm*128, +128) of A by rows [wn*128, +128) of
-// B over the stage's 64 K values. Operand lane layout of the 32x32x16 MFMA:
-// lane l supplies row l%32 and K elements 8*(l/32) .. +7 of the 16-wide step.
-__device__ __forceinline__ void mma_stage(const uint16_t* sA, const uint16_t* sB, int wm, int wn,
-                                          f32x16_t (&acc)[4][4]) {
-  const int lane = threadIdx.x & 63;
-  const int lr = lane & 31, lh = lane >> 5;
+  __device__ __forceinline__ void issue(char* dst, int64_t k0, int64_t kend) {
+    const int w = threadIdx.x >> 6;
+    const int rem = (int)(kend - k0);
+    const uint32_t kb = (uint32_t)(k0 * 2);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    bf16x8_t a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const bf16x8_t*>(sA + lds_off(wm * 128 + i * 32 + lr, kk * 2 + lh));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const bf16x8_t*>(sB + lds_off(wn * 128 + j * 32 + lr, kk * 2 + lh));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int q = 0; q < kDmaBlocks; ++q) {
+      const uint32_t v = c8[q] < rem ? off[q] + kb : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void_t*)(dst + (w * kDmaBlocks + q) * 1024), 16, v, 0, 0, 0);
+    }
   }
-}
+};
+
+// RMAJOR: a 1 KiB DMA block is 2 K rows x 512 bytes; lane l fetches the
+// 16-byte piece whose swizzled slot is l % 32 of K row l / 32. The resource is
+// rebased to each stage's first K row and ends at kend. `rows` must be a
+// multiple of 8 so an 8-row piece is either fully valid or not.
+template <>
+struct Dma<RMAJOR> {
+  const uint16_t* ptr;
+  int64_t ld;
+  uint32_t off[kDmaBlocks];
+  __device__ __forceinline__ void init(const Operand& op, int64_t r0) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    ptr = op.ptr;
+    ld = op.ld;
+#pragma unroll
+    for (int q = 0; q < kDmaBlocks; ++q) {
+      const int k = (w * kDmaBlocks + q) * 2 + (lane >> 5);
+      const int slot = lane & 31;
+      const int m = (((slot >> 2) ^ (k & 3)) << 5) + (slot & 3) * 8;
+      off[q] = r0 + m < op.rows ? (uint32_t)((k * op.ld + r0 + m) * 2) : kOOB;
+    }
+  }
+  __device__ __forceinline__ void issue(char* dst, int64_t k0, int64_t kend) {
+    const int w = threadIdx.x >> 6;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(ptr + k0 * ld, (kend - k0) * ld * 2);
+#pragma unroll
+    for (int q = 0; q < kDmaBlocks; ++q) {
+      uint32_t v = off[q];
+      opaque(v);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void_t*)(dst + (w * kDmaBlocks + q) * 1024), 16, v, 0, 0, 0);
+    }
+  }
+};
+
+// ---- LDS -> register operand fragments ---------------------------------------------
+
+// NB blocks of 32 tile rows from row0 (a multiple of 32); 16-wide K step kk
+// of a stage. 32x32x16 MFMA lane layout: lane l supplies tile row l % 32 and
+// K values 8*(l/32) .. +7 of the step.
+template <int L, int NB>
+struct FragSrc;
+
+template <int NB>
+struct FragSrc<KMAJOR, NB> {
+  int base[NB];
+  __device__ __forceinline__ void init(int row0) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) base[i] = kmaj_byte(row0 + i * 32 + (lane & 31), lane >> 5);
+  }
+  // Chunk 2kk + l/32: step kk = 1 flips bit 5 of the byte offset.
+  __device__ __forceinline__ void read(const char* st, int kk, bf16x8_t (&f)[NB]) const {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      f[i] = *reinterpret_cast<const bf16x8_t*>(st + (base[i] ^ (kk << 5)));
+  }
+};
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4
+// of the 8 bytes that lane 4j + i/4 addressed, for j = 0..3. Lane a of group g
+// addresses K row 8(g/2) + 4h + a/4 at tile rows 16(g%2) + 4(a%4) .. +3, so
+// lane i ends up with 4 consecutive K values of tile row 16(g%2) + i; the two
+// reads h = 0, 1 give the 8 K values of a 16-wide step.
+template <int NB>
+struct FragSrc<RMAJOR, NB> {
+  int base;
+  __device__ __forceinline__ void init(int row0) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, a = lane & 15;
+    base = rmaj_byte(8 * (g >> 1) + (a >> 2), row0 + 16 * (g & 1) + 4 * (a & 3));
+  }
+  // Block i adds 32i to the row: with row0 / 32 a multiple of NB that is an XOR
+  // of the segment bits; step kk adds 16 K rows.
+  __device__ __forceinline__ void read(const char* st, int kk, bf16x8_t (&f)[NB]) const {
+    int b = base;
+    opaque(b);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int o = (b ^ (i << 6)) + kk * 16 * 512;
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(st + o));
+      const i16x4_t hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(st + o + 4 * 512));
+      const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      f[i] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+};
 
 // Accumulator element r of block (i, j) of wave (wm, wn), lane l, sits at
 // tile row  wm*128 + i*32 + 8*(r/4) + 4*(l/32) + r%4  and
-// tile col  wn*128 + j*32 + l%32.
+// tile col  wn*64 + j*32 + l%32.
 __device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
   return wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 __device__ __forceinline__ int acc_col(int wn, int j, int lane) {
-  return wn * 128 + j * 32 + (lane & 31);
+  return wn * 64 + j * 32 + (lane & 31);
 }
 
-// ---- the pipelined tile loop -------------------------------------------------
+typedef f32x16_t Acc[4][2];
 
-// Runs `ntiles` output tiles back to back, each over K in [kbeg, kend). The
-// last K step of a tile already loads and stages the next tile's first K
-// slice, so the pipeline does not drain between tiles. coord(tile, a_row0,
-// b_row0) names the tile; epi(tile, acc, wm, wn) consumes the accumulators
-// after the tile's last block barrier (it must not touch LDS).
-template <int LA, int LB, class Coord, class Epi>
-__device__ __forceinline__ void gemm_tiles(const Operand& A, const Operand& B, int ntiles,
-                                           Coord coord, int64_t kbeg, int64_t kend, Epi epi,
-                                           uint16_t* lds) {
-  const int nk = (int)((kend - kbeg + kBK - 1) / kBK);
-  if (ntiles <= 0 || nk <= 0) return;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+// LDS for one block: four stages per operand, each a separate array.
+#define FLCE_DECLARE_STAGES(sa, sb)                                                   \
+  __shared__ __attribute__((aligned(1024))) char sa##_0[flce::kStageBytes],            \
+      sa##_1[flce::kStageBytes], sa##_2[flce::kStageBytes], sa##_3[flce::kStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) char sb##_0[flce::kStageBytes],            \
+      sb##_1[flce::kStageBytes], sb##_2[flce::kStageBytes], sb##_3[flce::kStageBytes]; \
+  char* const sa[flce::kStages] = {sa##_0, sa##_1, sa##_2, sa##_3};                    \
+  char* const sb[flce::kStages] = {sb##_0, sb##_1, sb##_2, sb##_3}
 
-  u32x4_t ra[8], rb[8];
-  int64_t ar, br;
-  coord(0, ar, br);
-  load_tile<LA>(A, ar, kbeg, kend, ra);
-  load_tile<LB>(B, br, kbeg, kend, rb);
-  store_tile<LA>(lds, ra);
-  store_tile<LB>(lds + kStageElems, rb);
-  __syncthreads();
+// ---- the pipelined K loop ------------------------------------------------------
 
-  int stage = 0;
-  for (int tile = 0; tile < ntiles; ++tile) {
-    f32x16_t acc[4][4];
+template <int LA, int LB>
+struct Mainloop {
+  struct Frags {
+    bf16x8_t a[4], b[2];
+  };
+  FragSrc<LA, 4> fa;
+  FragSrc<LB, 2> fb;
+  Dma<LA> da;
+  Dma<LB> db;
+
+  __device__ __forceinline__ void frags(const char* a, const char* b, int kk, Frags& f) const {
+    fa.read(a, kk, f.a);
+    fb.read(b, kk, f.b);
+  }
+  __device__ __forceinline__ static void mma(const Frags& f, Acc& acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  }
+
+  // One K slice, reading stage S: first the DMA of the slice three ahead is
+  // issued into the stage consumed last step; sub-step 1's fragments are read
+  // while sub-step 0's MFMAs run; then this wave's DMA of the next slice is
+  // awaited and the block synchronises (the next stage is now complete in
+  // LDS); the next slice's sub-step 0 fragments are read while this slice's
+  // sub-step 1 MFMAs run (they only need registers).
+  template <int S>
+  __device__ __forceinline__ void step(char* const (&sa)[kStages], char* const (&sb)[kStages],
+                                       Frags (&f)[2], Acc& acc, int64_t kiss, int64_t kend) {
+    constexpr int SI = (S + kStages - 1) % kStages;
+    constexpr int SN = (S + 1) % kStages;
+    da.issue(sa[SI], kiss, kend);
+    db.issue(sb[SI], kiss, kend);
+    frags(sa[S], sb[S], 1, f[1]);
+    mma(f[0], acc);
+    wait_vmcnt<2 * kDmaBlocks * (kStages - 2)>();
+    wait_lgkmcnt0();
+    block_barrier();
+    frags(sa[SN], sb[SN], 0, f[0]);
+    mma(f[1], acc);
+  }
+
+  // C tile = A rows [ar, ar+256) x B rows [br, br+256) over K in [kbeg, kend).
+  // Leaves every DMA drained and the block synchronised, so callers may reuse
+  // the stage arrays afterwards.
+  __device__ __forceinline__ void run(char* const (&sa)[kStages], char* const (&sb)[kStages],
+                                      const Operand& A, const Operand& B, int64_t ar, int64_t br,
+                                      int64_t kbeg, int64_t kend, Acc& acc) {
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    for (int kt = 0; kt < nk; ++kt) {
-      const bool last = kt + 1 == nk;
-      const bool more = !last || tile + 1 < ntiles;
-      if (more) {
-        int64_t k0 = kbeg + (int64_t)(kt + 1) * kBK;
-        if (last) {
-          coord(tile + 1, ar, br);
-          k0 = kbeg;
-        }
-        load_tile<LA>(A, ar, k0, kend, ra);
-        load_tile<LB>(B, br, k0, kend, rb);
-      }
-      uint16_t* cur = lds + stage * (2 * kStageElems);
-      uint16_t* nxt = lds + (stage ^ 1) * (2 * kStageElems);
-      mma_stage(cur, cur + kStageElems, wm, wn, acc);
-      if (more) {
-        store_tile<LA>(nxt, ra);
-        store_tile<LB>(nxt + kStageElems, rb);
-      }
-      __syncthreads();
-      stage ^= 1;
+    const int nk = (int)((kend - kbeg + kBK - 1) / kBK);
+    if (nk <= 0) return;
+    da.init(A, ar);
+    db.init(B, br);
+    fa.init(wm * 128);
+    fb.init(wn * 64);
+#pragma unroll
+    for (int s = 0; s + 1 < kStages; ++s) {
+      da.issue(sa[s], kbeg + (int64_t)s * kBK, kend);
+      db.issue(sb[s], kbeg + (int64_t)s * kBK, kend);
     }
-    epi(tile, acc, wm, wn);
+    wait_vmcnt<2 * kDmaBlocks * (kStages - 2)>();
+    block_barrier();
+    Frags f[2];
+    frags(sa[0], sb[0], 0, f[0]);
+    for (int kt = 0; kt < nk; kt += kStages) {
+      const int64_t k3 = kbeg + (int64_t)(kt + kStages - 1) * kBK;
+      step<0>(sa, sb, f, acc, k3, kend);
+      if (kt + 1 < nk) step<1>(sa, sb, f, acc, k3 + kBK, kend);
+      if (kt + 2 < nk) step<2>(sa, sb, f, acc, k3 + 2 * kBK, kend);
+      if (kt + 3 < nk) step<3>(sa, sb, f, acc, k3 + 3 * kBK, kend);
+    }
+    wait_vmcnt<0>();
+    block_barrier();
   }
-}
+};
 
 // ---- small numeric helpers ---------------------------------------------------
 

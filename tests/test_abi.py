@@ -76,7 +76,8 @@ def _bwd(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(hidden=None), 1), (dict(weight=None), 1), (dict(labels=None), 1), (dict(lse=None), 1),
     (dict(ws=None), 1), (dict(red=1), 1),                      # mean needs the mean outputs
-    (dict(N=-1), 2), (dict(H=0), 2), (dict(V=0), 2), (dict(H=(1 << 20) + 8), 2),
+    (dict(N=-1), 2), (dict(N=(1 << 21) + 1), 2), (dict(H=0), 2), (dict(V=0), 2),
+    (dict(H=(1 << 20) + 8), 2),
     (dict(V=(1 << 22) + 8), 2),
     (dict(red=2), 3), (dict(red=-1), 3),
     (dict(H=12), 4), (dict(V=1001), 4), (dict(hidden=A + 2), 4), (dict(weight=A + 8), 4),
