@@ -39,6 +39,7 @@ struct Plan {
   int dw_splits;       // split over tokens of the dW contraction
   int64_t dw_kper;     // tokens per dW split
   int64_t ldt;         // row stride of hidden^T and of the logit-gradient slice (N rounded to 8)
+  int group;           // tile rows per XCD patch of the block -> tile map
   // forward workspace
   size_t f_lab, f_part, f_zlab, f_bsum, f_xt, f_total;
   // backward workspace
@@ -90,6 +91,8 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   p.dw_kper = sp > 1 ? ceil_div(ceil_div(N, sp), kBK) * kBK : (N > 0 ? N : 1);
   if (sp > 1) p.dw_splits = (int)ceil_div(N, p.dw_kper);
   p.ldt = ceil_div(N > 0 ? N : 1, 8) * 8;
+  // FLCE_GROUP overrides the patch height, for tuning only.
+  p.group = (int)env_size("FLCE_GROUP", 4);
 
   size_t off = kHeaderBytes;
   p.f_lab = off;
@@ -283,6 +286,7 @@ flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t
     a.ldt = p.ldt;
     a.VT = p.VT;
     a.TB = p.TB;
+    a.group = p.group;
     a.cap = softcap > 0.f ? softcap : 0.f;
     a.cap_k = softcap > 0.f ? 2.f * kLog2e / softcap : 0.f;
     a.part = part;
@@ -367,6 +371,7 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
     d.vc = vc;
     d.VTc = vtc;
     d.TB = p.TB;
+    d.group = p.group;
     d.cap = capped ? softcap : 0.f;
     d.cap_k = capped ? 2.f * kLog2e / softcap : 0.f;
     d.inv_cap = capped ? 1.f / softcap : 0.f;
@@ -389,6 +394,7 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
     x.ldt = p.ldt;
     x.TB = p.TB;
     x.HT = p.HT;
+    x.group = p.group;
     x.acc = acc;
     x.gh = static_cast<uint16_t*>(grad_hidden);
     const int mode =
@@ -416,6 +422,7 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
     w.HT = p.HT;
     w.VTc = vtc;
     w.splits = p.dw_splits;
+    w.group = p.group;
     w.kper = p.dw_kper;
     w.gw = static_cast<uint16_t*>(grad_weight);
     w.part = part;

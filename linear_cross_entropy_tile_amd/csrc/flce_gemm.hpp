@@ -285,6 +285,28 @@ typedef f32x16_t Acc[4][2];
 
 // ---- the pipelined K loop ------------------------------------------------------
 
+// Instruction-class masks of __builtin_amdgcn_sched_group_barrier.
+enum : int { SG_MFMA = 0x8, SG_VMEM_RD = 0x20, SG_DS_RD = 0x100 };
+
+// Scheduling groups: 8 MFMAs, each followed by its share of NR LDS reads.
+template <int NR, int Q>
+__device__ __forceinline__ void sg_mfma_then_reads() {
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+  if constexpr ((NR + 7 - Q) / 8 > 0)
+    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, (NR + 7 - Q) / 8, 0);
+}
+template <int NR>
+__device__ __forceinline__ void interleave_reads() {
+  sg_mfma_then_reads<NR, 0>();
+  sg_mfma_then_reads<NR, 1>();
+  sg_mfma_then_reads<NR, 2>();
+  sg_mfma_then_reads<NR, 3>();
+  sg_mfma_then_reads<NR, 4>();
+  sg_mfma_then_reads<NR, 5>();
+  sg_mfma_then_reads<NR, 6>();
+  sg_mfma_then_reads<NR, 7>();
+}
+
 template <int LA, int LB>
 struct Mainloop {
   struct Frags {
@@ -313,6 +335,10 @@ struct Mainloop {
   // awaited and the block synchronises (the next stage is now complete in
   // LDS); the next slice's sub-step 0 fragments are read while this slice's
   // sub-step 1 MFMAs run (they only need registers).
+  // LDS fragment-read instructions per 16-wide K step: ds_read_b128 per
+  // K-major block, two ds_read_b64_tr_b16 per row-major block.
+  static constexpr int kReads = (LA == KMAJOR ? 4 : 8) + (LB == KMAJOR ? 2 : 4);
+
   template <int S>
   __device__ __forceinline__ void step(char* const (&sa)[kStages], char* const (&sb)[kStages],
                                        Frags (&f)[2], Acc& acc, int64_t kiss, int64_t kend) {
@@ -322,11 +348,16 @@ struct Mainloop {
     db.issue(sb[SI], kiss, kend);
     frags(sa[S], sb[S], 1, f[1]);
     mma(f[0], acc);
+    // DMA issue first, then the fragment reads spread one or two per MFMA,
+    // so the LDS sees a steady stream rather than a burst per wave.
+    __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 2 * kDmaBlocks, 0);
+    interleave_reads<kReads>();
     wait_vmcnt<2 * kDmaBlocks * (kStages - 2)>();
     wait_lgkmcnt0();
     block_barrier();
     frags(sa[SN], sb[SN], 0, f[0]);
     mma(f[1], acc);
+    interleave_reads<kReads>();
   }
 
   // C tile = A rows [ar, ar+256) x B rows [br, br+256) over K in [kbeg, kend).

@@ -110,6 +110,7 @@ struct FwdTileArgs {
   const int32_t* lab;      // [N], -1 = no label
   int64_t N, H, V, ldt;
   int VT, TB;              // vocabulary tiles, token blocks (256 each)
+  int group;               // token blocks per XCD patch (see group_map)
   float cap, cap_k;        // softcap c and 2*log2(e)/c
   float4* part;            // [VT][N] {m, s, u, 0} per vocabulary tile
   float* zlab;             // [N] capped logit of the label
@@ -138,7 +139,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 fwd_tile_kernel(FwdTileArgs a) {
   FLCE_DECLARE_STAGES(sa, sb);
   int tb, vt;
-  group_map(xcd_remap(blockIdx.x, gridDim.x), a.TB, a.VT, 4, tb, vt);
+  group_map(xcd_remap(blockIdx.x, gridDim.x), a.TB, a.VT, a.group, tb, vt);
   const int lane = threadIdx.x & 63, lh = lane >> 5;
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t n0 = (int64_t)tb * kTile;
@@ -362,6 +363,7 @@ struct DlogitsArgs {
   int64_t v0;              // first vocabulary column of this chunk
   int64_t vc;              // valid columns in this chunk
   int VTc, TB;             // vocabulary tiles in the chunk, token blocks
+  int group;
   float cap, cap_k, inv_cap;
   uint16_t* dt;            // [vc, ldt] bf16 logit gradient of the chunk, vocabulary-major
 };
@@ -374,7 +376,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 bwd_dlogits_kernel(DlogitsArgs a) {
   FLCE_DECLARE_STAGES(sa, sb);
   int tb, vt;
-  group_map(xcd_remap(blockIdx.x, gridDim.x), a.TB, a.VTc, 4, tb, vt);
+  group_map(xcd_remap(blockIdx.x, gridDim.x), a.TB, a.VTc, a.group, tb, vt);
   const int lane = threadIdx.x & 63, lh = lane >> 5;
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t n0 = (int64_t)tb * kTile;
@@ -450,6 +452,7 @@ struct DxArgs {
   const uint16_t* weight;  // [H,V]
   int64_t N, H, V, v0, vc, ldt;
   int TB, HT;              // token blocks, hidden tiles
+  int group;
   float* acc;              // [N,H] fp32 accumulator over chunks
   uint16_t* gh;            // [N,H] bf16 output
 };
@@ -463,7 +466,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 bwd_dx_kernel(DxArgs a) {
   FLCE_DECLARE_STAGES(sa, sb);
   int tb, ht;
-  group_map(xcd_remap(blockIdx.x, gridDim.x), a.TB, a.HT, 4, tb, ht);
+  group_map(xcd_remap(blockIdx.x, gridDim.x), a.TB, a.HT, a.group, tb, ht);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t m0 = (int64_t)tb * kTile, h0 = (int64_t)ht * kTile;
@@ -511,6 +514,7 @@ struct DwArgs {
   const uint16_t* dt;      // [vc, ldt] logit gradient, vocabulary-major
   int64_t N, H, V, v0, vc, ldt;
   int HT, VTc, splits;
+  int group;
   int64_t kper;            // tokens per split (multiple of 32)
   int64_t ldp;             // row stride of the split partials
   uint16_t* gw;            // [H,V] bf16 output
@@ -527,7 +531,7 @@ bwd_dw_kernel(DwArgs a) {
   const int per = a.HT * a.VTc;
   const int sp = L / per;
   int ht, vt;
-  group_map(L - sp * per, a.HT, a.VTc, 4, ht, vt);
+  group_map(L - sp * per, a.HT, a.VTc, a.group, ht, vt);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t h0 = (int64_t)ht * kTile, vl0 = (int64_t)vt * kTile;

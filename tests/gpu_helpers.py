@@ -30,8 +30,9 @@ def upload(x: dict) -> dict:
     return out
 
 
-def run(wl: W.Workload, t: dict, backward: bool = True) -> dict:
-    """Forward (+ backward) through the library; returns CPU numpy arrays."""
+def run(wl: W.Workload, t: dict, backward: bool = True, keep_grads_on_gpu: bool = False) -> dict:
+    """Forward (+ backward) through the library; returns CPU numpy arrays
+    (the gradients stay torch GPU tensors with keep_grads_on_gpu)."""
     out = flce.forward(t["hidden"], t["weight"], t["labels"], ignore_index=wl.ignore_index,
                        softcap=wl.softcap, reduction=wl.reduction)
     res = {}
@@ -40,8 +41,11 @@ def run(wl: W.Workload, t: dict, backward: bool = True) -> dict:
                                t["grad_logprob"], t["grad_entropy"], ignore_index=wl.ignore_index,
                                softcap=wl.softcap, reduction=wl.reduction)
         torch.cuda.synchronize()
-        res["grad_hidden"] = gh.float().cpu().numpy()
-        res["grad_weight"] = gw.float().cpu().numpy()
+        if keep_grads_on_gpu:
+            res["grad_hidden"], res["grad_weight"] = gh, gw
+        else:
+            res["grad_hidden"] = gh.float().cpu().numpy()
+            res["grad_weight"] = gw.float().cpu().numpy()
     torch.cuda.synchronize()
     for k in ("lse", "logprob", "entropy", "logprob_mean", "entropy_mean"):
         if k in out:

@@ -1,0 +1,55 @@
+"""GPU parity at the full workload sizes, through the same entry points and
+launch configuration the benchmark times, against stored float64-oracle
+values (tests/golden/<workload>.npz, written by tests/golden/make_golden.py,
+which calls only the oracle):
+
+  * every token's lse / logprob / entropy (and the means under "mean"),
+  * sampled rows of dHidden and sampled columns of dWeight.
+
+Tolerances: statistics within 2e-3 absolute or 1e-3 relative; gradients
+within 1e-2 relative L2 error over the sampled rows / columns.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_helpers as G
+from linear_cross_entropy_tile_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+FULL = ["llama3_head", "gemma2_softcap", "rl_rollout"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_parity_full_size(name):
+    path = os.path.join(HERE, "golden", f"{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    ref = np.load(path)
+    wl = W.WORKLOADS[name]
+    print(f"[full] {name} N={wl.N} H={wl.H} V={wl.V}", flush=True)
+    x = W.make_inputs(wl)
+    got = G.run(wl, G.upload(x), keep_grads_on_gpu=True)
+    for k in ("lse", "logprob", "entropy"):
+        e = G.stat_err(got[k], ref[k])
+        assert e <= 1.0, f"{name} {k}: error {e:.3f} x tolerance"
+    if wl.reduction == "mean":
+        for k in ("logprob_mean", "entropy_mean"):
+            e = G.stat_err(got[k], ref[k])
+            assert e <= 1.0, f"{name} {k}: error {e:.3f} x tolerance"
+    rows = torch.from_numpy(ref["rows"]).to(G.dev())
+    cols = torch.from_numpy(ref["cols"]).to(G.dev())
+    gh_rows = got["grad_hidden"].index_select(0, rows).float().cpu().numpy()
+    gw_cols = got["grad_weight"].index_select(1, cols).float().cpu().numpy()
+    e = G.rel_l2(gh_rows, ref["dhidden_rows"])
+    assert e <= G.GRAD_REL_L2, f"{name} grad_hidden rows rel L2 {e:.2e}"
+    e = G.rel_l2(gw_cols, ref["dweight_cols"])
+    assert e <= G.GRAD_REL_L2, f"{name} grad_weight cols rel L2 {e:.2e}"
+    ign = torch.from_numpy(x["labels"] == wl.ignore_index).to(G.dev())
+    if bool(ign.any()):
+        assert torch.count_nonzero(got["grad_hidden"][ign]).item() == 0
+    assert got["invalid_labels"] == 0
