@@ -18,10 +18,20 @@ Prints one JSON line. Besides the throughput it reports:
                 materialising implementation needs;
   torch_ref     (optional) a materialising torch implementation of the same
                 forward + backward on the same GPU, for context.
+
+roofline.traffic is the dominant kernel's HBM bytes per launch as measured
+by rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads
+for a plain device copy of known size in the same run), taken from
+profiles/traffic_<workload>.txt; it is null when that file is missing or was
+taken on kernel sources other than the ones built now (a SHA-256 over the
+library's sources is stored with the counters). --copy-calibration-mib runs
+that plain copy once before warmup, for the counter runs.
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import platform
@@ -51,7 +61,43 @@ def parse():
                     help="tokens of the CPU oracle sample (0 skips the CPU baseline)")
     ap.add_argument("--torch-ref", type=int, default=1,
                     help="also time a materialising torch fwd+bwd (0/1)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before warmup "
+                         "(the reference point of the HBM byte counters)")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """SHA-256 over the library's kernel and boundary sources, in a fixed order."""
+    files = sorted(glob.glob(os.path.join(ROOT, "linear_cross_entropy_tile_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "flce.h"))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counted_traffic(workload: str):
+    """Per-kernel HBM bytes per launch from profiles/traffic_<workload>.txt, or
+    None when absent or taken on other sources. Lines of that file:
+      source_sha256 <hex>
+      kernel <kind> fetch_bytes <B> write_bytes <B>"""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    sha, per = None, {}
+    with open(path) as fh:
+        for line in fh:
+            f = line.split()
+            if len(f) >= 2 and f[0] == "source_sha256":
+                sha = f[1]
+            elif len(f) >= 6 and f[0] == "kernel" and f[2] == "fetch_bytes" and f[4] == "write_bytes":
+                per[f[1]] = float(f[3]) + float(f[5])
+    if sha != kernel_source_hash():
+        return None
+    return per
 
 
 def cpu_baseline(wl, x, ntok):
@@ -171,6 +217,16 @@ def main():
                            P["grad_entropy"], gh.data_ptr(), gw.data_ptr(), wsb.data_ptr(),
                            bbytes, stream)
 
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 19   # bf16 elements
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done", flush=True)
+
     # Peak memory of one fused step, everything allocated by torch.
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
@@ -209,6 +265,7 @@ def main():
         kernels[name] = row
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dom]
+    traffic = counted_traffic(wl.name)
     step_tflops = 8.0 * n_valid * H * V / (ms * 1e-3) / 1e12
 
     out = {
@@ -229,7 +286,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": dk.get("tflops"),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": dk.get("mfma_frac"), "traffic": None},
+                     "frac": dk.get("mfma_frac"),
+                     "traffic": (traffic or {}).get(dom)},
         "step_tflops": step_tflops,
         "step_mfma_frac": step_tflops / PEAK_BF16_TFLOPS,
         "kernels": kernels,
