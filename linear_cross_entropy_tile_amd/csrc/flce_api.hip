@@ -19,12 +19,14 @@ using namespace flce;
 
 constexpr size_t kAlign = 256;
 constexpr size_t kHeaderBytes = 256;
-constexpr int64_t kMaxN = (int64_t)1 << 21;   // keeps every 32-bit buffer offset below 2^31
+// Limits keep every 32-bit buffer offset below 2^31: a blocked strip of K
+// values takes K * 512 bytes (K padded to 256 for the vocabulary).
+constexpr int64_t kMaxN = (int64_t)1 << 21;
 constexpr int64_t kMaxH = (int64_t)1 << 20;
-constexpr int64_t kMaxV = (int64_t)1 << 22;
+constexpr int64_t kMaxV = ((int64_t)1 << 22) - 256;
 constexpr int64_t kMaxVc = (int64_t)1 << 18;
 constexpr int kNumCUs = 256;                              // MI355X
-constexpr size_t kDefaultDBudget = (size_t)512 << 20;     // bytes of the bf16 logit-gradient slice
+constexpr size_t kDefaultDBudget = (size_t)1 << 30;       // bytes of both bf16 logit-gradient images
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -32,18 +34,20 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ---- the plan: every size the kernels and the workspace depend on ----------
 struct Plan {
   int64_t N, H, V;
-  int TB, VT;          // token blocks, vocabulary tiles (256 wide)
-  int64_t Vc;          // backward chunk capacity (multiple of 256)
+  int TB, VT, HT;      // token blocks, vocabulary tiles, hidden tiles (256 each)
+  int hkb;             // K blocks of a strip with K = H
+  int nkb;             // K blocks of a strip with K = tokens (TB * 8)
+  int64_t Vc;          // vocabulary chunk capacity (multiple of 256)
+  int kbv;             // Vc / 32
   int nchunks;
-  int HT, VTc;         // hidden tiles, vocabulary tiles per chunk
+  int VTc;             // vocabulary tiles per chunk
   int dw_splits;       // split over tokens of the dW contraction
-  int64_t dw_kper;     // tokens per dW split
-  int64_t ldt;         // row stride of hidden^T and of the logit-gradient slice (N rounded to 8)
+  int dw_kper;         // K blocks per dW split
   int group;           // tile rows per XCD patch of the block -> tile map
   // forward workspace
-  size_t f_lab, f_part, f_zlab, f_bsum, f_xt, f_total;
+  size_t f_lab, f_part, f_zlab, f_bsum, f_wt, f_xb, f_total;
   // backward workspace
-  size_t b_lab, b_coef, b_xt, b_D, b_acc, b_part, b_total;
+  size_t b_lab, b_coef, b_wt, b_wb, b_xb, b_xtb, b_dtv, b_dvt, b_acc, b_part, b_total;
 };
 
 size_t env_size(const char* name, size_t dflt) {
@@ -61,39 +65,40 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   p.V = V;
   p.TB = (int)ceil_div(N, kTile);
   p.VT = (int)ceil_div(V, kTile);
-  // Backward: vocabulary chunk so the bf16 slice D[N, Vc] stays within budget.
-  // FLCE_D_BUDGET (bytes) overrides the budget, for tests and tuning only; the
-  // 2048-column floor applies to the default budget.
+  p.HT = (int)ceil_div(H, kTile);
+  p.hkb = (int)ceil_div(H, kBK);
+  p.nkb = p.TB * (kTile / kBK);
+  // The vocabulary is processed in chunks of Vc columns: the weight images
+  // are built per chunk, and the backward's two bf16 images of the logit
+  // gradient (2 x 2 bytes x 256 TB x Vc) stay within budget. FLCE_D_BUDGET (bytes)
+  // overrides the budget, for tests and tuning only; the 2048-column floor
+  // applies to the default budget.
   const size_t budget = env_size("FLCE_D_BUDGET", 0);
   const int64_t vfull = (int64_t)p.VT * kTile;
   const size_t bud = budget > 0 ? budget : kDefaultDBudget;
-  int64_t vc = N > 0 ? (int64_t)(bud / (2 * (size_t)N)) / kTile * kTile : vfull;
+  const int64_t npad = (int64_t)(p.TB > 0 ? p.TB : 1) * kTile;
+  int64_t vc = (int64_t)(bud / (4 * (size_t)npad)) / kTile * kTile;
   if (vc < (budget > 0 ? kTile : 2048)) vc = budget > 0 ? kTile : 2048;
   if (vc > kMaxVc) vc = kMaxVc;
-  // The slice's byte offsets are 32-bit: 2 * Vc * ldt < 2^31.
-  const int64_t ldt8 = ceil_div(N > 0 ? N : 1, 8) * 8;
-  const int64_t vcap = ((((int64_t)1 << 30) - 1) / ldt8) / kTile * kTile;
-  if (vc > vcap) vc = vcap > kTile ? vcap : kTile;
   if (vc > vfull) vc = vfull;
   p.Vc = vc;
+  p.kbv = (int)(vc / kBK);
   p.nchunks = (int)ceil_div(V, vc);
-  p.HT = (int)ceil_div(H, kTile);
   p.VTc = (int)(vc / kTile);
   // dW: split the token reduction when there are too few output tiles.
   const int64_t tiles = (int64_t)p.HT * p.VTc;
   int sp = 1;
   if (tiles < kNumCUs) {
     sp = (int)(kNumCUs / tiles);
-    const int64_t maxsp = N / 1024;  // keep >= 1024 tokens per split
+    const int64_t maxsp = p.nkb / 32;  // keep >= 1024 tokens per split
     if (sp > maxsp) sp = (int)(maxsp > 1 ? maxsp : 1);
   }
-  p.dw_splits = sp;
-  p.dw_kper = sp > 1 ? ceil_div(ceil_div(N, sp), kBK) * kBK : (N > 0 ? N : 1);
-  if (sp > 1) p.dw_splits = (int)ceil_div(N, p.dw_kper);
-  p.ldt = ceil_div(N > 0 ? N : 1, 8) * 8;
+  p.dw_kper = p.nkb > 0 ? (int)ceil_div(p.nkb, sp) : 1;
+  p.dw_splits = p.nkb > 0 ? (int)ceil_div(p.nkb, p.dw_kper) : 1;
   // FLCE_GROUP overrides the patch height, for tuning only.
   p.group = (int)env_size("FLCE_GROUP", 4);
 
+  const size_t blk = (size_t)kBlockBytes;
   size_t off = kHeaderBytes;
   p.f_lab = off;
   off = align_up(off + 4 * (size_t)N);
@@ -103,8 +108,10 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   off = align_up(off + 4 * (size_t)N);
   p.f_bsum = off;
   off = align_up(off + (reduction == FLCE_REDUCTION_MEAN ? 16 * (size_t)ceil_div(N, 256) : 0));
-  p.f_xt = off;
-  off = align_up(off + 2 * (size_t)H * (size_t)p.ldt);
+  p.f_wt = off;
+  off = align_up(off + blk * (size_t)p.VTc * (size_t)p.hkb);
+  p.f_xb = off;
+  off = align_up(off + blk * (size_t)p.TB * (size_t)p.hkb);
   p.f_total = off;
 
   off = kHeaderBytes;
@@ -112,10 +119,18 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   off = align_up(off + 4 * (size_t)N);
   p.b_coef = off;
   off = align_up(off + 16 * (size_t)N);
-  p.b_xt = off;
-  off = align_up(off + 2 * (size_t)H * (size_t)p.ldt);
-  p.b_D = off;
-  off = align_up(off + 2 * (size_t)p.ldt * (size_t)p.Vc);
+  p.b_wt = off;
+  off = align_up(off + blk * (size_t)p.VTc * (size_t)p.hkb);
+  p.b_wb = off;
+  off = align_up(off + blk * (size_t)p.HT * (size_t)p.kbv);
+  p.b_xb = off;
+  off = align_up(off + blk * (size_t)p.TB * (size_t)p.hkb);
+  p.b_xtb = off;
+  off = align_up(off + blk * (size_t)p.HT * (size_t)p.nkb);
+  p.b_dtv = off;
+  off = align_up(off + blk * (size_t)p.TB * (size_t)p.kbv);
+  p.b_dvt = off;
+  off = align_up(off + blk * (size_t)p.VTc * (size_t)p.nkb);
   p.b_acc = off;
   off = align_up(off + (p.nchunks > 1 ? 4 * (size_t)N * (size_t)H : 0));
   p.b_part = off;
@@ -136,11 +151,11 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // ---- kernel timing hooks --------------------------------------------------------
 enum Kind {
   K_FWD_PREP, K_FWD_TILE, K_FWD_COMBINE, K_FWD_MEAN, K_BWD_PREP, K_BWD_DLOGITS, K_BWD_DX,
-  K_BWD_DW, K_DW_REDUCE, K_FILL, K_TRANSPOSE, K_NUM
+  K_BWD_DW, K_DW_REDUCE, K_FILL, K_PACK_WEIGHT, K_PACK_HIDDEN, K_NUM
 };
 const char* kKindNames[K_NUM] = {"fwd_prep", "fwd_tile", "fwd_combine", "fwd_mean", "bwd_prep",
                                  "bwd_dlogits", "bwd_dx", "bwd_dw", "dw_reduce", "fill_zero",
-                                 "transpose"};
+                                 "pack_weight", "pack_hidden"};
 
 struct Pending {
   int kind;
@@ -220,12 +235,21 @@ flce_status_t zero_fill(void* p, size_t bytes, hipStream_t st) {
   });
 }
 
-// hidden [N,H] -> hidden^T [H, ldt] (zero columns past N).
-flce_status_t transpose_hidden(const void* hidden, const Plan& p, uint16_t* xt, hipStream_t st) {
-  const dim3 grid((unsigned)ceil_div(p.H, 64), (unsigned)ceil_div(p.ldt, 64));
-  return launch(K_TRANSPOSE, st, [&] {
-    transpose_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(hidden), p.N, p.H, p.ldt,
-                                           xt);
+// Blocked image of a K-contiguous source (element (r, k) at src[r * ld + k]).
+flce_status_t pack_rows(int kind, const void* src, int64_t R, int64_t K, int64_t ld, int nkb,
+                        uint16_t* dst, hipStream_t st) {
+  const dim3 grid((unsigned)ceil_div(nkb, 8), (unsigned)ceil_div(R, kTile));
+  return launch(kind, st, [&] {
+    pack_rows_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(src), R, K, ld, nkb, dst);
+  });
+}
+
+// Blocked image of a row-contiguous source (element (r, k) at src[k * ld + r]).
+flce_status_t pack_cols(int kind, const void* src, int64_t R, int64_t K, int64_t ld, int nkb,
+                        uint16_t* dst, hipStream_t st) {
+  const dim3 grid((unsigned)ceil_div(nkb, 2), (unsigned)ceil_div(R, kTile));
+  return launch(kind, st, [&] {
+    pack_cols_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(src), R, K, ld, nkb, dst);
   });
 }
 
@@ -274,16 +298,17 @@ flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t
     fwd_prep_kernel<<<1, 1024, 0, st>>>(labels, N, V, ignore_index, lab32, header);
   }));
   if (N > 0) {
-    uint16_t* xt = reinterpret_cast<uint16_t*>(wsp(workspace, p.f_xt));
-    FLCE_TRY(transpose_hidden(hidden, p, xt, st));
+    uint16_t* wt = reinterpret_cast<uint16_t*>(wsp(workspace, p.f_wt));
+    uint16_t* xb = reinterpret_cast<uint16_t*>(wsp(workspace, p.f_xb));
+    FLCE_TRY(pack_rows(K_PACK_HIDDEN, hidden, N, H, H, p.hkb, xb, st));
     FwdTileArgs a{};
-    a.weight = static_cast<const uint16_t*>(weight);
-    a.xt = xt;
+    a.wt = wt;
+    a.xb = xb;
     a.lab = lab32;
     a.N = N;
     a.H = H;
     a.V = V;
-    a.ldt = p.ldt;
+    a.hkb = p.hkb;
     a.VT = p.VT;
     a.TB = p.TB;
     a.group = p.group;
@@ -291,13 +316,22 @@ flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t
     a.cap_k = softcap > 0.f ? 2.f * kLog2e / softcap : 0.f;
     a.part = part;
     a.zlab = zlab;
-    const int grid = p.TB * p.VT;
-    FLCE_TRY(launch(K_FWD_TILE, st, [&] {
-      if (softcap > 0.f)
-        fwd_tile_kernel<true><<<grid, kThreads, 0, st>>>(a);
-      else
-        fwd_tile_kernel<false><<<grid, kThreads, 0, st>>>(a);
-    }));
+    for (int c = 0; c < p.nchunks; ++c) {
+      const int64_t v0 = (int64_t)c * p.Vc;
+      const int64_t vc = V - v0 < p.Vc ? V - v0 : p.Vc;
+      // weight[:, v0 : v0 + vc] is row-contiguous for the (vocabulary x H) operand.
+      FLCE_TRY(pack_cols(K_PACK_WEIGHT, static_cast<const uint16_t*>(weight) + v0, vc, H, V,
+                         p.hkb, wt, st));
+      a.v0 = v0;
+      a.VTc = (int)ceil_div(vc, kTile);
+      const int grid = p.TB * a.VTc;
+      FLCE_TRY(launch(K_FWD_TILE, st, [&] {
+        if (softcap > 0.f)
+          fwd_tile_kernel<true><<<grid, kThreads, 0, st>>>(a);
+        else
+          fwd_tile_kernel<false><<<grid, kThreads, 0, st>>>(a);
+      }));
+    }
     const int nb = (int)ceil_div(N, 256);
     FLCE_TRY(launch(K_FWD_COMBINE, st, [&] {
       fwd_combine_kernel<<<nb, 256, 0, st>>>(part, p.VT, zlab, lab32, N, lse, logprob, entropy,
@@ -341,8 +375,12 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
   int32_t* header = reinterpret_cast<int32_t*>(workspace);
   int32_t* lab32 = reinterpret_cast<int32_t*>(wsp(workspace, p.b_lab));
   float4* coef = reinterpret_cast<float4*>(wsp(workspace, p.b_coef));
-  uint16_t* xt = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_xt));
-  uint16_t* D = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_D));
+  uint16_t* wt = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_wt));
+  uint16_t* wb = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_wb));
+  uint16_t* xb = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_xb));
+  uint16_t* xtb = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_xtb));
+  uint16_t* dtv = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_dtv));
+  uint16_t* dvt = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_dvt));
   float* acc = reinterpret_cast<float*>(wsp(workspace, p.b_acc));
   float* part = reinterpret_cast<float*>(wsp(workspace, p.b_part));
 
@@ -351,31 +389,40 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
                                         grad_logprob, grad_entropy, coef, lab32, header);
   }));
 
-  FLCE_TRY(transpose_hidden(hidden, p, xt, st));
+  // Operands: weight^T (vocabulary x H) for the recompute, weight (H x
+  // vocabulary) for dH, hidden (tokens x H) for the recompute, hidden^T
+  // (H x tokens) for dW.
+  FLCE_TRY(pack_rows(K_PACK_HIDDEN, hidden, N, H, H, p.hkb, xb, st));
+  FLCE_TRY(pack_cols(K_PACK_HIDDEN, hidden, H, N, H, p.nkb, xtb, st));
   const bool capped = softcap > 0.f;
   for (int c = 0; c < p.nchunks; ++c) {
     const int64_t v0 = (int64_t)c * p.Vc;
     const int64_t vc = V - v0 < p.Vc ? V - v0 : p.Vc;
     const int vtc = (int)ceil_div(vc, kTile);
+    const uint16_t* wchunk = static_cast<const uint16_t*>(weight) + v0;
+    FLCE_TRY(pack_cols(K_PACK_WEIGHT, wchunk, vc, H, V, p.hkb, wt, st));
+    FLCE_TRY(pack_rows(K_PACK_WEIGHT, wchunk, H, vc, V, p.kbv, wb, st));
 
     DlogitsArgs d{};
-    d.weight = static_cast<const uint16_t*>(weight);
-    d.xt = xt;
+    d.wt = wt;
+    d.xb = xb;
     d.coef = coef;
     d.lab = lab32;
     d.N = N;
     d.H = H;
     d.V = V;
-    d.ldt = p.ldt;
+    d.hkb = p.hkb;
     d.v0 = v0;
-    d.vc = vc;
     d.VTc = vtc;
     d.TB = p.TB;
     d.group = p.group;
+    d.kbv = p.kbv;
+    d.kbn = p.nkb;
     d.cap = capped ? softcap : 0.f;
     d.cap_k = capped ? 2.f * kLog2e / softcap : 0.f;
     d.inv_cap = capped ? 1.f / softcap : 0.f;
-    d.dt = D;
+    d.dtv = dtv;
+    d.dvt = dvt;
     FLCE_TRY(launch(K_BWD_DLOGITS, st, [&] {
       if (capped)
         bwd_dlogits_kernel<true><<<vtc * p.TB, kThreads, 0, st>>>(d);
@@ -384,14 +431,13 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
     }));
 
     DxArgs x{};
-    x.dt = D;
-    x.weight = static_cast<const uint16_t*>(weight);
+    x.dtv = dtv;
+    x.wb = wb;
     x.N = N;
     x.H = H;
     x.V = V;
-    x.v0 = v0;
-    x.vc = vc;
-    x.ldt = p.ldt;
+    x.kbv = p.kbv;
+    x.nk = vtc * (kTile / kBK);
     x.TB = p.TB;
     x.HT = p.HT;
     x.group = p.group;
@@ -410,14 +456,14 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
     }));
 
     DwArgs w{};
-    w.hidden = static_cast<const uint16_t*>(hidden);
-    w.dt = D;
+    w.xtb = xtb;
+    w.dvt = dvt;
     w.N = N;
     w.H = H;
     w.V = V;
     w.v0 = v0;
     w.vc = vc;
-    w.ldt = p.ldt;
+    w.kbn = p.nkb;
     w.ldp = p.Vc;
     w.HT = p.HT;
     w.VTc = vtc;

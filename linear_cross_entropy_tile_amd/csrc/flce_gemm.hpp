@@ -1,5 +1,5 @@
-// Block-tile bf16 GEMM core for gfx950 (CDNA4), shared by every kernel of the
-// fused linear cross-entropy head.
+// Block-tile bf16 GEMM core for gfx950 (CDNA4), shared by every contraction of
+// the fused linear cross-entropy head.
 //
 // A block of 512 threads (8 wave64s, two per SIMD) owns a 256 x 256 output
 // tile C[m][n] = sum_k A[m][k] * B[n][k], fp32 accumulators. Wave w computes
@@ -7,23 +7,25 @@
 // v_mfma_f32_32x32x16_bf16 (4 x 2 blocks of 32 x 32, 128 accumulators per
 // lane), so two waves share each SIMD and hide each other's stalls.
 //
-// Operands move global -> LDS by direct DMA (buffer_load_dwordx4 ... lds): no
-// staging registers and no LDS store instructions. Four LDS stages of 32 K
-// values (16 KiB per operand each, 128 KiB in all) keep three K slices in
-// flight while one is consumed; every stage is a separate __shared__ array so
-// the compiler can tell a stage being read from the ones being filled.
+// Operand layout ("blocked"). Every GEMM operand is first arranged in HBM as
+// strips of 256 rows; a strip is a sequence of K blocks of 32 values, and a
+// block is 16 KiB holding exactly the bytes one LDS stage of that operand
+// needs, in LDS order: row r (0..255) takes 64 bytes, its four 16-byte chunks
+// of 8 K values stored at positions c ^ ((r >> 2) & 3). Rows and K values past
+// the operand's extent are zero. The arrangement pays off twice:
+//   * global -> LDS is a straight copy: each DMA instruction
+//     (buffer_load_dwordx4 ... lds) moves 1 KiB of contiguous memory, and a
+//     strip is streamed front to back, so HBM sees long sequential runs rather
+//     than one 64-byte piece per row;
+//   * every fragment is read with ds_read_b128 (full LDS rate on gfx950; the
+//     transposing ds_read_b64_tr_b16 runs at well under half of it).
+// The producers of blocked operands (pack kernels, the logit-gradient
+// epilogue) live in flce_kernels.hpp.
 //
-// Two global layouts per operand:
-//   KMAJOR  element (r, k) at ptr[r * ld + k]   (K contiguous)
-//   RMAJOR  element (r, k) at ptr[k * ld + r]   (rows contiguous)
-// KMAJOR stages are stored row-major in LDS and read with ds_read_b128;
-// RMAJOR stages are stored K-row-major and read with the gfx950 transposing
-// read ds_read_b64_tr_b16, which hands each lane 4 consecutive K values of one
-// tile row. Both LDS layouts are XOR-swizzled so the DMA writes and the
-// fragment reads are free of bank conflicts.
-//
-// All global loads go through raw buffer resources: out-of-range offsets
-// (tails in rows and K) read as zero, also into LDS.
+// Four LDS stages (16 KiB per operand each, 128 KiB in all) keep three K
+// blocks in flight while one is consumed; every stage is a separate
+// __shared__ array so the compiler can tell a stage being read from the ones
+// being filled.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,28 +34,29 @@
 namespace flce {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int kTile = 256;                          // M and N extent of a block tile
-constexpr int kBK = 32;                             // K per LDS stage
+constexpr int kTile = 256;                          // M and N extent of a block tile; strip height
+constexpr int kBK = 32;                             // K values per block / LDS stage
 constexpr int kStages = 4;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStageBytes = kTile * kBK * 2;        // 16 KiB per operand per stage
-constexpr int kDmaBlocks = kStageBytes / 1024 / kWaves;  // 1 KiB DMA blocks per wave
+constexpr int kBlockBytes = kTile * kBK * 2;        // 16 KiB: one K block of one strip
+constexpr int kBlockElems = kBlockBytes / 2;
+constexpr int kDmaBlocks = kBlockBytes / 1024 / kWaves;  // 1 KiB DMA pieces per wave per block
 
-enum { KMAJOR = 0, RMAJOR = 1 };
+// Byte offset of element (r, k) inside a block (r < 256, k < 32).
+__host__ __device__ __forceinline__ int blk_byte(int r, int k) {
+  return r * 64 + ((((k >> 3) ^ ((r >> 2) & 3))) << 4) + (k & 7) * 2;
+}
 
-struct Operand {
-  const uint16_t* ptr;  // bf16 bits
-  int64_t ld;           // leading dimension, elements
-  int64_t rows;         // valid rows; rows >= this read as zero
+// One strip of a blocked operand.
+struct Strip {
+  const uint16_t* ptr;  // block 0 of the strip
+  int nkb;              // K blocks the strip holds (bounds every load)
 };
 
 // ---- block numbering ------------------------------------------------------------
@@ -97,6 +100,9 @@ __device__ __forceinline__ void buf_store_f32(float v, __amdgpu_buffer_rsrc_t r,
 __device__ __forceinline__ void buf_store_u16(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, voff, 0, 0);
 }
+__device__ __forceinline__ void buf_store_u32x2(u32x2_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);
+}
 
 // Keeps the compiler from hoisting work that depends on `x` out of a loop.
 template <class T>
@@ -122,86 +128,29 @@ __device__ __forceinline__ void block_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
-// ---- LDS layouts of one operand stage (256 tile rows x 32 K) ------------------
+// ---- global -> LDS DMA of one block -------------------------------------------------
 
-// KMAJOR: tile row r is 64 bytes (four 16-byte chunks of 8 K values); chunk c
-// sits at position c ^ ((r >> 2) & 3). Sixteen consecutive rows reading one
-// logical chunk hit sixteen distinct 16-byte bank groups.
-__device__ __forceinline__ int kmaj_byte(int r, int c) {
-  return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
-}
-// RMAJOR: K row k is 512 bytes (all 256 tile rows); the 64-byte segment of
-// tile rows [32s, 32s+32) sits at position s ^ (k & 3), so the four K rows a
-// transposing read touches land in four distinct bank groups.
-__device__ __forceinline__ int rmaj_byte(int k, int m) {
-  return k * 512 + ((((m >> 5) ^ (k & 3))) << 6) + (m & 31) * 2;
-}
-
-// ---- global -> LDS DMA of one operand stage -------------------------------------
-
-template <int L>
-struct Dma;
-
-// KMAJOR: a 1 KiB DMA block is 16 tile rows x 64 bytes; lane l fetches the
-// logical chunk whose swizzled position is l % 4 of row l / 4. The resource
-// starts at the tile's first row and ends at `rows`.
-template <>
-struct Dma<KMAJOR> {
+// Wave w copies pieces [w * kDmaBlocks, +kDmaBlocks) of 1 KiB; lane l moves
+// bytes [16 l, +16) of each piece. Block indices at or past the strip's end
+// are sent to an out-of-range offset (no memory access; zeros land in LDS), so
+// every step issues the same number of loads.
+struct Dma {
   __amdgpu_buffer_rsrc_t rs;
-  uint32_t off[kDmaBlocks];
-  int c8[kDmaBlocks];
-  __device__ __forceinline__ void init(const Operand& op, int64_t r0) {
+  uint32_t off;
+  int nkb;
+  __device__ __forceinline__ void init(const Strip& s) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    rs = make_rsrc(op.ptr + r0 * op.ld, (op.rows - r0) * op.ld * 2);
-#pragma unroll
-    for (int q = 0; q < kDmaBlocks; ++q) {
-      const int r = (w * kDmaBlocks + q) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((r >> 2) & 3);
-      off[q] = (uint32_t)((r * op.ld + c * 8) * 2);
-      c8[q] = c * 8;
-    }
+    rs = make_rsrc(s.ptr, (int64_t)s.nkb * kBlockBytes);
+    off = (uint32_t)(w * kDmaBlocks * 1024 + lane * 16);
+    nkb = s.nkb;
   }
-  __device__ __forceinline__ void issue(char* dst, int64_t k0, int64_t kend) {
+  __device__ __forceinline__ void issue(char* dst, int kb) const {
     const int w = threadIdx.x >> 6;
-    const int rem = (int)(kend - k0);
-    const uint32_t kb = (uint32_t)(k0 * 2);
+    const bool ok = kb < nkb;
+    const uint32_t base = off + (uint32_t)kb * (uint32_t)kBlockBytes;
 #pragma unroll
     for (int q = 0; q < kDmaBlocks; ++q) {
-      const uint32_t v = c8[q] < rem ? off[q] + kb : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void_t*)(dst + (w * kDmaBlocks + q) * 1024), 16, v, 0, 0, 0);
-    }
-  }
-};
-
-// RMAJOR: a 1 KiB DMA block is 2 K rows x 512 bytes; lane l fetches the
-// 16-byte piece whose swizzled slot is l % 32 of K row l / 32. The resource is
-// rebased to each stage's first K row and ends at kend. `rows` must be a
-// multiple of 8 so an 8-row piece is either fully valid or not.
-template <>
-struct Dma<RMAJOR> {
-  const uint16_t* ptr;
-  int64_t ld;
-  uint32_t off[kDmaBlocks];
-  __device__ __forceinline__ void init(const Operand& op, int64_t r0) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    ptr = op.ptr;
-    ld = op.ld;
-#pragma unroll
-    for (int q = 0; q < kDmaBlocks; ++q) {
-      const int k = (w * kDmaBlocks + q) * 2 + (lane >> 5);
-      const int slot = lane & 31;
-      const int m = (((slot >> 2) ^ (k & 3)) << 5) + (slot & 3) * 8;
-      off[q] = r0 + m < op.rows ? (uint32_t)((k * op.ld + r0 + m) * 2) : kOOB;
-    }
-  }
-  __device__ __forceinline__ void issue(char* dst, int64_t k0, int64_t kend) {
-    const int w = threadIdx.x >> 6;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(ptr + k0 * ld, (kend - k0) * ld * 2);
-#pragma unroll
-    for (int q = 0; q < kDmaBlocks; ++q) {
-      uint32_t v = off[q];
-      opaque(v);
+      const uint32_t v = ok ? base + q * 1024 : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (lds_void_t*)(dst + (w * kDmaBlocks + q) * 1024), 16, v, 0, 0, 0);
     }
@@ -212,53 +161,22 @@ struct Dma<RMAJOR> {
 
 // NB blocks of 32 tile rows from row0 (a multiple of 32); 16-wide K step kk
 // of a stage. 32x32x16 MFMA lane layout: lane l supplies tile row l % 32 and
-// K values 8*(l/32) .. +7 of the step.
-template <int L, int NB>
-struct FragSrc;
-
+// K values 8*(l/32) .. +7 of the step, i.e. chunk 2kk + l/32 of its row.
+// Eight consecutive rows reading one logical chunk hit eight distinct 16-byte
+// bank groups thanks to the chunk swizzle.
 template <int NB>
-struct FragSrc<KMAJOR, NB> {
+struct FragSrc {
   int base[NB];
   __device__ __forceinline__ void init(int row0) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) base[i] = kmaj_byte(row0 + i * 32 + (lane & 31), lane >> 5);
+    for (int i = 0; i < NB; ++i) base[i] = blk_byte(row0 + i * 32 + (lane & 31), 8 * (lane >> 5));
   }
   // Chunk 2kk + l/32: step kk = 1 flips bit 5 of the byte offset.
   __device__ __forceinline__ void read(const char* st, int kk, bf16x8_t (&f)[NB]) const {
 #pragma unroll
     for (int i = 0; i < NB; ++i)
       f[i] = *reinterpret_cast<const bf16x8_t*>(st + (base[i] ^ (kk << 5)));
-  }
-};
-
-// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4
-// of the 8 bytes that lane 4j + i/4 addressed, for j = 0..3. Lane a of group g
-// addresses K row 8(g/2) + 4h + a/4 at tile rows 16(g%2) + 4(a%4) .. +3, so
-// lane i ends up with 4 consecutive K values of tile row 16(g%2) + i; the two
-// reads h = 0, 1 give the 8 K values of a 16-wide step.
-template <int NB>
-struct FragSrc<RMAJOR, NB> {
-  int base;
-  __device__ __forceinline__ void init(int row0) {
-    const int lane = threadIdx.x & 63;
-    const int g = lane >> 4, a = lane & 15;
-    base = rmaj_byte(8 * (g >> 1) + (a >> 2), row0 + 16 * (g & 1) + 4 * (a & 3));
-  }
-  // Block i adds 32i to the row: with row0 / 32 a multiple of NB that is an XOR
-  // of the segment bits; step kk adds 16 K rows.
-  __device__ __forceinline__ void read(const char* st, int kk, bf16x8_t (&f)[NB]) const {
-    int b = base;
-    opaque(b);
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int o = (b ^ (i << 6)) + kk * 16 * 512;
-      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(st + o));
-      const i16x4_t hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(st + o + 4 * 512));
-      const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      f[i] = __builtin_bit_cast(bf16x8_t, v);
-    }
   }
 };
 
@@ -276,10 +194,10 @@ typedef f32x16_t Acc[4][2];
 
 // LDS for one block: four stages per operand, each a separate array.
 #define FLCE_DECLARE_STAGES(sa, sb)                                                   \
-  __shared__ __attribute__((aligned(1024))) char sa##_0[flce::kStageBytes],            \
-      sa##_1[flce::kStageBytes], sa##_2[flce::kStageBytes], sa##_3[flce::kStageBytes]; \
-  __shared__ __attribute__((aligned(1024))) char sb##_0[flce::kStageBytes],            \
-      sb##_1[flce::kStageBytes], sb##_2[flce::kStageBytes], sb##_3[flce::kStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) char sa##_0[flce::kBlockBytes],            \
+      sa##_1[flce::kBlockBytes], sa##_2[flce::kBlockBytes], sa##_3[flce::kBlockBytes]; \
+  __shared__ __attribute__((aligned(1024))) char sb##_0[flce::kBlockBytes],            \
+      sb##_1[flce::kBlockBytes], sb##_2[flce::kBlockBytes], sb##_3[flce::kBlockBytes]; \
   char* const sa[flce::kStages] = {sa##_0, sa##_1, sa##_2, sa##_3};                    \
   char* const sb[flce::kStages] = {sb##_0, sb##_1, sb##_2, sb##_3}
 
@@ -307,15 +225,15 @@ __device__ __forceinline__ void interleave_reads() {
   sg_mfma_then_reads<NR, 7>();
 }
 
-template <int LA, int LB>
 struct Mainloop {
   struct Frags {
     bf16x8_t a[4], b[2];
   };
-  FragSrc<LA, 4> fa;
-  FragSrc<LB, 2> fb;
-  Dma<LA> da;
-  Dma<LB> db;
+  FragSrc<4> fa;
+  FragSrc<2> fb;
+  Dma da;
+  Dma db;
+  int a_kb0, b_kb0;
 
   __device__ __forceinline__ void frags(const char* a, const char* b, int kk, Frags& f) const {
     fa.read(a, kk, f.a);
@@ -328,28 +246,32 @@ struct Mainloop {
       for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   }
+  // Block kt of the K range; past the range both operands get out-of-range
+  // offsets.
+  __device__ __forceinline__ void issue(char* a, char* b, int kt, int nk) const {
+    da.issue(a, kt < nk ? a_kb0 + kt : da.nkb);
+    db.issue(b, kt < nk ? b_kb0 + kt : db.nkb);
+  }
 
-  // One K slice, reading stage S: first the DMA of the slice three ahead is
+  // LDS fragment-read instructions per 16-wide K step.
+  static constexpr int kReads = 4 + 2;
+
+  // One K block, reading stage S: first the DMA of the block three ahead is
   // issued into the stage consumed last step; sub-step 1's fragments are read
-  // while sub-step 0's MFMAs run; then this wave's DMA of the next slice is
+  // while sub-step 0's MFMAs run; then this wave's DMA of the next block is
   // awaited and the block synchronises (the next stage is now complete in
-  // LDS); the next slice's sub-step 0 fragments are read while this slice's
+  // LDS); the next block's sub-step 0 fragments are read while this block's
   // sub-step 1 MFMAs run (they only need registers).
-  // LDS fragment-read instructions per 16-wide K step: ds_read_b128 per
-  // K-major block, two ds_read_b64_tr_b16 per row-major block.
-  static constexpr int kReads = (LA == KMAJOR ? 4 : 8) + (LB == KMAJOR ? 2 : 4);
-
   template <int S>
   __device__ __forceinline__ void step(char* const (&sa)[kStages], char* const (&sb)[kStages],
-                                       Frags (&f)[2], Acc& acc, int64_t kiss, int64_t kend) {
+                                       Frags (&f)[2], Acc& acc, int kiss, int nk) {
     constexpr int SI = (S + kStages - 1) % kStages;
     constexpr int SN = (S + 1) % kStages;
-    da.issue(sa[SI], kiss, kend);
-    db.issue(sb[SI], kiss, kend);
+    issue(sa[SI], sb[SI], kiss, nk);
     frags(sa[S], sb[S], 1, f[1]);
     mma(f[0], acc);
-    // DMA issue first, then the fragment reads spread one or two per MFMA,
-    // so the LDS sees a steady stream rather than a burst per wave.
+    // DMA issue first, then the fragment reads spread over the MFMAs, so the
+    // LDS sees a steady stream rather than a burst per wave.
     __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 2 * kDmaBlocks, 0);
     interleave_reads<kReads>();
     wait_vmcnt<2 * kDmaBlocks * (kStages - 2)>();
@@ -360,12 +282,12 @@ struct Mainloop {
     interleave_reads<kReads>();
   }
 
-  // C tile = A rows [ar, ar+256) x B rows [br, br+256) over K in [kbeg, kend).
-  // Leaves every DMA drained and the block synchronised, so callers may reuse
-  // the stage arrays afterwards.
+  // C tile = strip A x strip B over K blocks [akb0, akb0 + nk) of A and
+  // [bkb0, bkb0 + nk) of B. Leaves every DMA drained and the block
+  // synchronised, so callers may reuse the stage arrays afterwards.
   __device__ __forceinline__ void run(char* const (&sa)[kStages], char* const (&sb)[kStages],
-                                      const Operand& A, const Operand& B, int64_t ar, int64_t br,
-                                      int64_t kbeg, int64_t kend, Acc& acc) {
+                                      const Strip& A, int akb0, const Strip& B, int bkb0, int nk,
+                                      Acc& acc) {
     const int wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
 #pragma unroll
@@ -374,27 +296,25 @@ struct Mainloop {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    const int nk = (int)((kend - kbeg + kBK - 1) / kBK);
     if (nk <= 0) return;
-    da.init(A, ar);
-    db.init(B, br);
+    da.init(A);
+    db.init(B);
+    a_kb0 = akb0;
+    b_kb0 = bkb0;
     fa.init(wm * 128);
     fb.init(wn * 64);
 #pragma unroll
-    for (int s = 0; s + 1 < kStages; ++s) {
-      da.issue(sa[s], kbeg + (int64_t)s * kBK, kend);
-      db.issue(sb[s], kbeg + (int64_t)s * kBK, kend);
-    }
+    for (int s = 0; s + 1 < kStages; ++s) issue(sa[s], sb[s], s, nk);
     wait_vmcnt<2 * kDmaBlocks * (kStages - 2)>();
     block_barrier();
     Frags f[2];
     frags(sa[0], sb[0], 0, f[0]);
     for (int kt = 0; kt < nk; kt += kStages) {
-      const int64_t k3 = kbeg + (int64_t)(kt + kStages - 1) * kBK;
-      step<0>(sa, sb, f, acc, k3, kend);
-      if (kt + 1 < nk) step<1>(sa, sb, f, acc, k3 + kBK, kend);
-      if (kt + 2 < nk) step<2>(sa, sb, f, acc, k3 + 2 * kBK, kend);
-      if (kt + 3 < nk) step<3>(sa, sb, f, acc, k3 + 3 * kBK, kend);
+      const int k3 = kt + kStages - 1;
+      step<0>(sa, sb, f, acc, k3, nk);
+      if (kt + 1 < nk) step<1>(sa, sb, f, acc, k3 + 1, nk);
+      if (kt + 2 < nk) step<2>(sa, sb, f, acc, k3 + 2, nk);
+      if (kt + 3 < nk) step<3>(sa, sb, f, acc, k3 + 3, nk);
     }
     wait_vmcnt<0>();
     block_barrier();

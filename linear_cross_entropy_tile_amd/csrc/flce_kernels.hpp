@@ -1,8 +1,13 @@
 // Kernels of the fused linear cross-entropy + entropy head (gfx950).
 //
-// Forward:  fwd_prep, transpose -> fwd_tile -> fwd_combine (-> fwd_mean)
-// Backward: bwd_prep, transpose -> per vocabulary chunk { bwd_dlogits -> bwd_dx
-//           -> bwd_dw (-> dw_reduce) }
+// Forward:  fwd_prep, pack (weight^T, hidden) -> fwd_tile -> fwd_combine
+//           (-> fwd_mean)
+// Backward: bwd_prep, pack (weight^T, weight, hidden, hidden^T) -> per
+//           vocabulary chunk { bwd_dlogits -> bwd_dx -> bwd_dw (-> dw_reduce) }
+//
+// Every GEMM operand is read in the blocked layout of flce_gemm.hpp; the pack
+// kernels below build it from the caller's row-major tensors, and the
+// logit-gradient epilogue writes its output directly in it.
 //
 // The quantities follow the definition in verl pull request #462 ("Equivalent
 // compute logic"): per token the logsumexp of the logits, the entropy
@@ -67,49 +72,84 @@ __global__ void __launch_bounds__(1024) fwd_prep_kernel(const int64_t* __restric
   }
 }
 
-// ---- hidden^T, the token-contiguous copy the logit GEMMs read ------------------
+// ---- blocked operand images ----------------------------------------------------
 
-// XT[h][t] = hidden[t][h] for t < N; columns t in [N, ldt) are zero. 64 x 64
-// tiles through LDS, 16-byte loads and stores.
-__global__ void __launch_bounds__(256) transpose_kernel(const uint16_t* __restrict__ X, int64_t N,
-                                                        int64_t H, int64_t ldt,
-                                                        uint16_t* __restrict__ XT) {
-  __shared__ uint16_t tile[64][72];
-  const int64_t h0 = (int64_t)blockIdx.x * 64, t0 = (int64_t)blockIdx.y * 64;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int r = tid / 8 + 32 * p, c = (tid % 8) * 8;
+// Operand (R rows, K values per row) whose source is K-contiguous:
+// element (r, k) at src[r * ld + k]. Writes the blocked image `dst` of
+// ceil(R/256) strips x nkb K blocks; rows >= R and K values >= K are zero.
+// A workgroup fills 8 consecutive K blocks of one strip; consecutive threads
+// read consecutive 16-byte pieces of one source row (512 bytes per row).
+// K must be a multiple of 8 and ld a multiple of 8.
+__global__ void __launch_bounds__(256) pack_rows_kernel(const uint16_t* __restrict__ src,
+                                                        int64_t R, int64_t K, int64_t ld, int nkb,
+                                                        uint16_t* __restrict__ dst) {
+  const int64_t strip = blockIdx.y;
+  const int kb0 = blockIdx.x * 8;
+  const int t = threadIdx.x;
+#pragma unroll 4
+  for (int p = 0; p < 32; ++p) {
+    const int i = p * 256 + t;
+    const int r = i >> 5, kbl = (i >> 2) & 7, c = i & 3;
+    const int kb = kb0 + kbl;
+    if (kb >= nkb) continue;
+    const int64_t row = strip * kTile + r;
+    const int64_t k = (int64_t)kb * kBK + c * 8;
     u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-    if (t0 + r < N && h0 + c < H) v = *reinterpret_cast<const u32x4_t*>(X + (t0 + r) * H + h0 + c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tile[r][c + 2 * e] = (uint16_t)(v[e] & 0xFFFFu);
-      tile[r][c + 2 * e + 1] = (uint16_t)(v[e] >> 16);
-    }
+    if (row < R && k < K) v = *reinterpret_cast<const u32x4_t*>(src + row * ld + k);
+    char* blk = reinterpret_cast<char*>(dst) + (strip * nkb + kb) * (int64_t)kBlockBytes;
+    *reinterpret_cast<u32x4_t*>(blk + blk_byte(r, c * 8)) = v;
   }
-  __syncthreads();
+}
+
+// Operand (R rows, K values per row) whose source is row-contiguous:
+// element (r, k) at src[k * ld + r] (a transposing pack). Writes the blocked
+// image `dst` of ceil(R/256) strips x nkb K blocks, zero past R and K. A
+// workgroup fills K blocks (2 bx, 2 bx + 1) of one strip: thread (g, q) reads
+// rows r = 8g .. 8g+7 of the 8 source rows k = 8q .. 8q+7 (16 bytes each;
+// 32 consecutive threads read 512 contiguous bytes), transposes the 8 x 8
+// piece in registers and writes eight 16-byte chunks. R must be a multiple of
+// 8 and ld a multiple of 8.
+__global__ void __launch_bounds__(256) pack_cols_kernel(const uint16_t* __restrict__ src,
+                                                        int64_t R, int64_t K, int64_t ld, int nkb,
+                                                        uint16_t* __restrict__ dst) {
+  const int64_t strip = blockIdx.y;
+  const int t = threadIdx.x;
+  const int g = t & 31, q = t >> 5;                 // row group, K chunk (0..7)
+  const int kb = blockIdx.x * 2 + (q >> 2);
+  if (kb >= nkb) return;
+  const int c = q & 3;                              // chunk within the block
+  const int64_t r0 = strip * kTile + 8 * g;
+  const int64_t k0 = (int64_t)kb * kBK + c * 8;
+  u32x4_t in[8];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int hr = tid / 8 + 32 * p, tc = (tid % 8) * 8;
-    if (h0 + hr < H && t0 + tc < ldt) {
-      u32x4_t v;
+  for (int e = 0; e < 8; ++e) {
+    in[e] = u32x4_t{0u, 0u, 0u, 0u};
+    if (r0 < R && k0 + e < K) in[e] = *reinterpret_cast<const u32x4_t*>(src + (k0 + e) * ld + r0);
+  }
+  char* blk = reinterpret_cast<char*>(dst) + (strip * nkb + kb) * (int64_t)kBlockBytes;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        v[e] = (uint32_t)tile[tc + 2 * e][hr] | ((uint32_t)tile[tc + 2 * e + 1][hr] << 16);
-      *reinterpret_cast<u32x4_t*>(XT + (h0 + hr) * ldt + t0 + tc) = v;
+  for (int j = 0; j < 8; ++j) {
+    // Output row 8g + j holds K values k0 .. k0+7: element j of each in[e].
+    u32x4_t o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t x = in[2 * w][j >> 1], y = in[2 * w + 1][j >> 1];
+      o[w] = (j & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
     }
+    *reinterpret_cast<u32x4_t*>(blk + blk_byte(8 * g + j, c * 8)) = o;
   }
 }
 
 // ---- forward: fused logit tiles + online row statistics ---------------------
 
 struct FwdTileArgs {
-  const uint16_t* weight;  // [H,V]
-  const uint16_t* xt;      // [H, ldt] hidden^T
+  const uint16_t* wt;      // blocked weight^T of the chunk: strips of 256 vocabulary rows, K = H
+  const uint16_t* xb;      // blocked hidden: strips of 256 tokens, K = H
   const int32_t* lab;      // [N], -1 = no label
-  int64_t N, H, V, ldt;
-  int VT, TB;              // vocabulary tiles, token blocks (256 each)
+  int64_t N, H, V;
+  int64_t v0;              // first vocabulary column of the chunk (multiple of 256)
+  int hkb;                 // K blocks per strip, ceil(H / 32)
+  int VT, VTc, TB;         // vocabulary tiles (all, in the chunk), token blocks
   int group;               // token blocks per XCD patch (see group_map)
   float cap, cap_k;        // softcap c and 2*log2(e)/c
   float4* part;            // [VT][N] {m, s, u, 0} per vocabulary tile
@@ -127,9 +167,9 @@ __device__ __forceinline__ void merge_state2(float& m, float& s, float& u, float
   m = mn;
 }
 
-// Block (tb, vt): tokens [256 tb, +256) against vocabulary [256 vt, +256).
-// The MFMA tile is z^T: rows = vocabulary (A = weight, row-major [H,V]), cols =
-// tokens (B = hidden^T), so each lane's 64 accumulators of one 32-column block
+// Block (tb, vt): tokens [256 tb, +256) against vocabulary [v0 + 256 vt, +256).
+// The MFMA tile is z^T: rows = vocabulary (A = weight^T strip), cols = tokens
+// (B = hidden strip), so each lane's 64 accumulators of one 32-column block
 // belong to one token and the row statistics need no cross-lane work until the
 // end. The block reduces its tile to (m, s, u) per token and stores it as the
 // tile's partial state.
@@ -138,17 +178,18 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(2, 2)))
 fwd_tile_kernel(FwdTileArgs a) {
   FLCE_DECLARE_STAGES(sa, sb);
-  int tb, vt;
-  group_map(xcd_remap(blockIdx.x, gridDim.x), a.TB, a.VT, a.group, tb, vt);
+  int tb, vl;
+  group_map(xcd_remap(blockIdx.x, gridDim.x), a.TB, a.VTc, a.group, tb, vl);
   const int lane = threadIdx.x & 63, lh = lane >> 5;
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t n0 = (int64_t)tb * kTile;
+  const int vt = (int)(a.v0 / kTile) + vl;  // vocabulary tile in the whole vocabulary
 
   Acc acc;
   {
-    Mainloop<RMAJOR, RMAJOR> ml;
-    ml.run(sa, sb, Operand{a.weight, a.V, a.V}, Operand{a.xt, a.ldt, a.N}, (int64_t)vt * kTile,
-           n0, 0, a.H, acc);
+    Mainloop ml;
+    const int64_t sz = (int64_t)a.hkb * kBlockElems;
+    ml.run(sa, sb, Strip{a.wt + vl * sz, a.hkb}, 0, Strip{a.xb + tb * sz, a.hkb}, 0, a.hkb, acc);
   }
 
   const int vb = vt * kTile + wm * 128;  // first vocabulary row of this wave
@@ -355,21 +396,27 @@ __global__ void __launch_bounds__(1024) bwd_prep_kernel(
 // ---- backward: recompute logits, form the logit gradient ----------------------
 
 struct DlogitsArgs {
-  const uint16_t* weight;  // [H,V]
-  const uint16_t* xt;      // [H, ldt] hidden^T
+  const uint16_t* wt;      // blocked weight^T of the chunk (as in the forward)
+  const uint16_t* xb;      // blocked hidden
   const float4* coef;      // [N]
   const int32_t* lab;      // [N]
-  int64_t N, H, V, ldt;
-  int64_t v0;              // first vocabulary column of this chunk
-  int64_t vc;              // valid columns in this chunk
+  int64_t N, H, V;
+  int hkb;                 // K blocks of the weight^T / hidden strips
+  int64_t v0;              // first vocabulary column of this chunk (multiple of 256)
   int VTc, TB;             // vocabulary tiles in the chunk, token blocks
   int group;
+  int kbv;                 // K blocks per strip of dtv (chunk capacity / 32)
+  int kbn;                 // K blocks per strip of dvt (token blocks * 8)
   float cap, cap_k, inv_cap;
-  uint16_t* dt;            // [vc, ldt] bf16 logit gradient of the chunk, vocabulary-major
+  uint16_t* dtv;           // blocked D, strips of 256 tokens, K = chunk vocabulary
+  uint16_t* dvt;           // blocked D^T, strips of 256 chunk vocabulary rows, K = tokens
 };
 
 // dz' = gbar ([v == y] - p) - ebar p (z' - S), dz = dz' (1 - (z'/c)^2) if
-// capped; written as bf16 dt[v - v0][t]. Token columns in [N, ldt) get 0.
+// capped, rounded to bf16 and written into both blocked images of the chunk:
+// dtv (the A operand of dH = D W^T) and dvt (the B operand of dW = hidden^T D).
+// Tokens past N have coefficients that make dz = 0, vocabulary rows past V
+// are set to 0, so the padded parts of both images hold zeros.
 template <bool CAP>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(2, 2)))
@@ -380,64 +427,68 @@ bwd_dlogits_kernel(DlogitsArgs a) {
   const int lane = threadIdx.x & 63, lh = lane >> 5;
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t n0 = (int64_t)tb * kTile;
-  const int64_t vl0 = (int64_t)vt * kTile;  // chunk-local first column of the tile
+  const int64_t vg0 = a.v0 + (int64_t)vt * kTile;  // first vocabulary column of the tile
 
   Acc acc;
   {
-    Mainloop<RMAJOR, RMAJOR> ml;
-    ml.run(sa, sb, Operand{a.weight + a.v0, a.V, a.vc}, Operand{a.xt, a.ldt, a.N}, vl0, n0, 0,
-           a.H, acc);
+    Mainloop ml;
+    const int64_t sz = (int64_t)a.hkb * kBlockElems;
+    ml.run(sa, sb, Strip{a.wt + vt * sz, a.hkb}, 0, Strip{a.xb + tb * sz, a.hkb}, 0, a.hkb, acc);
   }
 
-  // Rows (vocabulary) past vc fall outside the resource; columns (tokens) past
-  // ldt are masked explicitly.
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dt, a.vc * a.ldt * 2);
+  // Each tile owns 8 consecutive K blocks in each image: dtv strip tb, blocks
+  // [8 vt, +8) (K = vocabulary); dvt strip vt, blocks [8 tb, +8) (K = tokens).
+  const __amdgpu_buffer_rsrc_t rtv = make_rsrc(
+      a.dtv + ((int64_t)tb * a.kbv + 8 * vt) * kBlockElems, 8 * (int64_t)kBlockBytes);
+  const __amdgpu_buffer_rsrc_t rvt = make_rsrc(
+      a.dvt + ((int64_t)vt * a.kbn + 8 * tb) * kBlockElems, 8 * (int64_t)kBlockBytes);
+  // Rows at offset o (i*32 + 8*(r/4) + r%4) of this lane are inside the
+  // vocabulary iff o < lim.
+  const int lim = (int)(a.V - vg0) - wm * 128 - 4 * lh;
+  const bool full = vg0 + kTile <= a.V;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int64_t t = n0 + acc_col(wn, j, lane);
+    const int n = acc_col(wn, j, lane);
+    const int64_t t = n0 + n;
     float4 c = make_float4(1e30f, 0.f, 0.f, 0.f);
     int y = -1;
     if (t < a.N) {
       c = a.coef[t];
       y = a.lab[t];
     }
-    const bool tok = t < a.ldt;
+    // The label's row offset within this lane's rows, or -1.
+    const int64_t yo = (int64_t)y - vg0 - wm * 128 - 4 * lh;
+    const int yl = (y >= 0 && yo >= 0 && yo < 128) ? (int)yo : -1;
     const float nl = -c.x * kLog2e;
     const float cS = c.z - c.w * c.y;  // gbar - ebar * S
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float z = acc[i][j][r];
-        if constexpr (CAP) z = softcap_apply(z, a.cap, a.cap_k);
-        const float p = fast_exp2(fmaf(z, kLog2e, nl));
-        float d = -p * fmaf(c.w, z, cS);
-        if constexpr (CAP) {
-          const float q = z * a.inv_cap;
-          d *= fmaf(-q, q, 1.f);
+      for (int rq = 0; rq < 4; ++rq) {
+        uint32_t h[4];
+#pragma unroll
+        for (int r3 = 0; r3 < 4; ++r3) {
+          const int r = rq * 4 + r3;
+          const int o = i * 32 + 8 * rq + r3;
+          float z = acc[i][j][r];
+          if constexpr (CAP) z = softcap_apply(z, a.cap, a.cap_k);
+          const float p = fast_exp2(fmaf(z, kLog2e, nl));
+          float d = fmaf(-p, fmaf(c.w, z, cS), o == yl ? c.z : 0.f);
+          if constexpr (CAP) {
+            const float qz = z * a.inv_cap;
+            d *= fmaf(-qz, qz, 1.f);
+          }
+          if (!full) d = o < lim ? d : 0.f;
+          h[r3] = bf16_bits(d);
+          // dvt: row m (vocabulary), K = token n.
+          const int m = acc_row(wm, i, r, lane);
+          buf_store_u16(h[r3], rvt, (uint32_t)((wn * 2 + j) * kBlockBytes + blk_byte(m, lane & 31)));
         }
-        const int64_t vl = vl0 + acc_row(wm, i, r, lane);
-        buf_store_u16(bf16_bits(d), rd, tok ? (uint32_t)((vl * a.ldt + t) * 2) : kOOB);
+        // dtv: row n (token), K = vocabulary rows m .. m+3 (one 8-byte piece).
+        const int m0 = acc_row(wm, i, rq * 4, lane);
+        const u32x2_t v2 = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        buf_store_u32x2(v2, rtv, (uint32_t)((m0 >> 5) * kBlockBytes + blk_byte(n, m0 & 31)));
       }
-    // The label entry gets + gbar (times the cap factor): rewrite that element
-    // after the stores above (same lane and address, so it lands last).
-    const int64_t off = (int64_t)y - a.v0 - vl0 - wm * 128;
-    if (y >= 0 && off >= 0 && off < 128 && (((off & 31) >> 2) & 1) == lh) {
-      const int isel = (int)(off >> 5);
-      const int rsel = (int)((((off & 31) >> 3) << 2) | (off & 3));
-      float z = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) z = (i == isel && r == rsel) ? acc[i][j][r] : z;
-      if constexpr (CAP) z = softcap_apply(z, a.cap, a.cap_k);
-      const float p = fast_exp2(fmaf(z, kLog2e, nl));
-      float d = c.z - p * fmaf(c.w, z, cS);
-      if constexpr (CAP) {
-        const float q = z * a.inv_cap;
-        d *= fmaf(-q, q, 1.f);
-      }
-      buf_store_u16(bf16_bits(d), rd, (uint32_t)(((y - a.v0) * a.ldt + t) * 2));
     }
     __builtin_amdgcn_sched_barrier(0);  // one token column at a time
   }
@@ -448,16 +499,18 @@ bwd_dlogits_kernel(DlogitsArgs a) {
 enum { DX_ONLY = 0, DX_FIRST = 1, DX_MID = 2, DX_LAST = 3 };
 
 struct DxArgs {
-  const uint16_t* dt;      // [vc, ldt] logit gradient, vocabulary-major
-  const uint16_t* weight;  // [H,V]
-  int64_t N, H, V, v0, vc, ldt;
+  const uint16_t* dtv;     // blocked D of the chunk (strips of tokens, K = vocabulary)
+  const uint16_t* wb;      // blocked weight of the chunk (strips of 256 hidden rows, K = vocabulary)
+  int64_t N, H, V;
+  int kbv;                 // K blocks per strip of both images (chunk capacity / 32)
+  int nk;                  // K blocks of the chunk
   int TB, HT;              // token blocks, hidden tiles
   int group;
   float* acc;              // [N,H] fp32 accumulator over chunks
   uint16_t* gh;            // [N,H] bf16 output
 };
 
-// C[t][h] = sum_v dt[v][t] W[h][v0 + v]. MODE: DX_ONLY (single chunk: write
+// C[t][h] = sum_v D[t][v] W[h][v0 + v] over the chunk. MODE: DX_ONLY (single chunk: write
 // bf16), DX_FIRST (store fp32), DX_MID (add into fp32), DX_LAST (add and write
 // bf16). Out-of-range rows and columns fall outside the buffer resources.
 template <int MODE>
@@ -472,9 +525,9 @@ bwd_dx_kernel(DxArgs a) {
   const int64_t m0 = (int64_t)tb * kTile, h0 = (int64_t)ht * kTile;
   Acc acc;
   {
-    Mainloop<RMAJOR, KMAJOR> ml;
-    ml.run(sa, sb, Operand{a.dt, a.ldt, a.N}, Operand{a.weight + a.v0, a.V, a.H}, m0, h0, 0,
-           a.vc, acc);
+    Mainloop ml;
+    ml.run(sa, sb, Strip{a.dtv + (int64_t)tb * a.kbv * kBlockElems, a.kbv}, 0,
+           Strip{a.wb + (int64_t)ht * a.kbv * kBlockElems, a.kbv}, 0, a.nk, acc);
   }
   const int64_t base = m0 * a.H + h0;
   const int64_t span = (a.N - m0) * a.H - h0;  // elements from the tile origin to the end
@@ -510,18 +563,19 @@ bwd_dx_kernel(DxArgs a) {
 // ---- backward: dW_chunk = hidden^T D ------------------------------------------
 
 struct DwArgs {
-  const uint16_t* hidden;  // [N,H]
-  const uint16_t* dt;      // [vc, ldt] logit gradient, vocabulary-major
-  int64_t N, H, V, v0, vc, ldt;
+  const uint16_t* xtb;     // blocked hidden^T (strips of 256 hidden rows, K = tokens)
+  const uint16_t* dvt;     // blocked D^T of the chunk (strips of 256 vocabulary rows, K = tokens)
+  int64_t N, H, V, v0, vc;
+  int kbn;                 // K blocks per strip of both (token blocks * 8)
   int HT, VTc, splits;
   int group;
-  int64_t kper;            // tokens per split (multiple of 32)
+  int kper;                // K blocks per split
   int64_t ldp;             // row stride of the split partials
   uint16_t* gw;            // [H,V] bf16 output
   float* part;             // [splits][H][ldp] fp32 (SPLIT only)
 };
 
-// C[h][v] = sum_t hidden[t][h] dt[v][t] over the split's tokens.
+// C[h][v] = sum_t hidden[t][h] D[t][v] over the split's tokens.
 template <bool SPLIT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(2, 2)))
@@ -535,13 +589,13 @@ bwd_dw_kernel(DwArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t h0 = (int64_t)ht * kTile, vl0 = (int64_t)vt * kTile;
-  const int64_t kbeg = (int64_t)sp * a.kper;
-  const int64_t kend = kbeg + a.kper < a.N ? kbeg + a.kper : a.N;
+  const int kbeg = sp * a.kper;
+  const int kend = kbeg + a.kper < a.kbn ? kbeg + a.kper : a.kbn;
   Acc acc;
   {
-    Mainloop<RMAJOR, KMAJOR> ml;
-    ml.run(sa, sb, Operand{a.hidden, a.H, a.H}, Operand{a.dt, a.ldt, a.vc}, h0, vl0, kbeg, kend,
-           acc);
+    Mainloop ml;
+    ml.run(sa, sb, Strip{a.xtb + (int64_t)ht * a.kbn * kBlockElems, a.kbn}, kbeg,
+           Strip{a.dvt + (int64_t)vt * a.kbn * kBlockElems, a.kbn}, kbeg, kend - kbeg, acc);
   }
   int64_t ld, base, span;
   if constexpr (SPLIT) {
