@@ -45,9 +45,9 @@ struct Plan {
   int dw_kper;         // K blocks per dW split
   int group;           // tile rows per XCD patch of the block -> tile map
   // forward workspace
-  size_t f_lab, f_part, f_zlab, f_bsum, f_wt, f_xb, f_total;
+  size_t f_lab, f_part, f_zlab, f_bsum, f_xb, f_total;
   // backward workspace
-  size_t b_lab, b_coef, b_wt, b_wb, b_xb, b_xtb, b_dtv, b_dvt, b_acc, b_part, b_total;
+  size_t b_lab, b_coef, b_wb, b_xb, b_xtb, b_dtv, b_dvt, b_acc, b_part, b_total;
 };
 
 size_t env_size(const char* name, size_t dflt) {
@@ -108,8 +108,6 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   off = align_up(off + 4 * (size_t)N);
   p.f_bsum = off;
   off = align_up(off + (reduction == FLCE_REDUCTION_MEAN ? 16 * (size_t)ceil_div(N, 256) : 0));
-  p.f_wt = off;
-  off = align_up(off + blk * (size_t)p.VTc * (size_t)p.hkb);
   p.f_xb = off;
   off = align_up(off + blk * (size_t)p.TB * (size_t)p.hkb);
   p.f_total = off;
@@ -119,8 +117,6 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   off = align_up(off + 4 * (size_t)N);
   p.b_coef = off;
   off = align_up(off + 16 * (size_t)N);
-  p.b_wt = off;
-  off = align_up(off + blk * (size_t)p.VTc * (size_t)p.hkb);
   p.b_wb = off;
   off = align_up(off + blk * (size_t)p.HT * (size_t)p.kbv);
   p.b_xb = off;
@@ -298,11 +294,10 @@ flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t
     fwd_prep_kernel<<<1, 1024, 0, st>>>(labels, N, V, ignore_index, lab32, header);
   }));
   if (N > 0) {
-    uint16_t* wt = reinterpret_cast<uint16_t*>(wsp(workspace, p.f_wt));
     uint16_t* xb = reinterpret_cast<uint16_t*>(wsp(workspace, p.f_xb));
     FLCE_TRY(pack_rows(K_PACK_HIDDEN, hidden, N, H, H, p.hkb, xb, st));
     FwdTileArgs a{};
-    a.wt = wt;
+    a.weight = static_cast<const uint16_t*>(weight);
     a.xb = xb;
     a.lab = lab32;
     a.N = N;
@@ -316,22 +311,13 @@ flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t
     a.cap_k = softcap > 0.f ? 2.f * kLog2e / softcap : 0.f;
     a.part = part;
     a.zlab = zlab;
-    for (int c = 0; c < p.nchunks; ++c) {
-      const int64_t v0 = (int64_t)c * p.Vc;
-      const int64_t vc = V - v0 < p.Vc ? V - v0 : p.Vc;
-      // weight[:, v0 : v0 + vc] is row-contiguous for the (vocabulary x H) operand.
-      FLCE_TRY(pack_cols(K_PACK_WEIGHT, static_cast<const uint16_t*>(weight) + v0, vc, H, V,
-                         p.hkb, wt, st));
-      a.v0 = v0;
-      a.VTc = (int)ceil_div(vc, kTile);
-      const int grid = p.TB * a.VTc;
-      FLCE_TRY(launch(K_FWD_TILE, st, [&] {
-        if (softcap > 0.f)
-          fwd_tile_kernel<true><<<grid, kThreads, 0, st>>>(a);
-        else
-          fwd_tile_kernel<false><<<grid, kThreads, 0, st>>>(a);
-      }));
-    }
+    const int grid = p.TB * p.VT;
+    FLCE_TRY(launch(K_FWD_TILE, st, [&] {
+      if (softcap > 0.f)
+        fwd_tile_kernel<true><<<grid, kThreads, 0, st>>>(a);
+      else
+        fwd_tile_kernel<false><<<grid, kThreads, 0, st>>>(a);
+    }));
     const int nb = (int)ceil_div(N, 256);
     FLCE_TRY(launch(K_FWD_COMBINE, st, [&] {
       fwd_combine_kernel<<<nb, 256, 0, st>>>(part, p.VT, zlab, lab32, N, lse, logprob, entropy,
@@ -375,7 +361,6 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
   int32_t* header = reinterpret_cast<int32_t*>(workspace);
   int32_t* lab32 = reinterpret_cast<int32_t*>(wsp(workspace, p.b_lab));
   float4* coef = reinterpret_cast<float4*>(wsp(workspace, p.b_coef));
-  uint16_t* wt = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_wt));
   uint16_t* wb = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_wb));
   uint16_t* xb = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_xb));
   uint16_t* xtb = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_xtb));
@@ -389,9 +374,9 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
                                         grad_logprob, grad_entropy, coef, lab32, header);
   }));
 
-  // Operands: weight^T (vocabulary x H) for the recompute, weight (H x
-  // vocabulary) for dH, hidden (tokens x H) for the recompute, hidden^T
-  // (H x tokens) for dW.
+  // Blocked operands: hidden (tokens x H) for the recompute, hidden^T
+  // (H x tokens) for dW, and per chunk the weight (H x vocabulary) for dH.
+  // The recompute reads the weight (vocabulary x H) row-contiguous.
   FLCE_TRY(pack_rows(K_PACK_HIDDEN, hidden, N, H, H, p.hkb, xb, st));
   FLCE_TRY(pack_cols(K_PACK_HIDDEN, hidden, H, N, H, p.nkb, xtb, st));
   const bool capped = softcap > 0.f;
@@ -400,11 +385,10 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
     const int64_t vc = V - v0 < p.Vc ? V - v0 : p.Vc;
     const int vtc = (int)ceil_div(vc, kTile);
     const uint16_t* wchunk = static_cast<const uint16_t*>(weight) + v0;
-    FLCE_TRY(pack_cols(K_PACK_WEIGHT, wchunk, vc, H, V, p.hkb, wt, st));
     FLCE_TRY(pack_rows(K_PACK_WEIGHT, wchunk, H, vc, V, p.kbv, wb, st));
 
     DlogitsArgs d{};
-    d.wt = wt;
+    d.weight = static_cast<const uint16_t*>(weight);
     d.xb = xb;
     d.coef = coef;
     d.lab = lab32;

@@ -22,6 +22,13 @@
 // The producers of blocked operands (pack kernels, the logit-gradient
 // epilogue) live in flce_kernels.hpp.
 //
+// The A operand may instead come straight from a row-contiguous tensor
+// (element (r, k) at ptr[k * ld + r], e.g. the [H,V] weight as the
+// vocabulary x H operand): one DMA instruction then moves two K rows of 512
+// contiguous bytes, and fragments are read with the gfx950 transposing read
+// ds_read_b64_tr_b16. This spares a transposed copy of the weight; the slower
+// LDS reads only touch one of the two operands.
+//
 // Four LDS stages (16 KiB per operand each, 128 KiB in all) keep three K
 // blocks in flight while one is consumed; every stage is a separate
 // __shared__ array so the compiler can tell a stage being read from the ones
@@ -34,10 +41,13 @@
 namespace flce {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kTile = 256;                          // M and N extent of a block tile; strip height
 constexpr int kBK = 32;                             // K values per block / LDS stage
@@ -157,6 +167,67 @@ struct Dma {
   }
 };
 
+// A operand taken from a blocked strip, K blocks [kb0, kb0 + nk).
+struct BlockedA {
+  Dma d;
+  int kb0;
+  __device__ __forceinline__ void init(const Strip& s, int kb0_) {
+    d.init(s);
+    kb0 = kb0_;
+  }
+  __device__ __forceinline__ void issue(char* dst, int kt, int nk) const {
+    d.issue(dst, kt < nk ? kb0 + kt : d.nkb);
+  }
+};
+
+// LDS layout of a row-contiguous stage: K row k is 512 bytes (all 256 tile
+// rows); the 64-byte segment of tile rows [32s, 32s+32) sits at position
+// s ^ (k & 3), so the four K rows a transposing read touches land in four
+// distinct bank groups.
+__device__ __forceinline__ int rmaj_byte(int k, int m) {
+  return k * 512 + ((((m >> 5) ^ (k & 3))) << 6) + (m & 31) * 2;
+}
+
+// A operand taken from a row-contiguous tensor: element (r, k) at
+// ptr[k * ld + r], tile rows [r0, r0 + 256) of `rows` valid ones, K values
+// [kbeg, kend). A 1 KiB DMA piece is 2 K rows x 512 bytes; lane l fetches the
+// 16-byte piece whose swizzled slot is l % 32 of K row l / 32. The resource is
+// rebased to each stage's first K row and ends at kend, so K tails and blocks
+// past the range read as zero. `rows`, r0 and ld must be multiples of 8.
+struct RowA {
+  const uint16_t* ptr;
+  int64_t ld, kbeg, kend;
+  uint32_t off[kDmaBlocks];
+  __device__ __forceinline__ void init(const uint16_t* p, int64_t ld_, int64_t rows, int64_t r0,
+                                       int64_t kb, int64_t ke) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    ptr = p;
+    ld = ld_;
+    kbeg = kb;
+    kend = ke;
+#pragma unroll
+    for (int q = 0; q < kDmaBlocks; ++q) {
+      const int k = (w * kDmaBlocks + q) * 2 + (lane >> 5);
+      const int slot = lane & 31;
+      const int m = (((slot >> 2) ^ (k & 3)) << 5) + (slot & 3) * 8;
+      off[q] = r0 + m < rows ? (uint32_t)((k * ld_ + r0 + m) * 2) : kOOB;
+    }
+  }
+  __device__ __forceinline__ void issue(char* dst, int kt, int nk) const {
+    const int w = threadIdx.x >> 6;
+    const int64_t k0 = kbeg + (int64_t)kt * kBK;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(ptr + k0 * ld, kt < nk ? (kend - k0) * ld * 2 : 0);
+#pragma unroll
+    for (int q = 0; q < kDmaBlocks; ++q) {
+      uint32_t v = off[q];
+      opaque(v);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void_t*)(dst + (w * kDmaBlocks + q) * 1024), 16, v, 0, 0, 0);
+    }
+  }
+};
+
 // ---- LDS -> register operand fragments ---------------------------------------------
 
 // NB blocks of 32 tile rows from row0 (a multiple of 32); 16-wide K step kk
@@ -166,6 +237,7 @@ struct Dma {
 // bank groups thanks to the chunk swizzle.
 template <int NB>
 struct FragSrc {
+  static constexpr int kReadsPerStep = NB;
   int base[NB];
   __device__ __forceinline__ void init(int row0) {
     const int lane = threadIdx.x & 63;
@@ -177,6 +249,38 @@ struct FragSrc {
 #pragma unroll
     for (int i = 0; i < NB; ++i)
       f[i] = *reinterpret_cast<const bf16x8_t*>(st + (base[i] ^ (kk << 5)));
+  }
+};
+
+// Fragments of a row-contiguous stage. ds_read_b64_tr_b16: within each
+// 16-lane group, lane i receives element i % 4 of the 8 bytes that lane
+// 4j + i/4 addressed, for j = 0..3. Lane a of group g addresses K row
+// 8(g/2) + 4h + a/4 at tile rows 16(g%2) + 4(a%4) .. +3, so lane i ends up with
+// 4 consecutive K values of tile row 16(g%2) + i; the two reads h = 0, 1 give
+// the 8 K values of a 16-wide step.
+template <int NB>
+struct FragRow {
+  static constexpr int kReadsPerStep = 2 * NB;
+  int base;
+  __device__ __forceinline__ void init(int row0) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, a = lane & 15;
+    base = rmaj_byte(8 * (g >> 1) + (a >> 2), row0 + 16 * (g & 1) + 4 * (a & 3));
+  }
+  // Block i adds 32i to the row: with row0 / 32 a multiple of NB that is an XOR
+  // of the segment bits; step kk adds 16 K rows.
+  __device__ __forceinline__ void read(const char* st, int kk, bf16x8_t (&f)[NB]) const {
+    int b = base;
+    opaque(b);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int o = (b ^ (i << 6)) + kk * 16 * 512;
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(st + o));
+      const i16x4_t hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(st + o + 4 * 512));
+      const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      f[i] = __builtin_bit_cast(bf16x8_t, v);
+    }
   }
 };
 
@@ -225,15 +329,18 @@ __device__ __forceinline__ void interleave_reads() {
   sg_mfma_then_reads<NR, 7>();
 }
 
-struct Mainloop {
+// ASrc: BlockedA or RowA (already initialised by the caller); AFrag: the
+// matching fragment reader, FragSrc<4> or FragRow<4>.
+template <class ASrc, class AFrag>
+struct MainloopT {
   struct Frags {
     bf16x8_t a[4], b[2];
   };
-  FragSrc<4> fa;
+  AFrag fa;
   FragSrc<2> fb;
-  Dma da;
+  ASrc da;
   Dma db;
-  int a_kb0, b_kb0;
+  int b_kb0;
 
   __device__ __forceinline__ void frags(const char* a, const char* b, int kk, Frags& f) const {
     fa.read(a, kk, f.a);
@@ -249,12 +356,12 @@ struct Mainloop {
   // Block kt of the K range; past the range both operands get out-of-range
   // offsets.
   __device__ __forceinline__ void issue(char* a, char* b, int kt, int nk) const {
-    da.issue(a, kt < nk ? a_kb0 + kt : da.nkb);
+    da.issue(a, kt, nk);
     db.issue(b, kt < nk ? b_kb0 + kt : db.nkb);
   }
 
   // LDS fragment-read instructions per 16-wide K step.
-  static constexpr int kReads = 4 + 2;
+  static constexpr int kReads = AFrag::kReadsPerStep + FragSrc<2>::kReadsPerStep;
 
   // One K block, reading stage S: first the DMA of the block three ahead is
   // issued into the stage consumed last step; sub-step 1's fragments are read
@@ -282,12 +389,11 @@ struct Mainloop {
     interleave_reads<kReads>();
   }
 
-  // C tile = strip A x strip B over K blocks [akb0, akb0 + nk) of A and
-  // [bkb0, bkb0 + nk) of B. Leaves every DMA drained and the block
-  // synchronised, so callers may reuse the stage arrays afterwards.
+  // C tile = A x strip B over nk K blocks (B's from bkb0). Leaves every DMA
+  // drained and the block synchronised, so callers may reuse the stage arrays
+  // afterwards.
   __device__ __forceinline__ void run(char* const (&sa)[kStages], char* const (&sb)[kStages],
-                                      const Strip& A, int akb0, const Strip& B, int bkb0, int nk,
-                                      Acc& acc) {
+                                      const ASrc& A, const Strip& B, int bkb0, int nk, Acc& acc) {
     const int wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
 #pragma unroll
@@ -297,9 +403,8 @@ struct Mainloop {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     if (nk <= 0) return;
-    da.init(A);
+    da = A;
     db.init(B);
-    a_kb0 = akb0;
     b_kb0 = bkb0;
     fa.init(wm * 128);
     fb.init(wn * 64);
@@ -320,6 +425,16 @@ struct Mainloop {
     block_barrier();
   }
 };
+
+typedef MainloopT<BlockedA, FragSrc<4>> Mainloop;     // both operands blocked
+typedef MainloopT<RowA, FragRow<4>> MainloopRowA;     // A row-contiguous, B blocked
+
+// Blocked A operand descriptor for Mainloop::run.
+__device__ __forceinline__ BlockedA blocked_a(const Strip& s, int kb0) {
+  BlockedA a;
+  a.init(s, kb0);
+  return a;
+}
 
 // ---- small numeric helpers ---------------------------------------------------
 

@@ -1,13 +1,15 @@
 // Kernels of the fused linear cross-entropy + entropy head (gfx950).
 //
-// Forward:  fwd_prep, pack (weight^T, hidden) -> fwd_tile -> fwd_combine
-//           (-> fwd_mean)
-// Backward: bwd_prep, pack (weight^T, weight, hidden, hidden^T) -> per
-//           vocabulary chunk { bwd_dlogits -> bwd_dx -> bwd_dw (-> dw_reduce) }
+// Forward:  fwd_prep, pack (hidden) -> fwd_tile -> fwd_combine (-> fwd_mean)
+// Backward: bwd_prep, pack (hidden, hidden^T) -> per vocabulary chunk
+//           { pack (weight chunk) -> bwd_dlogits -> bwd_dx -> bwd_dw
+//             (-> dw_reduce) }
 //
-// Every GEMM operand is read in the blocked layout of flce_gemm.hpp; the pack
+// GEMM operands are read in the blocked layout of flce_gemm.hpp (the pack
 // kernels below build it from the caller's row-major tensors, and the
-// logit-gradient epilogue writes its output directly in it.
+// logit-gradient epilogue writes its output directly in it), except the
+// weight as the vocabulary x H operand of the logit tiles, which is read
+// row-contiguous from the caller's [H,V] tensor.
 //
 // The quantities follow the definition in verl pull request #462 ("Equivalent
 // compute logic"): per token the logsumexp of the logits, the entropy
@@ -143,13 +145,12 @@ __global__ void __launch_bounds__(256) pack_cols_kernel(const uint16_t* __restri
 // ---- forward: fused logit tiles + online row statistics ---------------------
 
 struct FwdTileArgs {
-  const uint16_t* wt;      // blocked weight^T of the chunk: strips of 256 vocabulary rows, K = H
+  const uint16_t* weight;  // [H,V]
   const uint16_t* xb;      // blocked hidden: strips of 256 tokens, K = H
   const int32_t* lab;      // [N], -1 = no label
   int64_t N, H, V;
-  int64_t v0;              // first vocabulary column of the chunk (multiple of 256)
   int hkb;                 // K blocks per strip, ceil(H / 32)
-  int VT, VTc, TB;         // vocabulary tiles (all, in the chunk), token blocks
+  int VT, TB;              // vocabulary tiles, token blocks
   int group;               // token blocks per XCD patch (see group_map)
   float cap, cap_k;        // softcap c and 2*log2(e)/c
   float4* part;            // [VT][N] {m, s, u, 0} per vocabulary tile
@@ -167,9 +168,10 @@ __device__ __forceinline__ void merge_state2(float& m, float& s, float& u, float
   m = mn;
 }
 
-// Block (tb, vt): tokens [256 tb, +256) against vocabulary [v0 + 256 vt, +256).
-// The MFMA tile is z^T: rows = vocabulary (A = weight^T strip), cols = tokens
-// (B = hidden strip), so each lane's 64 accumulators of one 32-column block
+// Block (tb, vt): tokens [256 tb, +256) against vocabulary [256 vt, +256).
+// The MFMA tile is z^T: rows = vocabulary (A = the [H,V] weight read
+// row-contiguous), cols = tokens (B = hidden strip), so each lane's 64
+// accumulators of one 32-column block
 // belong to one token and the row statistics need no cross-lane work until the
 // end. The block reduces its tile to (m, s, u) per token and stores it as the
 // tile's partial state.
@@ -178,18 +180,18 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(2, 2)))
 fwd_tile_kernel(FwdTileArgs a) {
   FLCE_DECLARE_STAGES(sa, sb);
-  int tb, vl;
-  group_map(xcd_remap(blockIdx.x, gridDim.x), a.TB, a.VTc, a.group, tb, vl);
+  int tb, vt;
+  group_map(xcd_remap(blockIdx.x, gridDim.x), a.TB, a.VT, a.group, tb, vt);
   const int lane = threadIdx.x & 63, lh = lane >> 5;
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t n0 = (int64_t)tb * kTile;
-  const int vt = (int)(a.v0 / kTile) + vl;  // vocabulary tile in the whole vocabulary
 
   Acc acc;
   {
-    Mainloop ml;
-    const int64_t sz = (int64_t)a.hkb * kBlockElems;
-    ml.run(sa, sb, Strip{a.wt + vl * sz, a.hkb}, 0, Strip{a.xb + tb * sz, a.hkb}, 0, a.hkb, acc);
+    MainloopRowA ml;
+    RowA A;
+    A.init(a.weight, a.V, a.V, (int64_t)vt * kTile, 0, a.H);
+    ml.run(sa, sb, A, Strip{a.xb + (int64_t)tb * a.hkb * kBlockElems, a.hkb}, 0, a.hkb, acc);
   }
 
   const int vb = vt * kTile + wm * 128;  // first vocabulary row of this wave
@@ -396,7 +398,7 @@ __global__ void __launch_bounds__(1024) bwd_prep_kernel(
 // ---- backward: recompute logits, form the logit gradient ----------------------
 
 struct DlogitsArgs {
-  const uint16_t* wt;      // blocked weight^T of the chunk (as in the forward)
+  const uint16_t* weight;  // [H,V]
   const uint16_t* xb;      // blocked hidden
   const float4* coef;      // [N]
   const int32_t* lab;      // [N]
@@ -431,9 +433,10 @@ bwd_dlogits_kernel(DlogitsArgs a) {
 
   Acc acc;
   {
-    Mainloop ml;
-    const int64_t sz = (int64_t)a.hkb * kBlockElems;
-    ml.run(sa, sb, Strip{a.wt + vt * sz, a.hkb}, 0, Strip{a.xb + tb * sz, a.hkb}, 0, a.hkb, acc);
+    MainloopRowA ml;
+    RowA A;
+    A.init(a.weight, a.V, a.V, vg0, 0, a.H);
+    ml.run(sa, sb, A, Strip{a.xb + (int64_t)tb * a.hkb * kBlockElems, a.hkb}, 0, a.hkb, acc);
   }
 
   // Each tile owns 8 consecutive K blocks in each image: dtv strip tb, blocks
@@ -526,7 +529,7 @@ bwd_dx_kernel(DxArgs a) {
   Acc acc;
   {
     Mainloop ml;
-    ml.run(sa, sb, Strip{a.dtv + (int64_t)tb * a.kbv * kBlockElems, a.kbv}, 0,
+    ml.run(sa, sb, blocked_a(Strip{a.dtv + (int64_t)tb * a.kbv * kBlockElems, a.kbv}, 0),
            Strip{a.wb + (int64_t)ht * a.kbv * kBlockElems, a.kbv}, 0, a.nk, acc);
   }
   const int64_t base = m0 * a.H + h0;
@@ -594,7 +597,7 @@ bwd_dw_kernel(DwArgs a) {
   Acc acc;
   {
     Mainloop ml;
-    ml.run(sa, sb, Strip{a.xtb + (int64_t)ht * a.kbn * kBlockElems, a.kbn}, kbeg,
+    ml.run(sa, sb, blocked_a(Strip{a.xtb + (int64_t)ht * a.kbn * kBlockElems, a.kbn}, kbeg),
            Strip{a.dvt + (int64_t)vt * a.kbn * kBlockElems, a.kbn}, kbeg, kend - kbeg, acc);
   }
   int64_t ld, base, span;
