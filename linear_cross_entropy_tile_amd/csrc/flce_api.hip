@@ -107,7 +107,7 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   p.f_zlab = off;
   off = align_up(off + 4 * (size_t)N);
   p.f_bsum = off;
-  off = align_up(off + (reduction == FLCE_REDUCTION_MEAN ? 16 * (size_t)ceil_div(N, 256) : 0));
+  off = align_up(off + (reduction == FLCE_REDUCTION_MEAN ? 16 * (size_t)ceil_div(N, kCombineTokens) : 0));
   p.f_xb = off;
   off = align_up(off + blk * (size_t)p.TB * (size_t)p.hkb);
   p.f_total = off;
@@ -318,14 +318,14 @@ flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t
       else
         fwd_tile_kernel<false><<<grid, kThreads, 0, st>>>(a);
     }));
-    const int nb = (int)ceil_div(N, 256);
+    const int nb = (int)ceil_div(N, kCombineTokens);
     FLCE_TRY(launch(K_FWD_COMBINE, st, [&] {
-      fwd_combine_kernel<<<nb, 256, 0, st>>>(part, p.VT, zlab, lab32, N, lse, logprob, entropy,
-                                             bsum);
+      fwd_combine_kernel<<<nb, 64 * kCombineWaves, 0, st>>>(part, p.VT, zlab, lab32, N, lse,
+                                                            logprob, entropy, bsum);
     }));
   }
   if (mean) {
-    const int nb = (int)ceil_div(N, 256);
+    const int nb = (int)ceil_div(N, kCombineTokens);
     FLCE_TRY(launch(K_FWD_MEAN, st, [&] {
       fwd_mean_kernel<<<1, 256, 0, st>>>(bsum, nb, header, logprob_mean, entropy_mean);
     }));

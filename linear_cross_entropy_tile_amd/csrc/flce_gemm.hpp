@@ -113,6 +113,13 @@ __device__ __forceinline__ void buf_store_u16(uint32_t v, __amdgpu_buffer_rsrc_t
 __device__ __forceinline__ void buf_store_u32x2(u32x2_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);
 }
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4_t buf_load_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+__device__ __forceinline__ void buf_store_f32x4(f32x4_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, voff, 0, 0);
+}
 
 // Keeps the compiler from hoisting work that depends on `x` out of a loop.
 template <class T>
@@ -458,8 +465,53 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
 }
+// Two floats -> packed bf16 pair (lo in the low half), round to nearest even,
+// with the gfx950 conversion instruction.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
+
+// 4 x 4 transpose of bf16 values across the lanes of a quad (lanes 4q..4q+3).
+// On entry lane 4q+a holds X[a][0..3] packed as p0 = (X[a][0], X[a][1]),
+// p1 = (X[a][2], X[a][3]); on return it holds (X[0][a], X[1][a]) and
+// (X[2][a], X[3][a]). Two DPP stages: swap 2 x 2 blocks between lanes a and
+// a ^ 2, then 16-bit halves between lanes a and a ^ 1.
+__device__ __forceinline__ u32x2_t quad_transpose_bf16(uint32_t p0, uint32_t p1) {
+  const int a = threadIdx.x & 3;
+  const bool lo = a < 2;
+  const uint32_t sel = lo ? p1 : p0;
+  const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)sel, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  const uint32_t q0 = lo ? p0 : recv, q1 = lo ? recv : p1;
+  const uint32_t o0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)q0, 0xB1, 0xF, 0xF, false);    // [1,0,3,2]
+  const uint32_t o1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)q1, 0xB1, 0xF, 0xF, false);
+  u32x2_t r;
+  if (a & 1) {
+    r[0] = (o0 >> 16) | (q0 & 0xFFFF0000u);
+    r[1] = (o1 >> 16) | (q1 & 0xFFFF0000u);
+  } else {
+    r[0] = (q0 & 0xFFFFu) | (o0 << 16);
+    r[1] = (q1 & 0xFFFFu) | (o1 << 16);
+  }
+  return r;
+}
+
+// The same transpose for fp32 values: lane 4q+a holds X[a][0..3] on entry and
+// returns (X[0][a], X[1][a], X[2][a], X[3][a]).
+__device__ __forceinline__ float dpp_f32(float x, int ctrl_is_swap2) {
+  const int v = __builtin_bit_cast(int, x);
+  return __builtin_bit_cast(float, ctrl_is_swap2 ? __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false)
+                                                 : __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ f32x4_t quad_transpose_f32(float x0, float x1, float x2, float x3) {
+  const int a = threadIdx.x & 3;
+  const bool lo = a < 2;
+  const float r0 = dpp_f32(lo ? x2 : x0, 1), r1 = dpp_f32(lo ? x3 : x1, 1);
+  const float y0 = lo ? x0 : r0, y1 = lo ? x1 : r1, y2 = lo ? r0 : x2, y3 = lo ? r1 : x3;
+  const bool ev = (a & 1) == 0;
+  const float u0 = dpp_f32(ev ? y1 : y0, 0), u1 = dpp_f32(ev ? y3 : y2, 0);
+  return ev ? f32x4_t{y0, u0, y2, u1} : f32x4_t{u0, y1, u1, y3};
 }
 
 }  // namespace flce

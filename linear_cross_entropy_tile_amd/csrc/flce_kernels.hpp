@@ -287,49 +287,74 @@ fwd_tile_kernel(FwdTileArgs a) {
 
 // ---- forward: merge the vocabulary splits -------------------------------------
 
-// One thread per token. Writes lse, logprob, entropy; with bsum != nullptr also
-// the block's sums of logprob and entropy over valid tokens (float64).
-__global__ void __launch_bounds__(256) fwd_combine_kernel(const float4* __restrict__ part, int S,
-                                                          const float* __restrict__ zlab,
-                                                          const int32_t* __restrict__ lab32,
-                                                          int64_t N, float* __restrict__ lse,
-                                                          float* __restrict__ logprob,
-                                                          float* __restrict__ entropy,
-                                                          double2* __restrict__ bsum) {
-  __shared__ double sh[256];
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  double slp = 0.0, sent = 0.0;
-  if (t < N) {
-    if (lab32[t] >= 0) {
-      float4 p = part[t];
-      float m = p.x, s = p.y, u = p.z;
-      for (int k = 1; k < S; ++k) {
-        const float4 q = part[(int64_t)k * N + t];
-        const float mn = fmaxf(m, q.x);
-        const float a1 = expf(m - mn), a2 = expf(q.x - mn);
-        u = a1 * fmaf(m - mn, s, u) + a2 * fmaf(q.x - mn, q.y, q.z);
-        s = a1 * s + a2 * q.y;
-        m = mn;
-      }
-      const float ls = logf(s);
-      const float l = m + ls;
-      const float e = ls - u / s;
-      const float lp = zlab[t] - l;
-      lse[t] = l;
-      entropy[t] = e;
-      logprob[t] = lp;
-      slp = lp;
-      sent = e;
-    } else {
-      lse[t] = 0.f;
-      entropy[t] = 0.f;
-      logprob[t] = 0.f;
+// Merge state (m2, s2, u2) into (m, s, u), natural-log units. An empty state
+// is (kNegBig, 0, 0).
+__device__ __forceinline__ void merge_state(float& m, float& s, float& u, float m2, float s2,
+                                            float u2) {
+  const float mn = fmaxf(m, m2);
+  const float a1 = expf(m - mn), a2 = expf(m2 - mn);
+  u = a1 * fmaf(m - mn, s, u) + a2 * fmaf(m2 - mn, s2, u2);
+  s = a1 * s + a2 * s2;
+  m = mn;
+}
+
+constexpr int kCombineTokens = 64;   // tokens per combine block (one per lane)
+constexpr int kCombineWaves = 16;    // vocabulary-tile groups per combine block
+
+// Block of 1024 threads for 64 tokens: wave w merges the partial states of
+// vocabulary tiles w, w + 16, ... of token t0 + lane (consecutive lanes read
+// consecutive 16-byte states), then wave 0 merges the 16 states in wave order
+// and writes lse, logprob, entropy. With bsum != nullptr it also writes the
+// block's float64 sums of logprob and entropy over valid tokens. Fixed merge
+// and summation orders: the result does not depend on timing.
+__global__ void __launch_bounds__(1024) fwd_combine_kernel(const float4* __restrict__ part, int S,
+                                                           const float* __restrict__ zlab,
+                                                           const int32_t* __restrict__ lab32,
+                                                           int64_t N, float* __restrict__ lse,
+                                                           float* __restrict__ logprob,
+                                                           float* __restrict__ entropy,
+                                                           double2* __restrict__ bsum) {
+  __shared__ float4 st[kCombineWaves][kCombineTokens];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * kCombineTokens + lane;
+  const bool valid = t < N && lab32[t] >= 0;
+  float m = kNegBig, s = 0.f, u = 0.f;
+  if (valid)
+    for (int k = w; k < S; k += kCombineWaves) {
+      const float4 q = part[(int64_t)k * N + t];
+      merge_state(m, s, u, q.x, q.y, q.z);
     }
+  st[w][lane] = make_float4(m, s, u, 0.f);
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll 1
+  for (int k = 1; k < kCombineWaves; ++k) {
+    const float4 q = st[k][lane];
+    merge_state(m, s, u, q.x, q.y, q.z);
+  }
+  double slp = 0.0, sent = 0.0;
+  if (valid) {
+    const float ls = logf(s);
+    const float l = m + ls;
+    const float e = ls - u / s;
+    const float lp = zlab[t] - l;
+    lse[t] = l;
+    entropy[t] = e;
+    logprob[t] = lp;
+    slp = lp;
+    sent = e;
+  } else if (t < N) {
+    lse[t] = 0.f;
+    entropy[t] = 0.f;
+    logprob[t] = 0.f;
   }
   if (bsum != nullptr) {
-    slp = block_sum<double, 256>(slp, sh);
-    sent = block_sum<double, 256>(sent, sh);
-    if (threadIdx.x == 0) bsum[blockIdx.x] = make_double2(slp, sent);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      slp += __shfl_xor(slp, o);
+      sent += __shfl_xor(sent, o);
+    }
+    if (lane == 0) bsum[blockIdx.x] = make_double2(slp, sent);
   }
 }
 
@@ -468,29 +493,30 @@ bwd_dlogits_kernel(DlogitsArgs a) {
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        uint32_t h[4];
+        float d[4];
 #pragma unroll
         for (int r3 = 0; r3 < 4; ++r3) {
-          const int r = rq * 4 + r3;
           const int o = i * 32 + 8 * rq + r3;
-          float z = acc[i][j][r];
+          float z = acc[i][j][rq * 4 + r3];
           if constexpr (CAP) z = softcap_apply(z, a.cap, a.cap_k);
           const float p = fast_exp2(fmaf(z, kLog2e, nl));
-          float d = fmaf(-p, fmaf(c.w, z, cS), o == yl ? c.z : 0.f);
+          float v = fmaf(-p, fmaf(c.w, z, cS), o == yl ? c.z : 0.f);
           if constexpr (CAP) {
             const float qz = z * a.inv_cap;
-            d *= fmaf(-qz, qz, 1.f);
+            v *= fmaf(-qz, qz, 1.f);
           }
-          if (!full) d = o < lim ? d : 0.f;
-          h[r3] = bf16_bits(d);
-          // dvt: row m (vocabulary), K = token n.
-          const int m = acc_row(wm, i, r, lane);
-          buf_store_u16(h[r3], rvt, (uint32_t)((wn * 2 + j) * kBlockBytes + blk_byte(m, lane & 31)));
+          d[r3] = full || o < lim ? v : 0.f;
         }
-        // dtv: row n (token), K = vocabulary rows m .. m+3 (one 8-byte piece).
+        // Rows m0 .. m0+3 (vocabulary) of token column n.
         const int m0 = acc_row(wm, i, rq * 4, lane);
-        const u32x2_t v2 = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-        buf_store_u32x2(v2, rtv, (uint32_t)((m0 >> 5) * kBlockBytes + blk_byte(n, m0 & 31)));
+        const uint32_t p0 = pack_bf16x2(d[0], d[1]), p1 = pack_bf16x2(d[2], d[3]);
+        // dtv: row n (token), K = vocabulary m0 .. m0+3: one 8-byte piece.
+        buf_store_u32x2(u32x2_t{p0, p1}, rtv, (uint32_t)((m0 >> 5) * kBlockBytes + blk_byte(n, m0 & 31)));
+        // dvt: after the quad transpose, lane 4q+a holds row m0 + a for the
+        // four token columns of its quad: one 8-byte piece at K = n & ~3.
+        const u32x2_t tv = quad_transpose_bf16(p0, p1);
+        buf_store_u32x2(tv, rvt, (uint32_t)((wn * 2 + j) * kBlockBytes +
+                                            blk_byte(m0 + (lane & 3), (lane & 31) & ~3)));
       }
     }
     __builtin_amdgcn_sched_barrier(0);  // one token column at a time
@@ -536,26 +562,34 @@ bwd_dx_kernel(DxArgs a) {
   const int64_t span = (a.N - m0) * a.H - h0;  // elements from the tile origin to the end
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gh + base, span * 2);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.acc + base, span * 4);
+  // Per 4 accumulator rows of a 32 x 32 block, a quad transpose hands lane
+  // 4q+a row (first + a) at the quad's four columns: 16-byte fp32 and 8-byte
+  // bf16 accesses. H is a multiple of 4, so a quad's columns are all inside or
+  // all outside.
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int hl = acc_col(wn, j, lane);
-    const bool hok = h0 + hl < a.H;
+    const int hq = acc_col(wn, j, lane) & ~3;
+    const bool hok = h0 + hq < a.H;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t e = (uint32_t)(acc_row(wm, i, r, lane) * a.H + hl);
-        const float v = acc[i][j][r];
+      for (int rq = 0; rq < 4; ++rq) {
+        const int row = acc_row(wm, i, rq * 4, lane) + (lane & 3);
+        const uint32_t e = (uint32_t)(row * a.H + hq);
+        const float x[4] = {acc[i][j][rq * 4], acc[i][j][rq * 4 + 1], acc[i][j][rq * 4 + 2],
+                            acc[i][j][rq * 4 + 3]};
         if constexpr (MODE == DX_ONLY) {
-          buf_store_u16(bf16_bits(v), rg, hok ? e * 2 : kOOB);
-        } else if constexpr (MODE == DX_FIRST) {
-          buf_store_f32(v, ra, hok ? e * 4 : kOOB);
-        } else if constexpr (MODE == DX_MID) {
-          const uint32_t o = hok ? e * 4 : kOOB;
-          buf_store_f32(buf_load_f32(ra, o) + v, ra, o);
+          const u32x2_t v = quad_transpose_bf16(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+          buf_store_u32x2(v, rg, hok ? e * 2 : kOOB);
         } else {
+          f32x4_t v = quad_transpose_f32(x[0], x[1], x[2], x[3]);
           const uint32_t o = hok ? e * 4 : kOOB;
-          buf_store_u16(bf16_bits(buf_load_f32(ra, o) + v), rg, hok ? e * 2 : kOOB);
+          if constexpr (MODE != DX_FIRST) v += buf_load_f32x4(ra, o);
+          if constexpr (MODE == DX_LAST)
+            buf_store_u32x2(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rg,
+                            hok ? e * 2 : kOOB);
+          else
+            buf_store_f32x4(v, ra, o);
         }
       }
       __builtin_amdgcn_sched_barrier(0);  // one 32 x 32 block at a time
@@ -612,20 +646,26 @@ bwd_dw_kernel(DwArgs a) {
   }
   const __amdgpu_buffer_rsrc_t rs =
       SPLIT ? make_rsrc(a.part + base, span * 4) : make_rsrc(a.gw + base, span * 2);
+  // Quad transposes as in bwd_dx_kernel; vc is a multiple of 8.
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int vl = acc_col(wn, j, lane);
-    const bool vok = vl0 + vl < a.vc;
+    const int vq = acc_col(wn, j, lane) & ~3;
+    const bool vok = vl0 + vq < a.vc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t e = (uint32_t)(acc_row(wm, i, r, lane) * ld + vl);
+      for (int rq = 0; rq < 4; ++rq) {
+        const int row = acc_row(wm, i, rq * 4, lane) + (lane & 3);
+        const uint32_t e = (uint32_t)(row * ld + vq);
+        const float x[4] = {acc[i][j][rq * 4], acc[i][j][rq * 4 + 1], acc[i][j][rq * 4 + 2],
+                            acc[i][j][rq * 4 + 3]};
         if constexpr (SPLIT)
-          buf_store_f32(acc[i][j][r], rs, vok ? e * 4 : kOOB);
+          buf_store_f32x4(quad_transpose_f32(x[0], x[1], x[2], x[3]), rs, vok ? e * 4 : kOOB);
         else
-          buf_store_u16(bf16_bits(acc[i][j][r]), rs, vok ? e * 2 : kOOB);
+          buf_store_u32x2(quad_transpose_bf16(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])), rs,
+                          vok ? e * 2 : kOOB);
       }
+    }
   }
 }
 
@@ -639,7 +679,7 @@ __global__ void __launch_bounds__(256) dw_reduce_kernel(const float* __restrict_
     const int64_t h = e / vc, v = e % vc;
     float s = 0.f;
     for (int k = 0; k < splits; ++k) s += part[((int64_t)k * H + h) * ldd + v];
-    gw[h * V + v0 + v] = (uint16_t)bf16_bits(s);
+    gw[h * V + v0 + v] = (uint16_t)(pack_bf16x2(s, 0.f) & 0xFFFFu);
   }
 }
 
