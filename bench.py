@@ -57,7 +57,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_head")
-    ap.add_argument("--cpu-tokens", type=int, default=512,
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of the CPU oracle sample (0 skips the CPU baseline)")
     ap.add_argument("--torch-ref", type=int, default=1,
                     help="also time a materialising torch fwd+bwd (0/1)")
