@@ -168,6 +168,55 @@ __device__ __forceinline__ void merge_state2(float& m, float& s, float& u, float
   m = mn;
 }
 
+// Online-softmax state of one token column j of a wave's 128 x 32 block
+// (64 accumulators per lane): m = max z', s = sum exp(z' - m),
+// u = sum exp(z' - m)(z' - m) in base-2 units. The capped logits are left in
+// z[] for the label capture. MASK drops rows at offset >= lim (the last
+// vocabulary tile only).
+template <bool CAP, bool MASK>
+__device__ __forceinline__ void column_stats(const Acc& acc, int j, float cap, float cap_k, int lim,
+                                             float (&z)[64], float& m, float& s, float& u) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = acc[i][j][r];
+      if constexpr (CAP) x = softcap_apply(x, cap, cap_k);
+      if constexpr (MASK) x = (i * 32 + 8 * (r >> 2) + (r & 3)) < lim ? x : kNegBig;
+      z[i * 16 + r] = x;
+    }
+  float mx[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float x = z[i * 16];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) x = fmaxf(x, z[i * 16 + r]);
+    mx[i] = x;
+  }
+  const float mb = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+  const float nm = -mb * kLog2e;
+  float sp[4], up[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sp[i] = 0.f;
+    up[i] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      // A masked entry sits at kNegBig: if some entry of the lane is valid,
+      // mb is finite, d is hugely negative and e = 0; if none is, mb is
+      // kNegBig itself and the select drops the entry.
+      const float d = fmaf(z[i * 16 + r], kLog2e, nm);
+      float e = fast_exp2(d);
+      if constexpr (MASK) e = z[i * 16 + r] == kNegBig ? 0.f : e;
+      sp[i] += e;
+      up[i] = fmaf(e, d, up[i]);
+    }
+  }
+  m = mb;
+  s = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+  u = (up[0] + up[1]) + (up[2] + up[3]);
+}
+
 // Block (tb, vt): tokens [256 tb, +256) against vocabulary [256 vt, +256).
 // The MFMA tile is z^T: rows = vocabulary (A = the [H,V] weight read
 // row-contiguous), cols = tokens (B = hidden strip), so each lane's 64
@@ -202,51 +251,18 @@ fwd_tile_kernel(FwdTileArgs a) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     float z[64];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = acc[i][j][r];
-        if constexpr (CAP) x = softcap_apply(x, a.cap, a.cap_k);
-        if (!full) x = (i * 32 + 8 * (r >> 2) + (r & 3)) < lim ? x : kNegBig;
-        z[i * 16 + r] = x;
-      }
-    float mx[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = z[i * 16];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) x = fmaxf(x, z[i * 16 + r]);
-      mx[i] = x;
-    }
-    const float mb = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-    const float nm = -mb * kLog2e;
-    float sp[4], up[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sp[i] = 0.f;
-      up[i] = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // A masked entry sits at kNegBig: if some entry of the lane is valid,
-        // mb is finite, d is hugely negative and e = 0; if none is, mb is
-        // kNegBig itself and the select drops the entry.
-        const float d = fmaf(z[i * 16 + r], kLog2e, nm);
-        float e = fast_exp2(d);
-        if (!full) e = z[i * 16 + r] == kNegBig ? 0.f : e;
-        sp[i] += e;
-        up[i] = fmaf(e, d, up[i]);
-      }
-    }
-    m[j] = mb;
-    s[j] = (sp[0] + sp[1]) + (sp[2] + sp[3]);
-    u[j] = (up[0] + up[1]) + (up[2] + up[3]);
+    if (full)
+      column_stats<CAP, false>(acc, j, a.cap, a.cap_k, lim, z, m[j], s[j], u[j]);
+    else
+      column_stats<CAP, true>(acc, j, a.cap, a.cap_k, lim, z, m[j], s[j], u[j]);
 
-    // The label's logit: exactly one lane of one block in the grid owns it.
+    // The label's logit: exactly one lane of one block in the grid owns it,
+    // and most waves own none (skipped by a wave-uniform test).
     const int64_t t = n0 + acc_col(wn, j, lane);
     const int y = t < a.N ? a.lab[t] : -1;
     const int off = y - vb;
-    if ((unsigned)off < 128u && (((off & 31) >> 2) & 1) == lh) {
+    const bool hit = (unsigned)off < 128u && (((off & 31) >> 2) & 1) == lh;
+    if (__builtin_amdgcn_ballot_w64(hit) != 0 && hit) {
       const int sel = (off >> 5) * 16 + ((((off & 31) >> 3) << 2) | (off & 3));
       float zl = 0.f;
 #pragma unroll
@@ -439,6 +455,62 @@ struct DlogitsArgs {
   uint16_t* dvt;           // blocked D^T, strips of 256 chunk vocabulary rows, K = tokens
 };
 
+// Per-token constants of the logit gradient.
+struct DzCoef {
+  float nl;       // -lse * log2(e)
+  float ebar;     // upstream entropy gradient
+  float cS;       // gbar - ebar * S
+  float gbar;     // upstream logprob gradient (the label term)
+  float cap, cap_k, inv_cap;
+};
+
+// The logit gradient of token column j of a wave's 128 x 32 block, rounded to
+// bf16, for both blocked images (see bwd_dlogits_kernel). LABEL adds gbar at
+// the label's row offset yl; MASK zeroes rows at offset >= lim.
+// The token-major image goes to LDS (`lds[i]` holds block 4 wm + i of the
+// tile's 8 dtv blocks) and is copied out by the caller; the vocabulary-major
+// image is stored directly.
+template <bool CAP, bool MASK, bool LABEL>
+__device__ __forceinline__ void dz_column(const Acc& acc, int j, const DzCoef& k, int yl, int lim,
+                                          int n, int wm, int wn, int lane, char* const (&lds)[kStages],
+                                          __amdgpu_buffer_rsrc_t rvt) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      float d[4];
+#pragma unroll
+      for (int r3 = 0; r3 < 4; ++r3) {
+        const int o = i * 32 + 8 * rq + r3;
+        float z = acc[i][j][rq * 4 + r3];
+        if constexpr (CAP) z = softcap_apply(z, k.cap, k.cap_k);
+        const float p = fast_exp2(fmaf(z, kLog2e, k.nl));
+        float v;
+        if constexpr (LABEL)
+          v = fmaf(-p, fmaf(k.ebar, z, k.cS), o == yl ? k.gbar : 0.f);
+        else
+          v = -p * fmaf(k.ebar, z, k.cS);
+        if constexpr (CAP) {
+          const float qz = z * k.inv_cap;
+          v *= fmaf(-qz, qz, 1.f);
+        }
+        if constexpr (MASK) v = o < lim ? v : 0.f;
+        d[r3] = v;
+      }
+      // Rows m0 .. m0+3 (vocabulary) of token column n.
+      const int m0 = acc_row(wm, i, rq * 4, lane);
+      const uint32_t p0 = pack_bf16x2(d[0], d[1]), p1 = pack_bf16x2(d[2], d[3]);
+      // dtv: row n (token), K = vocabulary m0 .. m0+3: one 8-byte piece.
+      *reinterpret_cast<u32x2_t*>(lds[i] + blk_byte(n, m0 & 31)) = u32x2_t{p0, p1};
+      // dvt: after the quad transpose, lane 4q+a holds row m0 + a for the
+      // four token columns of its quad: one 8-byte piece at K = n & ~3.
+      const u32x2_t tv = quad_transpose_bf16(p0, p1);
+      buf_store_u32x2(tv, rvt, (uint32_t)((wn * 2 + j) * kBlockBytes +
+                                          blk_byte(m0 + (lane & 3), (lane & 31) & ~3)));
+    }
+  }
+}
+
 // dz' = gbar ([v == y] - p) - ebar p (z' - S), dz = dz' (1 - (z'/c)^2) if
 // capped, rounded to bf16 and written into both blocked images of the chunk:
 // dtv (the A operand of dH = D W^T) and dvt (the B operand of dW = hidden^T D).
@@ -474,6 +546,11 @@ bwd_dlogits_kernel(DlogitsArgs a) {
   // vocabulary iff o < lim.
   const int lim = (int)(a.V - vg0) - wm * 128 - 4 * lh;
   const bool full = vg0 + kTile <= a.V;
+  // The stage arrays are free after the main loop: the tile's 8 dtv blocks
+  // (128 KiB) are assembled there, block b in sa[b] (b < 4) or sb[b - 4].
+  char* lds[kStages];
+#pragma unroll
+  for (int i = 0; i < kStages; ++i) lds[i] = wm ? sb[i] : sa[i];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int n = acc_col(wn, j, lane);
@@ -487,39 +564,33 @@ bwd_dlogits_kernel(DlogitsArgs a) {
     // The label's row offset within this lane's rows, or -1.
     const int64_t yo = (int64_t)y - vg0 - wm * 128 - 4 * lh;
     const int yl = (y >= 0 && yo >= 0 && yo < 128) ? (int)yo : -1;
-    const float nl = -c.x * kLog2e;
-    const float cS = c.z - c.w * c.y;  // gbar - ebar * S
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        float d[4];
-#pragma unroll
-        for (int r3 = 0; r3 < 4; ++r3) {
-          const int o = i * 32 + 8 * rq + r3;
-          float z = acc[i][j][rq * 4 + r3];
-          if constexpr (CAP) z = softcap_apply(z, a.cap, a.cap_k);
-          const float p = fast_exp2(fmaf(z, kLog2e, nl));
-          float v = fmaf(-p, fmaf(c.w, z, cS), o == yl ? c.z : 0.f);
-          if constexpr (CAP) {
-            const float qz = z * a.inv_cap;
-            v *= fmaf(-qz, qz, 1.f);
-          }
-          d[r3] = full || o < lim ? v : 0.f;
-        }
-        // Rows m0 .. m0+3 (vocabulary) of token column n.
-        const int m0 = acc_row(wm, i, rq * 4, lane);
-        const uint32_t p0 = pack_bf16x2(d[0], d[1]), p1 = pack_bf16x2(d[2], d[3]);
-        // dtv: row n (token), K = vocabulary m0 .. m0+3: one 8-byte piece.
-        buf_store_u32x2(u32x2_t{p0, p1}, rtv, (uint32_t)((m0 >> 5) * kBlockBytes + blk_byte(n, m0 & 31)));
-        // dvt: after the quad transpose, lane 4q+a holds row m0 + a for the
-        // four token columns of its quad: one 8-byte piece at K = n & ~3.
-        const u32x2_t tv = quad_transpose_bf16(p0, p1);
-        buf_store_u32x2(tv, rvt, (uint32_t)((wn * 2 + j) * kBlockBytes +
-                                            blk_byte(m0 + (lane & 3), (lane & 31) & ~3)));
-      }
+    const DzCoef k{-c.x * kLog2e, c.w, c.z - c.w * c.y, c.z, a.cap, a.cap_k, a.inv_cap};
+    // Wave-uniform choice of the variant: the label term is needed by few
+    // waves, the row mask only in the last vocabulary tile.
+    const bool any_label = __builtin_amdgcn_ballot_w64(yl >= 0) != 0;
+    if (full) {
+      if (any_label)
+        dz_column<CAP, false, true>(acc, j, k, yl, lim, n, wm, wn, lane, lds, rvt);
+      else
+        dz_column<CAP, false, false>(acc, j, k, yl, lim, n, wm, wn, lane, lds, rvt);
+    } else {
+      if (any_label)
+        dz_column<CAP, true, true>(acc, j, k, yl, lim, n, wm, wn, lane, lds, rvt);
+      else
+        dz_column<CAP, true, false>(acc, j, k, yl, lim, n, wm, wn, lane, lds, rvt);
     }
     __builtin_amdgcn_sched_barrier(0);  // one token column at a time
+  }
+  // Copy the dtv blocks out: each wave instruction stores 1 KiB of contiguous
+  // memory. Iteration it covers half of block it / 2.
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 2 * 2 * kStages; ++it) {
+    const int b = it >> 1;
+    const int off = ((it & 1) * kThreads + (int)threadIdx.x) * 16;
+    const char* src = (b < kStages ? sa[b % kStages] : sb[b % kStages]) + off;
+    __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t*>(src), rtv,
+                                           (uint32_t)(b * kBlockBytes + off), 0, 0);
   }
 }
 
