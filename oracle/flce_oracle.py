@@ -41,6 +41,18 @@ Readings taken where the pages are silent or ambiguous:
   R6  Upstream gradients: under "none" one value per token for each output
       ([liger-435]: a non-scalar output needs an explicit per-element
       gradient); under "mean" one scalar per output, applied to the mean.
+  R7  reduction="sum" sums each output over the valid tokens (the
+      reduction modes the [liger-435] Summary refers to); its scalar upstream
+      gradients apply undivided. With n = 0 the sums are 0.
+  R8  Z-loss. The [liger-551] review names a fused "Z loss" without a
+      formula; it is taken as the usual auxiliary term z_loss = lam * lse^2 per
+      valid token (lam >= 0 a scale), computed on the capped logits.
+  R9  Label smoothing. The [liger-551] review lists label smoothing among the
+      fused options, again without a formula. The head exposes the building
+      block uniform_ce = lse - (1/V) sum_j z'_j, the cross-entropy against the
+      uniform distribution; the smoothed cross-entropy with weight eps is
+      (1 - eps) * (-logprob) + eps * uniform_ce, which is how
+      torch.nn.functional.cross_entropy defines label_smoothing.
 """
 from __future__ import annotations
 
@@ -123,17 +135,23 @@ def _valid_mask(labels, V, ignore_index):
     return labels, valid
 
 
+_REDUCTIONS = ("none", "mean", "sum")
+_OUTPUTS = ("logprob", "entropy", "uniform_ce", "z_loss")
+
+
 def forward(hidden, weight, labels, ignore_index=-100, softcap_c=0.0,
-            reduction="none", row_block=_ROW_BLOCK):
-    """Per-token lse, logprob and entropy, plus the means under "mean".
+            reduction="none", z_loss_scale=0.0, row_block=_ROW_BLOCK):
+    """Per-token lse, logprob, entropy, uniform_ce and z_loss, plus their
+    reductions under "mean" (keys ``<output>_mean``) and "sum" (``<output>_sum``).
 
     [verl-462] "Equivalent compute logic" (lse and entropy per token;
     logprobs = -cross_entropy) with the cap of [liger-127], the ignore rule and
-    the mean of [liger-551] (readings R1 to R4), and per-token outputs under
-    "none" as in [liger-435] Summary.
+    the mean of [liger-551] (readings R1 to R4), per-token outputs under
+    "none" as in [liger-435] Summary, the sum of R7 and the two auxiliary
+    outputs of R8 and R9.
     """
-    if reduction not in ("none", "mean"):
-        raise ValueError("reduction must be 'none' or 'mean'")
+    if reduction not in _REDUCTIONS:
+        raise ValueError("reduction must be 'none', 'mean' or 'sum'")
     N = hidden.shape[0]
     V = weight.shape[1]
     labels, valid = _valid_mask(labels, V, ignore_index)
@@ -141,6 +159,7 @@ def forward(hidden, weight, labels, ignore_index=-100, softcap_c=0.0,
     lse = np.zeros(N)
     lp = np.zeros(N)
     ent = np.zeros(N)
+    uce = np.zeros(N)
     for r0 in range(0, N, row_block):
         rows = np.arange(r0, min(N, r0 + row_block))
         rows = rows[valid[rows]]
@@ -151,20 +170,27 @@ def forward(hidden, weight, labels, ignore_index=-100, softcap_c=0.0,
         lse[rows] = l_
         ent[rows] = e_
         lp[rows] = zc[np.arange(rows.size), labels[rows]] - l_
+        uce[rows] = l_ - zc.mean(axis=1)
+    zl = z_loss_scale * lse * lse
     n = int(valid.sum())
-    out = {"lse": lse, "logprob": lp, "entropy": ent, "n_valid": n}
-    if reduction == "mean":
-        out["logprob_mean"] = float(lp[valid].sum() / n) if n else 0.0
-        out["entropy_mean"] = float(ent[valid].sum() / n) if n else 0.0
+    out = {"lse": lse, "logprob": lp, "entropy": ent, "uniform_ce": uce, "z_loss": zl,
+           "n_valid": n}
+    for name in _OUTPUTS:
+        tot = float(out[name][valid].sum())
+        if reduction == "mean":
+            out[name + "_mean"] = tot / n if n else 0.0
+        elif reduction == "sum":
+            out[name + "_sum"] = tot
     return out
 
 
-def _token_grads(labels, valid, reduction, grad_logprob, grad_entropy):
-    """Per-token upstream gradients (g_bar, e_bar) of logprob and entropy.
+def _token_grads(labels, valid, reduction, *grads):
+    """Per-token upstream gradients of the outputs, in the order given.
 
     "none": one value per token ([liger-435], "Why we pass gradient to
     output.backward()"); None means zero. "mean": the scalar gradient of each
-    mean, divided by n on valid tokens (reading R3). Ignored tokens get 0.
+    mean, divided by n on valid tokens (reading R3). "sum": the scalar
+    gradient of each sum (reading R7). Ignored tokens get 0.
     """
     N = labels.shape[0]
     n = int(valid.sum())
@@ -178,40 +204,54 @@ def _token_grads(labels, valid, reduction, grad_logprob, grad_entropy):
                 raise ValueError("reduction='none' needs one gradient per token")
             return g.copy()
         if g.size != 1:
-            raise ValueError("reduction='mean' needs one scalar gradient")
+            raise ValueError("reduction='%s' needs one scalar gradient" % reduction)
+        if reduction == "sum":
+            return np.full(N, g[0])
         return np.full(N, g[0] / n if n else 0.0)
 
-    gb = expand(grad_logprob)
-    eb = expand(grad_entropy)
-    gb[~valid] = 0.0
-    eb[~valid] = 0.0
-    return gb, eb
+    out = []
+    for g in grads:
+        e = expand(g)
+        e[~valid] = 0.0
+        out.append(e)
+    return tuple(out)
 
 
-def dlogits(zc, labels_rows, lse, s, gbar, ebar, c):
-    """Gradient of g_bar * logprob + e_bar * entropy w.r.t. the raw logits z.
+def dlogits(zc, labels_rows, lse, s, gbar, ebar, c, gunif=None, gzl=None, z_loss_scale=0.0):
+    """Gradient of g_bar * logprob + e_bar * entropy + g_u * uniform_ce +
+    g_z * z_loss w.r.t. the raw logits z.
 
     Derivation from the definitions of [verl-462] (chain rule, float64):
-      d logprob / d z'_j = [j == y] - p_j
-      d entropy / d z'_j = -p_j (z'_j - S),  S = sum_k p_k z'_k
+      d logprob / d z'_j    = [j == y] - p_j
+      d entropy / d z'_j    = -p_j (z'_j - S),  S = sum_k p_k z'_k
+      d uniform_ce / d z'_j = p_j - 1/V                      (reading R9)
+      d z_loss / d z'_j     = 2 lam lse p_j                  (reading R8)
     then the cap's chain rule factor 1 - (z'/c)^2 ([liger-127]).
     """
+    V = zc.shape[1]
     p = np.exp(zc - lse[:, None])
     onehot = np.zeros_like(zc)
     hit = gbar != 0.0
     onehot[np.arange(zc.shape[0])[hit], labels_rows[hit]] = 1.0
     dzc = gbar[:, None] * (onehot - p) - ebar[:, None] * p * (zc - s[:, None])
+    if gunif is not None:
+        dzc = dzc + gunif[:, None] * (p - 1.0 / V)
+    if gzl is not None:
+        dzc = dzc + (2.0 * z_loss_scale * gzl * lse)[:, None] * p
     return dzc * softcap_grad(zc, c)
 
 
-def _block_dz(hidden, w, labels, rows, gb, eb, softcap_c):
+def _block_dz(hidden, w, labels, rows, grads, softcap_c, z_loss_scale):
+    gb, eb, gu, gz = grads
     zc = logits(hidden[rows], w, softcap_c)
     l_, s_, _, _ = row_stats(zc)
-    return dlogits(zc, labels[rows], l_, s_, gb[rows], eb[rows], softcap_c)
+    return dlogits(zc, labels[rows], l_, s_, gb[rows], eb[rows], softcap_c,
+                   gu[rows], gz[rows], z_loss_scale)
 
 
 def backward(hidden, weight, labels, ignore_index=-100, softcap_c=0.0,
              reduction="none", grad_logprob=None, grad_entropy=None,
+             grad_uniform_ce=None, grad_z_loss=None, z_loss_scale=0.0,
              row_block=_ROW_BLOCK):
     """dHidden [N,H] and dWeight [H,V] in float64.
 
@@ -222,7 +262,8 @@ def backward(hidden, weight, labels, ignore_index=-100, softcap_c=0.0,
     N, H = hidden.shape
     V = weight.shape[1]
     labels, valid = _valid_mask(labels, V, ignore_index)
-    gb, eb = _token_grads(labels, valid, reduction, grad_logprob, grad_entropy)
+    grads = _token_grads(labels, valid, reduction, grad_logprob, grad_entropy,
+                         grad_uniform_ce, grad_z_loss)
     w = _as_f64(weight)
     dh = np.zeros((N, H))
     dw = np.zeros((H, V))
@@ -231,31 +272,34 @@ def backward(hidden, weight, labels, ignore_index=-100, softcap_c=0.0,
         rows = rows[valid[rows]]
         if rows.size == 0:
             continue
-        dz = _block_dz(hidden, w, labels, rows, gb, eb, softcap_c)
+        dz = _block_dz(hidden, w, labels, rows, grads, softcap_c, z_loss_scale)
         dh[rows] = dz @ w.T
         dw += _as_f64(hidden[rows]).T @ dz
     return dh, dw
 
 
 def dhidden_rows(hidden, weight, labels, rows, ignore_index=-100, softcap_c=0.0,
-                 reduction="none", grad_logprob=None, grad_entropy=None):
+                 reduction="none", grad_logprob=None, grad_entropy=None,
+                 grad_uniform_ce=None, grad_z_loss=None, z_loss_scale=0.0):
     """Rows ``rows`` of dHidden. A row of dH depends only on its own token
     (and on n under "mean", so all labels are passed)."""
     V = weight.shape[1]
     labels, valid = _valid_mask(labels, V, ignore_index)
-    gb, eb = _token_grads(labels, valid, reduction, grad_logprob, grad_entropy)
+    grads = _token_grads(labels, valid, reduction, grad_logprob, grad_entropy,
+                         grad_uniform_ce, grad_z_loss)
     rows = np.asarray(rows, dtype=np.int64)
     out = np.zeros((rows.size, hidden.shape[1]))
     keep = valid[rows]
     if keep.any():
         w = _as_f64(weight)
-        dz = _block_dz(hidden, w, labels, rows[keep], gb, eb, softcap_c)
+        dz = _block_dz(hidden, w, labels, rows[keep], grads, softcap_c, z_loss_scale)
         out[keep] = dz @ w.T
     return out
 
 
 def dweight_columns(hidden, weight, labels, cols, ignore_index=-100, softcap_c=0.0,
                     reduction="none", grad_logprob=None, grad_entropy=None,
+                    grad_uniform_ce=None, grad_z_loss=None, z_loss_scale=0.0,
                     row_block=_ROW_BLOCK):
     """Columns ``cols`` of dWeight, i.e. dW[:, cols] = hidden^T @ dZ[:, cols].
 
@@ -264,7 +308,8 @@ def dweight_columns(hidden, weight, labels, cols, ignore_index=-100, softcap_c=0
     N, H = hidden.shape
     V = weight.shape[1]
     labels, valid = _valid_mask(labels, V, ignore_index)
-    gb, eb = _token_grads(labels, valid, reduction, grad_logprob, grad_entropy)
+    grads = _token_grads(labels, valid, reduction, grad_logprob, grad_entropy,
+                         grad_uniform_ce, grad_z_loss)
     cols = np.asarray(cols, dtype=np.int64)
     w = _as_f64(weight)
     out = np.zeros((H, cols.size))
@@ -273,6 +318,6 @@ def dweight_columns(hidden, weight, labels, cols, ignore_index=-100, softcap_c=0
         rows = rows[valid[rows]]
         if rows.size == 0:
             continue
-        dz = _block_dz(hidden, w, labels, rows, gb, eb, softcap_c)
+        dz = _block_dz(hidden, w, labels, rows, grads, softcap_c, z_loss_scale)
         out += _as_f64(hidden[rows]).T @ dz[:, cols]
     return out

@@ -9,7 +9,8 @@ Sources of truth used here, none of which is the oracle's own code path:
     logits, zero-weight gradient);
   * invariants of softmax, entropy and the tanh cap;
   * torch float64 library routines on the CPU (logsumexp, cross_entropy with
-    ignore_index and reductions, Categorical.entropy, autograd);
+    ignore_index, reductions and label_smoothing, Categorical.entropy,
+    autograd);
   * central finite differences of the oracle's forward.
 """
 from __future__ import annotations
@@ -302,7 +303,137 @@ def pin_sampled_helpers():
     return max(np.abs(a - dh[rows]).max(), np.abs(b - dw[:, cols]).max()), 1e-12
 
 
+# ---------------------------------------------------------------- auxiliary outputs
+
+def pin_aux_closed_forms():
+    """W = 0: every logit is 0, so uniform_ce = ln V and z_loss = lam (ln V)^2;
+    on random logits 0 <= lse - max z' <= uniform_ce <= lse - min z'."""
+    err = 0.0
+    for V in (7, 4096):
+        h = np.random.default_rng(V + 1).standard_normal((3, 2))
+        out = O.forward(h, np.zeros((2, V)), np.array([0, V - 1, 1]), z_loss_scale=0.25)
+        lnV = math.log(V)
+        err = max(err, np.abs(out["uniform_ce"] - lnV).max(),
+                  np.abs(out["z_loss"] - 0.25 * lnV * lnV).max())
+    h, w, y, c = _rand_case(60, N=10, H=6, V=11, wstd=1.5, ignore_rows=(3,), c=2.0)
+    out = O.forward(h, w, y, softcap_c=c)
+    zc = O.softcap(h @ w, c)
+    valid = y != -100
+    u = out["uniform_ce"][valid]
+    lo = out["lse"][valid] - zc[valid].max(axis=1)
+    hi = out["lse"][valid] - zc[valid].min(axis=1)
+    viol = max(0.0, (lo - u).max(), (u - hi).max(), -lo.min())
+    return max(err, viol, np.abs(out["uniform_ce"][~valid]).max()), TOL_CLOSED
+
+
+def pin_library_label_smoothing():
+    """(1 - eps) logprob - eps uniform_ce equals -F.cross_entropy(...,
+    label_smoothing=eps) per token ('none') and for 'sum' and 'mean', with an
+    ignored token, cap off and on."""
+    err = 0.0
+    for seed, c, eps in ((61, 0.0, 0.1), (62, 2.5, 0.3)):
+        h, w, y, _ = _rand_case(seed, N=12, H=8, V=15, wstd=1.2, ignore_rows=(0, 5), c=c)
+        zt = torch.as_tensor(O.softcap(h @ w, c))
+        yt = torch.as_tensor(y)
+        for red in ("none", "sum", "mean"):
+            out = O.forward(h, w, y, softcap_c=c, reduction=red)
+            ref = -F.cross_entropy(zt, yt, ignore_index=-100, label_smoothing=eps, reduction=red)
+            if red == "none":
+                mine = (1 - eps) * out["logprob"] - eps * out["uniform_ce"]
+                err = max(err, np.abs(mine - ref.numpy()).max())
+            else:
+                mine = (1 - eps) * out["logprob_" + red] - eps * out["uniform_ce_" + red]
+                err = max(err, abs(mine - ref.item()))
+    return err, TOL_LIB
+
+
+def pin_library_sum():
+    """'sum': logprob_sum = -F.cross_entropy(..., reduction='sum'),
+    entropy_sum = sum of Categorical(logits).entropy() over valid tokens,
+    z_loss_sum = lam * sum of torch.logsumexp^2 over valid tokens."""
+    err = 0.0
+    for seed, c in ((63, 0.0), (64, 1.7)):
+        h, w, y, _ = _rand_case(seed, N=10, H=7, V=13, wstd=1.1, ignore_rows=(2, 9), c=c)
+        out = O.forward(h, w, y, softcap_c=c, reduction="sum", z_loss_scale=0.3)
+        z, lse, lp, ent = _torch_forward(h, w, y, c)
+        valid = y != -100
+        ce_sum = F.cross_entropy(z, torch.as_tensor(y), ignore_index=-100, reduction="sum").item()
+        err = max(err, abs(out["logprob_sum"] + ce_sum),
+                  abs(out["entropy_sum"] - ent.numpy()[valid].sum()),
+                  abs(out["z_loss_sum"] - 0.3 * (lse.numpy()[valid] ** 2).sum()))
+    return err, TOL_LIB
+
+
+def pin_library_aux_grads():
+    """Gradients vs torch autograd (float64): of
+    F.cross_entropy(..., label_smoothing=eps, reduction='sum') (= the oracle's
+    backward with grad_logprob = -(1 - eps), grad_uniform_ce = eps under
+    'sum') and of lam * sum torch.logsumexp(z')^2 (grad_z_loss = 1), cap off
+    and on, with an ignored token."""
+    err = 0.0
+    for seed, c, eps, lam in ((65, 0.0, 0.2, 0.1), (66, 2.0, 0.05, 0.7)):
+        h, w, y, _ = _rand_case(seed, N=6, H=5, V=8, wstd=1.0, ignore_rows=(3,), c=c)
+        ht = torch.tensor(h, requires_grad=True)
+        wt = torch.tensor(w, requires_grad=True)
+        z = ht @ wt
+        if c > 0:
+            z = c * torch.tanh(z / c)
+        yt = torch.as_tensor(y)
+        valid = (yt != -100).to(torch.float64)
+        loss = F.cross_entropy(z, yt, ignore_index=-100, label_smoothing=eps, reduction="sum")
+        loss = loss + lam * (torch.logsumexp(z, dim=-1) ** 2 * valid).sum()
+        loss.backward()
+        dh, dw = O.backward(h, w, y, softcap_c=c, reduction="sum", grad_logprob=np.array([-(1 - eps)]),
+                            grad_uniform_ce=np.array([eps]), grad_z_loss=np.array([1.0]),
+                            z_loss_scale=lam)
+        scale = max(np.abs(ht.grad.numpy()).max(), np.abs(wt.grad.numpy()).max())
+        err = max(err, np.abs(dh - ht.grad.numpy()).max() / scale,
+                  np.abs(dw - wt.grad.numpy()).max() / scale)
+    return err, TOL_LIB
+
+
+def _aux_objective(h, w, y, c, red, gs, lam):
+    out = O.forward(h, w, y, softcap_c=c, reduction=red, z_loss_scale=lam)
+    names = ("logprob", "entropy", "uniform_ce", "z_loss")
+    if red == "none":
+        return float(sum((g * out[k]).sum() for g, k in zip(gs, names)))
+    return float(sum(g[0] * out[k + "_" + red] for g, k in zip(gs, names)))
+
+
+def pin_aux_finite_differences():
+    """Central differences of g.logprob + e.entropy + u.uniform_ce + q.z_loss
+    (none / sum / mean, cap off and on, an ignored token) vs the backward."""
+    worst = 0.0
+    step = 1e-6
+    for seed, c, red, lam in ((67, 0.0, "none", 0.2), (68, 2.0, "sum", 0.5), (69, 1.5, "mean", 0.3)):
+        h, w, y, _ = _rand_case(seed, N=4, H=3, V=6, wstd=1.0, ignore_rows=(2,), c=c)
+        rng = np.random.default_rng(seed + 11)
+        gs = [rng.standard_normal(4) if red == "none" else rng.standard_normal(1) for _ in range(4)]
+        dh, dw = O.backward(h, w, y, softcap_c=c, reduction=red, grad_logprob=gs[0],
+                            grad_entropy=gs[1], grad_uniform_ce=gs[2], grad_z_loss=gs[3],
+                            z_loss_scale=lam)
+        fdh = np.zeros_like(h)
+        fdw = np.zeros_like(w)
+        for arr, out in ((h, fdh), (w, fdw)):
+            for idx in np.ndindex(arr.shape):
+                old = arr[idx]
+                arr[idx] = old + step
+                fp = _aux_objective(h, w, y, c, red, gs, lam)
+                arr[idx] = old - step
+                fm = _aux_objective(h, w, y, c, red, gs, lam)
+                arr[idx] = old
+                out[idx] = (fp - fm) / (2 * step)
+        scale = max(np.abs(fdh).max(), np.abs(fdw).max())
+        worst = max(worst, np.abs(dh - fdh).max() / scale, np.abs(dw - fdw).max() / scale)
+    return worst, TOL_FD
+
+
 ALL_PINS = [
+    pin_aux_closed_forms,
+    pin_library_label_smoothing,
+    pin_library_sum,
+    pin_library_aux_grads,
+    pin_aux_finite_differences,
     pin_zero_weight_forward,
     pin_dominant_logit,
     pin_k_tied,

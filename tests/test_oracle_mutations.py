@@ -15,8 +15,8 @@ import oracle_pins as P
 def _entropy_sign(mp):
     orig = O.dlogits
 
-    def bad(zc, y, lse, s, g, e, c):
-        return orig(zc, y, lse, s, g, -e, c)
+    def bad(zc, y, lse, s, g, e, c, *rest):
+        return orig(zc, y, lse, s, g, -e, c, *rest)
     mp.setattr(O, "dlogits", bad)
 
 
@@ -68,15 +68,15 @@ def _no_cap_in_logits(mp):
 def _entropy_grad_uses_lse(mp):
     orig = O.dlogits
 
-    def bad(zc, y, lse, s, g, e, c):
-        return orig(zc, y, lse, lse, g, e, c)
+    def bad(zc, y, lse, s, g, e, c, *rest):
+        return orig(zc, y, lse, lse, g, e, c, *rest)
     mp.setattr(O, "dlogits", bad)
 
 
 def _onehot_dropped(mp):
     orig = O.dlogits
 
-    def bad(zc, y, lse, s, g, e, c):
+    def bad(zc, y, lse, s, g, e, c, *rest):
         p = np.exp(zc - lse[:, None])
         d = -g[:, None] * p - e[:, None] * p * (zc - s[:, None])
         return d * O.softcap_grad(zc, c)
@@ -86,15 +86,60 @@ def _onehot_dropped(mp):
 def _transposed_weight_in_dh(mp):
     orig = O._block_dz
 
-    def bad(hidden, w, labels, rows, gb, eb, c):
+    def bad(*args):
         # reverses the vocabulary order of dZ: as if W^T were indexed backwards
-        return orig(hidden, w, labels, rows, gb, eb, c)[:, ::-1]
+        return orig(*args)[:, ::-1]
     mp.setattr(O, "_block_dz", bad)
+
+
+def _uniform_grad_drops_inv_v(mp):
+    orig = O.dlogits
+
+    def bad(zc, y, lse, s, g, e, c, gu=None, gz=None, lam=0.0):
+        d = orig(zc, y, lse, s, g, e, c, None, gz, lam)
+        if gu is not None:
+            d = d + (gu[:, None] * np.exp(zc - lse[:, None])) * O.softcap_grad(zc, c)
+        return d
+    mp.setattr(O, "dlogits", bad)
+
+
+def _zloss_grad_no_factor2(mp):
+    orig = O.dlogits
+
+    def bad(zc, y, lse, s, g, e, c, gu=None, gz=None, lam=0.0):
+        return orig(zc, y, lse, s, g, e, c, gu, gz, lam / 2)
+    mp.setattr(O, "dlogits", bad)
+
+
+def _sum_divides_by_n(mp):
+    orig = O.forward
+
+    def bad(h, w, y, *a, **k):
+        out = orig(h, w, y, *a, **k)
+        n = out["n_valid"]
+        for key in list(out):
+            if key.endswith("_sum") and n:
+                out[key] = out[key] / n
+        return out
+    mp.setattr(O, "forward", bad)
+
+
+def _uniform_ce_sums_logits(mp):
+    orig = O.forward
+
+    def bad(h, w, y, *a, **k):
+        out = orig(h, w, y, *a, **k)
+        V = w.shape[1]
+        valid = np.asarray(y) != -100
+        out["uniform_ce"] = np.where(valid, out["lse"] - V * (out["lse"] - out["uniform_ce"]), 0.0)
+        return out
+    mp.setattr(O, "forward", bad)
 
 
 MUTATIONS = [_entropy_sign, _drop_cap_factor, _cap_factor_not_squared, _label_off_by_one,
              _entropy_plus, _mean_over_all_tokens, _no_cap_in_logits, _entropy_grad_uses_lse,
-             _onehot_dropped, _transposed_weight_in_dh]
+             _onehot_dropped, _transposed_weight_in_dh, _uniform_grad_drops_inv_v,
+             _zloss_grad_no_factor2, _sum_divides_by_n, _uniform_ce_sums_logits]
 
 
 def test_pins_pass_unmutated():
