@@ -12,7 +12,16 @@
  *   entropy_i = lse_i - sum_j p_ij z'_ij,  p_ij = exp(z'_ij - lse_i)
  *
  * and the gradients of  sum_i gbar_i logprob_i + ebar_i entropy_i  with respect
- * to hidden and weight.
+ * to hidden and weight. The extended entry points (flce_forward_ex,
+ * flce_backward_ex) add two per-token outputs with their gradients:
+ *
+ *   uniform_ce_i = lse_i - (1/V) sum_j z'_ij    (cross-entropy against the uniform
+ *                                                distribution: with weight eps,
+ *                                                (1-eps)(-logprob) + eps uniform_ce
+ *                                                is the label-smoothed cross-entropy)
+ *   z_loss_i     = lam * lse_i^2                (z-loss with scale lam)
+ *
+ * a "sum" reduction, and fp32 gradient outputs.
  *
  * Sources: verl pull request #462 (memory-efficient linear_cross_entropy),
  * sections "Equivalent compute logic" (the definition above, and that logprobs
@@ -30,11 +39,17 @@
  * matmul; discussion: tanh cap, gradients of hidden and weight by the chain
  * rule).
  *
+ * The review thread of Liger-Kernel pull request #551 names a fused z-loss,
+ * label smoothing and a sum reduction among the options of such a head,
+ * without formulas; the definitions above are the usual ones (the smoothed
+ * cross-entropy as torch.nn.functional.cross_entropy defines label_smoothing).
+ *
  * Readings where those pages are silent:
- *   - A token whose label equals ignore_index gets lse = logprob = entropy = 0
+ *   - A token whose label equals ignore_index gets every per-token output 0
  *     and no gradient, and is not counted by the mean.
- *   - reduction MEAN reduces both outputs over the n non-ignored tokens (n = 0
- *     gives 0); the per-token vectors are written under both reductions.
+ *   - reduction MEAN reduces each output over the n non-ignored tokens (n = 0
+ *     gives 0), SUM sums them; the per-token vectors are written under every
+ *     reduction.
  *   - A label that is neither ignore_index nor in [0, V) is treated as ignored
  *     and counted in the workspace status word (see flce_get_status).
  *
@@ -67,26 +82,31 @@ typedef enum {
   FLCE_OK = 0,
   FLCE_ERR_NULL_POINTER = 1,      /* a required pointer is NULL */
   FLCE_ERR_BAD_SHAPE = 2,         /* N < 0, H < 1, V < 1, or a size beyond the limits below */
-  FLCE_ERR_BAD_REDUCTION = 3,     /* reduction not FLCE_REDUCTION_NONE / _MEAN */
+  FLCE_ERR_BAD_REDUCTION = 3,     /* reduction not FLCE_REDUCTION_NONE / _MEAN / _SUM */
   FLCE_ERR_MISALIGNED = 4,        /* see "Alignment" above */
   FLCE_ERR_WORKSPACE_TOO_SMALL = 5,
   FLCE_ERR_BAD_SOFTCAP = 6,       /* softcap is NaN or infinite */
   FLCE_ERR_HIP = 7,               /* a HIP runtime call or kernel launch failed */
-  FLCE_ERR_INVALID_LABEL = 8      /* reported only by flce_get_status */
+  FLCE_ERR_INVALID_LABEL = 8,     /* reported only by flce_get_status */
+  FLCE_ERR_BAD_OPTION = 9         /* z_loss_scale negative or not finite, unknown grad_dtype */
 } flce_status_t;
 
-enum { FLCE_REDUCTION_NONE = 0, FLCE_REDUCTION_MEAN = 1 };
+enum { FLCE_REDUCTION_NONE = 0, FLCE_REDUCTION_MEAN = 1, FLCE_REDUCTION_SUM = 2 };
+enum { FLCE_GRAD_BF16 = 0, FLCE_GRAD_F32 = 1 };
 
-/* Size limits: N <= 2^21, H <= 2^20, V <= 2^22 (FLCE_ERR_BAD_SHAPE beyond). */
+/* Size limits: N <= 2^21, H <= 2^20, V <= 2^22 - 256, and V <= 2^21 with
+ * fp32 gradient outputs (FLCE_ERR_BAD_SHAPE beyond). */
 
-/* Workspace bytes needed by flce_forward (*fwd_bytes) and flce_backward
- * (*bwd_bytes) for this shape. Host only; either out-pointer may be NULL.
- * The forward size is about 16 * N * ceil(V/256) bytes (one partial softmax
- * state per token and 256-wide vocabulary tile). The backward size holds a
- * bounded bf16 slice of the logit gradient (N x Vc with 2*N*Vc <= 512 MiB
- * unless Vc is at its floor of 2048 columns; independent of V) and, when that
- * slice does not cover the whole vocabulary, an fp32 accumulator of N*H*4
- * bytes. */
+/* Workspace bytes needed by the forward (*fwd_bytes) and backward
+ * (*bwd_bytes) entry points for this shape and reduction. Host only; either
+ * out-pointer may be NULL. The forward size is about 16 * N * ceil(V/256) +
+ * 2 * N * H bytes (one partial softmax state per token and 256-wide
+ * vocabulary tile, and a re-laid-out copy of hidden). The backward size holds
+ * a bounded slice of the logit gradient in two bf16 layouts
+ * (4 * 256*ceil(N/256) * Vc <= 1 GiB unless Vc is at its floor of 2048
+ * columns; independent of V), re-laid-out copies of hidden and of a weight
+ * slice, and, when the slice does not cover the whole vocabulary, an fp32
+ * accumulator of N*H*4 bytes. */
 flce_status_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int reduction,
                                   size_t* fwd_bytes, size_t* bwd_bytes);
 
@@ -97,7 +117,8 @@ flce_status_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int reduction
  *   lse, logprob, entropy   device fp32 [N] outputs (always written).
  *                           Keep lse and entropy for flce_backward.
  *   logprob_mean, entropy_mean  device fp32 [1] outputs; required when
- *                           reduction == FLCE_REDUCTION_MEAN, ignored otherwise.
+ *                           reduction is MEAN (the means) or SUM (the sums),
+ *                           ignored under NONE.
  *   workspace  device scratch of at least the forward size from
  *              flce_workspace_size; its first 256 bytes hold the status word.
  */
@@ -117,6 +138,8 @@ flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t
  *                   (gbar_i = grad_logprob[i]).
  *   reduction MEAN: they are device fp32 [1], the gradients of the two means
  *                   (gbar_i = grad_logprob[0] / n on non-ignored tokens).
+ *   reduction SUM:  device fp32 [1], the gradients of the two sums
+ *                   (gbar_i = grad_logprob[0] on non-ignored tokens).
  * Either gradient pointer may be NULL, meaning zero. Ignored tokens get zero
  * rows in grad_hidden. The logit gradient is recomputed, not stored by the
  * forward.
@@ -128,6 +151,44 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
                             const float* grad_logprob, const float* grad_entropy,
                             void* grad_hidden, void* grad_weight,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Options of the extended entry points. */
+typedef struct flce_options {
+  int64_t ignore_index;  /* label value that marks a skipped token */
+  float softcap;         /* c > 0: z' = c*tanh(z/c); c <= 0: no cap; must be finite */
+  int reduction;         /* FLCE_REDUCTION_NONE, _MEAN or _SUM */
+  float z_loss_scale;    /* lam >= 0 (finite) of z_loss = lam * lse^2 */
+  int grad_dtype;        /* FLCE_GRAD_BF16 or FLCE_GRAD_F32: type of grad_hidden/grad_weight */
+} flce_options_t;
+
+/* Extended forward. As flce_forward, plus
+ *   uniform_ce, z_loss  device fp32 [N] outputs, each optional (NULL = not
+ *                       written);
+ *   reduced             device fp32 [4]: the reductions (MEAN: means over the
+ *                       n non-ignored tokens; SUM: sums) of logprob, entropy,
+ *                       uniform_ce and z_loss, in that order; required unless
+ *                       reduction is NONE, ignored then.
+ * The workspace size is the forward size of flce_workspace_size. */
+flce_status_t flce_forward_ex(const void* hidden, const void* weight, const int64_t* labels,
+                              int64_t N, int64_t H, int64_t V, const flce_options_t* opt,
+                              float* lse, float* logprob, float* entropy,
+                              float* uniform_ce, float* z_loss, float* reduced,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Extended backward: grad_hidden [N,H] and grad_weight [H,V] (device; bf16
+ * or fp32 as opt->grad_dtype says) of
+ *   L = sum_i gbar_i logprob_i + ebar_i entropy_i + gu_i uniform_ce_i + gz_i z_loss_i,
+ * with the four upstream gradients given as for flce_backward (device fp32,
+ * [N] under NONE, [1] under MEAN and SUM; NULL means zero). opt and the
+ * tensors must be those of the matching flce_forward_ex. The workspace size is
+ * the backward size of flce_workspace_size. */
+flce_status_t flce_backward_ex(const void* hidden, const void* weight, const int64_t* labels,
+                               int64_t N, int64_t H, int64_t V, const flce_options_t* opt,
+                               const float* lse, const float* entropy,
+                               const float* grad_logprob, const float* grad_entropy,
+                               const float* grad_uniform_ce, const float* grad_z_loss,
+                               void* grad_hidden, void* grad_weight,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Reads the status word that the last flce_forward / flce_backward on this
  * workspace left, after synchronising `stream`. *invalid_labels (may be NULL)

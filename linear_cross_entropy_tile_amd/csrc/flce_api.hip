@@ -107,7 +107,7 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   p.f_zlab = off;
   off = align_up(off + 4 * (size_t)N);
   p.f_bsum = off;
-  off = align_up(off + (reduction == FLCE_REDUCTION_MEAN ? 16 * (size_t)ceil_div(N, kCombineTokens) : 0));
+  off = align_up(off + (reduction != FLCE_REDUCTION_NONE ? 32 * (size_t)ceil_div(N, kCombineTokens) : 0));
   p.f_xb = off;
   off = align_up(off + blk * (size_t)p.TB * (size_t)p.hkb);
   p.f_total = off;
@@ -116,7 +116,7 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   p.b_lab = off;
   off = align_up(off + 4 * (size_t)N);
   p.b_coef = off;
-  off = align_up(off + 16 * (size_t)N);
+  off = align_up(off + sizeof(DzToken) * (size_t)N);
   p.b_wb = off;
   off = align_up(off + blk * (size_t)p.HT * (size_t)p.kbv);
   p.b_xb = off;
@@ -144,12 +144,20 @@ flce_status_t check_shape(int64_t N, int64_t H, int64_t V) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+bool valid_reduction(int r) {
+  return r == FLCE_REDUCTION_NONE || r == FLCE_REDUCTION_MEAN || r == FLCE_REDUCTION_SUM;
+}
+
+// fp32 gradient outputs: a dW tile's byte offsets (up to ~1024 * V) must stay
+// below 2^31.
+constexpr int64_t kMaxVF32 = (int64_t)1 << 21;
+
 // ---- kernel timing hooks --------------------------------------------------------
 enum Kind {
-  K_FWD_PREP, K_FWD_TILE, K_FWD_COMBINE, K_FWD_MEAN, K_BWD_PREP, K_BWD_DLOGITS, K_BWD_DX,
+  K_FWD_PREP, K_FWD_TILE, K_FWD_COMBINE, K_FWD_REDUCE, K_BWD_PREP, K_BWD_DLOGITS, K_BWD_DX,
   K_BWD_DW, K_DW_REDUCE, K_FILL, K_PACK_WEIGHT, K_PACK_HIDDEN, K_NUM
 };
-const char* kKindNames[K_NUM] = {"fwd_prep", "fwd_tile", "fwd_combine", "fwd_mean", "bwd_prep",
+const char* kKindNames[K_NUM] = {"fwd_prep", "fwd_tile", "fwd_combine", "fwd_reduce", "bwd_prep",
                                  "bwd_dlogits", "bwd_dx", "bwd_dw", "dw_reduce", "fill_zero",
                                  "pack_weight", "pack_hidden"};
 
@@ -256,26 +264,36 @@ extern "C" {
 flce_status_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int reduction,
                                   size_t* fwd_bytes, size_t* bwd_bytes) {
   FLCE_TRY(check_shape(N, H, V));
-  if (reduction != FLCE_REDUCTION_NONE && reduction != FLCE_REDUCTION_MEAN)
-    return FLCE_ERR_BAD_REDUCTION;
+  if (!valid_reduction(reduction)) return FLCE_ERR_BAD_REDUCTION;
   const Plan p = make_plan(N, H, V, reduction);
   if (fwd_bytes) *fwd_bytes = p.f_total;
   if (bwd_bytes) *bwd_bytes = p.b_total;
   return FLCE_OK;
 }
 
-flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t* labels,
-                           int64_t N, int64_t H, int64_t V, int64_t ignore_index,
-                           float softcap, int reduction, float* lse, float* logprob,
-                           float* entropy, float* logprob_mean, float* entropy_mean,
-                           void* workspace, size_t workspace_bytes, void* stream) {
-  FLCE_TRY(check_shape(N, H, V));
-  if (reduction != FLCE_REDUCTION_NONE && reduction != FLCE_REDUCTION_MEAN)
-    return FLCE_ERR_BAD_REDUCTION;
-  if (!std::isfinite(softcap)) return FLCE_ERR_BAD_SOFTCAP;
-  const bool mean = reduction == FLCE_REDUCTION_MEAN;
+}  // extern "C"
+
+namespace {
+
+flce_status_t check_options(const flce_options_t* o) {
+  if (o == nullptr) return FLCE_ERR_NULL_POINTER;
+  if (!valid_reduction(o->reduction)) return FLCE_ERR_BAD_REDUCTION;
+  if (!std::isfinite(o->softcap)) return FLCE_ERR_BAD_SOFTCAP;
+  if (!std::isfinite(o->z_loss_scale) || o->z_loss_scale < 0.f) return FLCE_ERR_BAD_OPTION;
+  if (o->grad_dtype != FLCE_GRAD_BF16 && o->grad_dtype != FLCE_GRAD_F32) return FLCE_ERR_BAD_OPTION;
+  return FLCE_OK;
+}
+
+// reduced[k] receives the reduction of output k (logprob, entropy,
+// uniform_ce, z_loss); each may be null.
+flce_status_t forward_impl(const void* hidden, const void* weight, const int64_t* labels,
+                           int64_t N, int64_t H, int64_t V, const flce_options_t& o, float* lse,
+                           float* logprob, float* entropy, float* uniform_ce, float* z_loss,
+                           float* const (&reduced)[4], void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  const int reduction = o.reduction;
+  const bool reduce = reduction != FLCE_REDUCTION_NONE;
   if (workspace == nullptr) return FLCE_ERR_NULL_POINTER;
-  if (mean && (logprob_mean == nullptr || entropy_mean == nullptr)) return FLCE_ERR_NULL_POINTER;
   if (N > 0 && (hidden == nullptr || weight == nullptr || labels == nullptr || lse == nullptr ||
                 logprob == nullptr || entropy == nullptr))
     return FLCE_ERR_NULL_POINTER;
@@ -283,16 +301,18 @@ flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t
   const Plan p = make_plan(N, H, V, reduction);
   if (workspace_bytes < p.f_total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const float softcap = o.softcap;
 
   int32_t* header = reinterpret_cast<int32_t*>(workspace);
   int32_t* lab32 = reinterpret_cast<int32_t*>(wsp(workspace, p.f_lab));
   float4* part = reinterpret_cast<float4*>(wsp(workspace, p.f_part));
   float* zlab = reinterpret_cast<float*>(wsp(workspace, p.f_zlab));
-  double2* bsum = mean ? reinterpret_cast<double2*>(wsp(workspace, p.f_bsum)) : nullptr;
+  double4* bsum = reduce ? reinterpret_cast<double4*>(wsp(workspace, p.f_bsum)) : nullptr;
 
   FLCE_TRY(launch(K_FWD_PREP, st, [&] {
-    fwd_prep_kernel<<<1, 1024, 0, st>>>(labels, N, V, ignore_index, lab32, header);
+    fwd_prep_kernel<<<1, 1024, 0, st>>>(labels, N, V, o.ignore_index, lab32, header);
   }));
+  const int nb = (int)ceil_div(N, kCombineTokens);
   if (N > 0) {
     uint16_t* xb = reinterpret_cast<uint16_t*>(wsp(workspace, p.f_xb));
     FLCE_TRY(pack_rows(K_PACK_HIDDEN, hidden, N, H, H, p.hkb, xb, st));
@@ -318,32 +338,43 @@ flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t
       else
         fwd_tile_kernel<false><<<grid, kThreads, 0, st>>>(a);
     }));
-    const int nb = (int)ceil_div(N, kCombineTokens);
+    CombineArgs c{};
+    c.part = part;
+    c.S = p.VT;
+    c.zlab = zlab;
+    c.lab32 = lab32;
+    c.N = N;
+    c.V = V;
+    c.zl_scale = o.z_loss_scale;
+    c.lse = lse;
+    c.logprob = logprob;
+    c.entropy = entropy;
+    c.uniform_ce = uniform_ce;
+    c.z_loss = z_loss;
+    c.bsum = bsum;
     FLCE_TRY(launch(K_FWD_COMBINE, st, [&] {
-      fwd_combine_kernel<<<nb, 64 * kCombineWaves, 0, st>>>(part, p.VT, zlab, lab32, N, lse,
-                                                            logprob, entropy, bsum);
+      fwd_combine_kernel<<<nb, 64 * kCombineWaves, 0, st>>>(c);
     }));
   }
-  if (mean) {
-    const int nb = (int)ceil_div(N, kCombineTokens);
-    FLCE_TRY(launch(K_FWD_MEAN, st, [&] {
-      fwd_mean_kernel<<<1, 256, 0, st>>>(bsum, nb, header, logprob_mean, entropy_mean);
+  if (reduce) {
+    const int mean = reduction == FLCE_REDUCTION_MEAN;
+    FLCE_TRY(launch(K_FWD_REDUCE, st, [&] {
+      fwd_reduce_kernel<<<1, 256, 0, st>>>(bsum, N > 0 ? nb : 0, header, mean, reduced[0],
+                                           reduced[1], reduced[2], reduced[3]);
     }));
   }
   return FLCE_OK;
 }
 
-flce_status_t flce_backward(const void* hidden, const void* weight, const int64_t* labels,
-                            int64_t N, int64_t H, int64_t V, int64_t ignore_index,
-                            float softcap, int reduction, const float* lse,
-                            const float* entropy, const float* grad_logprob,
-                            const float* grad_entropy, void* grad_hidden, void* grad_weight,
+flce_status_t backward_impl(const void* hidden, const void* weight, const int64_t* labels,
+                            int64_t N, int64_t H, int64_t V, const flce_options_t& o,
+                            const float* lse, const float* entropy, const float* grad_logprob,
+                            const float* grad_entropy, const float* grad_uniform_ce,
+                            const float* grad_z_loss, void* grad_hidden, void* grad_weight,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  FLCE_TRY(check_shape(N, H, V));
-  if (reduction != FLCE_REDUCTION_NONE && reduction != FLCE_REDUCTION_MEAN)
-    return FLCE_ERR_BAD_REDUCTION;
-  if (!std::isfinite(softcap)) return FLCE_ERR_BAD_SOFTCAP;
-  const bool mean = reduction == FLCE_REDUCTION_MEAN;
+  const int reduction = o.reduction;
+  const bool f32 = o.grad_dtype == FLCE_GRAD_F32;
+  if (f32 && V > kMaxVF32) return FLCE_ERR_BAD_SHAPE;
   if (workspace == nullptr || weight == nullptr || grad_weight == nullptr)
     return FLCE_ERR_NULL_POINTER;
   if (N > 0 && (hidden == nullptr || labels == nullptr || lse == nullptr || entropy == nullptr ||
@@ -355,12 +386,13 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
   const Plan p = make_plan(N, H, V, reduction);
   if (workspace_bytes < p.b_total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t out_elem = f32 ? 4 : 2;
 
-  if (N == 0) return zero_fill(grad_weight, 2 * (size_t)H * (size_t)V, st);
+  if (N == 0) return zero_fill(grad_weight, out_elem * (size_t)H * (size_t)V, st);
 
   int32_t* header = reinterpret_cast<int32_t*>(workspace);
   int32_t* lab32 = reinterpret_cast<int32_t*>(wsp(workspace, p.b_lab));
-  float4* coef = reinterpret_cast<float4*>(wsp(workspace, p.b_coef));
+  DzToken* coef = reinterpret_cast<DzToken*>(wsp(workspace, p.b_coef));
   uint16_t* wb = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_wb));
   uint16_t* xb = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_xb));
   uint16_t* xtb = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_xtb));
@@ -369,16 +401,30 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
   float* acc = reinterpret_cast<float*>(wsp(workspace, p.b_acc));
   float* part = reinterpret_cast<float*>(wsp(workspace, p.b_part));
 
-  FLCE_TRY(launch(K_BWD_PREP, st, [&] {
-    bwd_prep_kernel<<<1, 1024, 0, st>>>(labels, N, V, ignore_index, mean ? 1 : 0, lse, entropy,
-                                        grad_logprob, grad_entropy, coef, lab32, header);
-  }));
+  PrepArgs pa{};
+  pa.labels = labels;
+  pa.N = N;
+  pa.V = V;
+  pa.ignore_index = o.ignore_index;
+  pa.reduction = reduction;
+  pa.zl_scale = o.z_loss_scale;
+  pa.lse = lse;
+  pa.entropy = entropy;
+  pa.glp = grad_logprob;
+  pa.gent = grad_entropy;
+  pa.guce = grad_uniform_ce;
+  pa.gzl = grad_z_loss;
+  pa.coef = coef;
+  pa.lab32 = lab32;
+  pa.header = header;
+  FLCE_TRY(launch(K_BWD_PREP, st, [&] { bwd_prep_kernel<<<1, 1024, 0, st>>>(pa); }));
 
   // Blocked operands: hidden (tokens x H) for the recompute, hidden^T
   // (H x tokens) for dW, and per chunk the weight (H x vocabulary) for dH.
   // The recompute reads the weight (vocabulary x H) row-contiguous.
   FLCE_TRY(pack_rows(K_PACK_HIDDEN, hidden, N, H, H, p.hkb, xb, st));
   FLCE_TRY(pack_cols(K_PACK_HIDDEN, hidden, H, N, H, p.nkb, xtb, st));
+  const float softcap = o.softcap;
   const bool capped = softcap > 0.f;
   for (int c = 0; c < p.nchunks; ++c) {
     const int64_t v0 = (int64_t)c * p.Vc;
@@ -426,16 +472,25 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
     x.HT = p.HT;
     x.group = p.group;
     x.acc = acc;
-    x.gh = static_cast<uint16_t*>(grad_hidden);
+    x.gh = grad_hidden;
     const int mode =
         p.nchunks == 1 ? DX_ONLY : (c == 0 ? DX_FIRST : (c == p.nchunks - 1 ? DX_LAST : DX_MID));
     const int gx = p.TB * p.HT;
     FLCE_TRY(launch(K_BWD_DX, st, [&] {
-      switch (mode) {
-        case DX_ONLY: bwd_dx_kernel<DX_ONLY><<<gx, kThreads, 0, st>>>(x); break;
-        case DX_FIRST: bwd_dx_kernel<DX_FIRST><<<gx, kThreads, 0, st>>>(x); break;
-        case DX_MID: bwd_dx_kernel<DX_MID><<<gx, kThreads, 0, st>>>(x); break;
-        default: bwd_dx_kernel<DX_LAST><<<gx, kThreads, 0, st>>>(x); break;
+      if (f32) {
+        switch (mode) {
+          case DX_ONLY: bwd_dx_kernel<DX_ONLY, true><<<gx, kThreads, 0, st>>>(x); break;
+          case DX_FIRST: bwd_dx_kernel<DX_FIRST, true><<<gx, kThreads, 0, st>>>(x); break;
+          case DX_MID: bwd_dx_kernel<DX_MID, true><<<gx, kThreads, 0, st>>>(x); break;
+          default: bwd_dx_kernel<DX_LAST, true><<<gx, kThreads, 0, st>>>(x); break;
+        }
+      } else {
+        switch (mode) {
+          case DX_ONLY: bwd_dx_kernel<DX_ONLY, false><<<gx, kThreads, 0, st>>>(x); break;
+          case DX_FIRST: bwd_dx_kernel<DX_FIRST, false><<<gx, kThreads, 0, st>>>(x); break;
+          case DX_MID: bwd_dx_kernel<DX_MID, false><<<gx, kThreads, 0, st>>>(x); break;
+          default: bwd_dx_kernel<DX_LAST, false><<<gx, kThreads, 0, st>>>(x); break;
+        }
       }
     }));
 
@@ -454,25 +509,92 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
     w.splits = p.dw_splits;
     w.group = p.group;
     w.kper = p.dw_kper;
-    w.gw = static_cast<uint16_t*>(grad_weight);
+    w.gw = grad_weight;
     w.part = part;
     const int gw = p.HT * vtc * p.dw_splits;
     FLCE_TRY(launch(K_BWD_DW, st, [&] {
       if (p.dw_splits > 1)
-        bwd_dw_kernel<true><<<gw, kThreads, 0, st>>>(w);
+        bwd_dw_kernel<true, false><<<gw, kThreads, 0, st>>>(w);
+      else if (f32)
+        bwd_dw_kernel<false, true><<<gw, kThreads, 0, st>>>(w);
       else
-        bwd_dw_kernel<false><<<gw, kThreads, 0, st>>>(w);
+        bwd_dw_kernel<false, false><<<gw, kThreads, 0, st>>>(w);
     }));
     if (p.dw_splits > 1) {
       const int64_t n = H * vc;
       const int blocks = (int)(ceil_div(n, 256) < 8192 ? ceil_div(n, 256) : 8192);
       FLCE_TRY(launch(K_DW_REDUCE, st, [&] {
-        dw_reduce_kernel<<<blocks, 256, 0, st>>>(part, p.dw_splits, H, vc, p.Vc, V, v0,
-                                                 static_cast<uint16_t*>(grad_weight));
+        if (f32)
+          dw_reduce_kernel<true><<<blocks, 256, 0, st>>>(part, p.dw_splits, H, vc, p.Vc, V, v0,
+                                                         grad_weight);
+        else
+          dw_reduce_kernel<false><<<blocks, 256, 0, st>>>(part, p.dw_splits, H, vc, p.Vc, V, v0,
+                                                          grad_weight);
       }));
     }
   }
   return FLCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t* labels,
+                           int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                           float softcap, int reduction, float* lse, float* logprob,
+                           float* entropy, float* logprob_mean, float* entropy_mean,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  FLCE_TRY(check_shape(N, H, V));
+  const flce_options_t o{ignore_index, softcap, reduction, 0.f, FLCE_GRAD_BF16};
+  FLCE_TRY(check_options(&o));
+  if (reduction != FLCE_REDUCTION_NONE && (logprob_mean == nullptr || entropy_mean == nullptr))
+    return FLCE_ERR_NULL_POINTER;
+  float* const red[4] = {logprob_mean, entropy_mean, nullptr, nullptr};
+  return forward_impl(hidden, weight, labels, N, H, V, o, lse, logprob, entropy, nullptr, nullptr,
+                      red, workspace, workspace_bytes, stream);
+}
+
+flce_status_t flce_forward_ex(const void* hidden, const void* weight, const int64_t* labels,
+                              int64_t N, int64_t H, int64_t V, const flce_options_t* opt,
+                              float* lse, float* logprob, float* entropy, float* uniform_ce,
+                              float* z_loss, float* reduced, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  FLCE_TRY(check_shape(N, H, V));
+  FLCE_TRY(check_options(opt));
+  if (opt->reduction != FLCE_REDUCTION_NONE && reduced == nullptr) return FLCE_ERR_NULL_POINTER;
+  float* const red[4] = {reduced, reduced ? reduced + 1 : nullptr, reduced ? reduced + 2 : nullptr,
+                         reduced ? reduced + 3 : nullptr};
+  return forward_impl(hidden, weight, labels, N, H, V, *opt, lse, logprob, entropy, uniform_ce,
+                      z_loss, red, workspace, workspace_bytes, stream);
+}
+
+flce_status_t flce_backward(const void* hidden, const void* weight, const int64_t* labels,
+                            int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                            float softcap, int reduction, const float* lse,
+                            const float* entropy, const float* grad_logprob,
+                            const float* grad_entropy, void* grad_hidden, void* grad_weight,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  FLCE_TRY(check_shape(N, H, V));
+  const flce_options_t o{ignore_index, softcap, reduction, 0.f, FLCE_GRAD_BF16};
+  FLCE_TRY(check_options(&o));
+  return backward_impl(hidden, weight, labels, N, H, V, o, lse, entropy, grad_logprob,
+                       grad_entropy, nullptr, nullptr, grad_hidden, grad_weight, workspace,
+                       workspace_bytes, stream);
+}
+
+flce_status_t flce_backward_ex(const void* hidden, const void* weight, const int64_t* labels,
+                               int64_t N, int64_t H, int64_t V, const flce_options_t* opt,
+                               const float* lse, const float* entropy,
+                               const float* grad_logprob, const float* grad_entropy,
+                               const float* grad_uniform_ce, const float* grad_z_loss,
+                               void* grad_hidden, void* grad_weight, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  FLCE_TRY(check_shape(N, H, V));
+  FLCE_TRY(check_options(opt));
+  return backward_impl(hidden, weight, labels, N, H, V, *opt, lse, entropy, grad_logprob,
+                       grad_entropy, grad_uniform_ce, grad_z_loss, grad_hidden, grad_weight,
+                       workspace, workspace_bytes, stream);
 }
 
 flce_status_t flce_get_status(const void* workspace, int64_t* invalid_labels, void* stream) {
@@ -491,17 +613,18 @@ const char* flce_status_string(flce_status_t s) {
     case FLCE_OK: return "ok";
     case FLCE_ERR_NULL_POINTER: return "a required pointer is NULL";
     case FLCE_ERR_BAD_SHAPE: return "bad shape (need N >= 0, H >= 1, V >= 1 within limits)";
-    case FLCE_ERR_BAD_REDUCTION: return "reduction must be NONE (0) or MEAN (1)";
+    case FLCE_ERR_BAD_REDUCTION: return "reduction must be NONE (0), MEAN (1) or SUM (2)";
     case FLCE_ERR_MISALIGNED: return "pointers must be 16-byte aligned and H, V multiples of 8";
     case FLCE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than flce_workspace_size";
     case FLCE_ERR_BAD_SOFTCAP: return "softcap must be finite";
     case FLCE_ERR_HIP: return "HIP runtime error or failed kernel launch";
     case FLCE_ERR_INVALID_LABEL: return "labels outside [0, V) that are not ignore_index";
+    case FLCE_ERR_BAD_OPTION: return "z_loss_scale must be finite and >= 0; grad_dtype BF16 or F32";
   }
   return "unknown status";
 }
 
-int flce_version(void) { return 100; }
+int flce_version(void) { return 200; }
 
 flce_status_t flce_profile_enable(int enable) {
   Profiler& P = prof();

@@ -1,6 +1,6 @@
 // Kernels of the fused linear cross-entropy + entropy head (gfx950).
 //
-// Forward:  fwd_prep, pack (hidden) -> fwd_tile -> fwd_combine (-> fwd_mean)
+// Forward:  fwd_prep, pack (hidden) -> fwd_tile -> fwd_combine (-> fwd_reduce)
 // Backward: bwd_prep, pack (hidden, hidden^T) -> per vocabulary chunk
 //           { pack (weight chunk) -> bwd_dlogits -> bwd_dx -> bwd_dw
 //             (-> dw_reduce) }
@@ -153,7 +153,7 @@ struct FwdTileArgs {
   int VT, TB;              // vocabulary tiles, token blocks
   int group;               // token blocks per XCD patch (see group_map)
   float cap, cap_k;        // softcap c and 2*log2(e)/c
-  float4* part;            // [VT][N] {m, s, u, 0} per vocabulary tile
+  float4* part;            // [VT][N] {m, s, u, sum z'} per vocabulary tile
   float* zlab;             // [N] capped logit of the label
 };
 
@@ -170,12 +170,13 @@ __device__ __forceinline__ void merge_state2(float& m, float& s, float& u, float
 
 // Online-softmax state of one token column j of a wave's 128 x 32 block
 // (64 accumulators per lane): m = max z', s = sum exp(z' - m),
-// u = sum exp(z' - m)(z' - m) in base-2 units. The capped logits are left in
-// z[] for the label capture. MASK drops rows at offset >= lim (the last
-// vocabulary tile only).
+// u = sum exp(z' - m)(z' - m) in base-2 units, and zs = sum z' (for the
+// uniform cross-entropy). The capped logits are left in z[] for the label
+// capture. MASK drops rows at offset >= lim (the last vocabulary tile only).
 template <bool CAP, bool MASK>
 __device__ __forceinline__ void column_stats(const Acc& acc, int j, float cap, float cap_k, int lim,
-                                             float (&z)[64], float& m, float& s, float& u) {
+                                             float (&z)[64], float& m, float& s, float& u,
+                                             float& zs) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -185,15 +186,24 @@ __device__ __forceinline__ void column_stats(const Acc& acc, int j, float cap, f
       if constexpr (MASK) x = (i * 32 + 8 * (r >> 2) + (r & 3)) < lim ? x : kNegBig;
       z[i * 16 + r] = x;
     }
-  float mx[4];
+  float mx[4], sz[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float x = z[i * 16];
+    float t = MASK ? (z[i * 16] == kNegBig ? 0.f : z[i * 16]) : z[i * 16];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) x = fmaxf(x, z[i * 16 + r]);
+    for (int r = 1; r < 16; ++r) {
+      x = fmaxf(x, z[i * 16 + r]);
+      if constexpr (MASK)
+        t += z[i * 16 + r] == kNegBig ? 0.f : z[i * 16 + r];
+      else
+        t += z[i * 16 + r];
+    }
     mx[i] = x;
+    sz[i] = t;
   }
   const float mb = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+  zs = (sz[0] + sz[1]) + (sz[2] + sz[3]);
   const float nm = -mb * kLog2e;
   float sp[4], up[4];
 #pragma unroll
@@ -247,14 +257,14 @@ fwd_tile_kernel(FwdTileArgs a) {
   const bool full = (int64_t)vb + 128 <= a.V;
   // Rows at offset o (0..127, without the lane-half term) are valid iff o < lim.
   const int lim = (int)(a.V - vb) - 4 * lh;
-  float m[2], s[2], u[2];
+  float m[2], s[2], u[2], zs[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     float z[64];
     if (full)
-      column_stats<CAP, false>(acc, j, a.cap, a.cap_k, lim, z, m[j], s[j], u[j]);
+      column_stats<CAP, false>(acc, j, a.cap, a.cap_k, lim, z, m[j], s[j], u[j], zs[j]);
     else
-      column_stats<CAP, true>(acc, j, a.cap, a.cap_k, lim, z, m[j], s[j], u[j]);
+      column_stats<CAP, true>(acc, j, a.cap, a.cap_k, lim, z, m[j], s[j], u[j], zs[j]);
 
     // The label's logit: exactly one lane of one block in the grid owns it,
     // and most waves own none (skipped by a wave-uniform test).
@@ -278,25 +288,22 @@ fwd_tile_kernel(FwdTileArgs a) {
   for (int j = 0; j < 2; ++j) {
     const float m2 = __shfl_xor(m[j], 32), s2 = __shfl_xor(s[j], 32), u2 = __shfl_xor(u[j], 32);
     merge_state2(m[j], s[j], u[j], m2, s2, u2);
+    zs[j] += __shfl_xor(zs[j], 32);
   }
-  float* red = reinterpret_cast<float*>(sa[0]);
+  float4* red = reinterpret_cast<float4*>(sa[0]);
   if (wm == 1 && lane < 32) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = acc_col(wn, j, lane);
-      red[c * 3 + 0] = m[j];
-      red[c * 3 + 1] = s[j];
-      red[c * 3 + 2] = u[j];
-    }
+    for (int j = 0; j < 2; ++j) red[acc_col(wn, j, lane)] = make_float4(m[j], s[j], u[j], zs[j]);
   }
   __syncthreads();
   if (wm == 0 && lane < 32) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int c = acc_col(wn, j, lane);
-      merge_state2(m[j], s[j], u[j], red[c * 3 + 0], red[c * 3 + 1], red[c * 3 + 2]);
+      const float4 q = red[c];
+      merge_state2(m[j], s[j], u[j], q.x, q.y, q.z);
       const int64_t t = n0 + c;
-      if (t < a.N) a.part[(int64_t)vt * a.N + t] = make_float4(m[j], s[j], u[j] * kLn2, 0.f);
+      if (t < a.N) a.part[(int64_t)vt * a.N + t] = make_float4(m[j], s[j], u[j] * kLn2, zs[j] + q.w);
     }
   }
 }
@@ -320,119 +327,178 @@ constexpr int kCombineWaves = 16;    // vocabulary-tile groups per combine block
 // Block of 1024 threads for 64 tokens: wave w merges the partial states of
 // vocabulary tiles w, w + 16, ... of token t0 + lane (consecutive lanes read
 // consecutive 16-byte states), then wave 0 merges the 16 states in wave order
-// and writes lse, logprob, entropy. With bsum != nullptr it also writes the
-// block's float64 sums of logprob and entropy over valid tokens. Fixed merge
-// and summation orders: the result does not depend on timing.
-__global__ void __launch_bounds__(1024) fwd_combine_kernel(const float4* __restrict__ part, int S,
-                                                           const float* __restrict__ zlab,
-                                                           const int32_t* __restrict__ lab32,
-                                                           int64_t N, float* __restrict__ lse,
-                                                           float* __restrict__ logprob,
-                                                           float* __restrict__ entropy,
-                                                           double2* __restrict__ bsum) {
+// and writes lse, logprob, entropy and, when requested, the uniform
+// cross-entropy lse - (1/V) sum z' and the z-loss lam * lse^2. With
+// bsum != nullptr it also writes the block's float64 sums of the four outputs
+// over valid tokens. Fixed merge and summation orders: the result does not
+// depend on timing.
+struct CombineArgs {
+  const float4* part;
+  int S;                   // vocabulary tiles
+  const float* zlab;
+  const int32_t* lab32;
+  int64_t N, V;
+  float zl_scale;          // lam
+  float *lse, *logprob, *entropy;
+  float *uniform_ce, *z_loss;  // optional
+  double4* bsum;               // optional: {logprob, entropy, uniform_ce, z_loss} per block
+};
+
+__global__ void __launch_bounds__(1024) fwd_combine_kernel(CombineArgs a) {
   __shared__ float4 st[kCombineWaves][kCombineTokens];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * kCombineTokens + lane;
-  const bool valid = t < N && lab32[t] >= 0;
-  float m = kNegBig, s = 0.f, u = 0.f;
+  const bool valid = t < a.N && a.lab32[t] >= 0;
+  float m = kNegBig, s = 0.f, u = 0.f, zs = 0.f;
   if (valid)
-    for (int k = w; k < S; k += kCombineWaves) {
-      const float4 q = part[(int64_t)k * N + t];
+    for (int k = w; k < a.S; k += kCombineWaves) {
+      const float4 q = a.part[(int64_t)k * a.N + t];
       merge_state(m, s, u, q.x, q.y, q.z);
+      zs += q.w;
     }
-  st[w][lane] = make_float4(m, s, u, 0.f);
+  st[w][lane] = make_float4(m, s, u, zs);
   __syncthreads();
   if (w != 0) return;
 #pragma unroll 1
   for (int k = 1; k < kCombineWaves; ++k) {
     const float4 q = st[k][lane];
     merge_state(m, s, u, q.x, q.y, q.z);
+    zs += q.w;
   }
-  double slp = 0.0, sent = 0.0;
+  double r0 = 0.0, r1 = 0.0, r2 = 0.0, r3 = 0.0;
   if (valid) {
     const float ls = logf(s);
     const float l = m + ls;
     const float e = ls - u / s;
-    const float lp = zlab[t] - l;
-    lse[t] = l;
-    entropy[t] = e;
-    logprob[t] = lp;
-    slp = lp;
-    sent = e;
-  } else if (t < N) {
-    lse[t] = 0.f;
-    entropy[t] = 0.f;
-    logprob[t] = 0.f;
+    const float lp = a.zlab[t] - l;
+    const float uc = l - zs / (float)a.V;
+    const float zl = a.zl_scale * l * l;
+    a.lse[t] = l;
+    a.entropy[t] = e;
+    a.logprob[t] = lp;
+    if (a.uniform_ce) a.uniform_ce[t] = uc;
+    if (a.z_loss) a.z_loss[t] = zl;
+    r0 = lp;
+    r1 = e;
+    r2 = uc;
+    r3 = zl;
+  } else if (t < a.N) {
+    a.lse[t] = 0.f;
+    a.entropy[t] = 0.f;
+    a.logprob[t] = 0.f;
+    if (a.uniform_ce) a.uniform_ce[t] = 0.f;
+    if (a.z_loss) a.z_loss[t] = 0.f;
   }
-  if (bsum != nullptr) {
+  if (a.bsum != nullptr) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-      slp += __shfl_xor(slp, o);
-      sent += __shfl_xor(sent, o);
+      r0 += __shfl_xor(r0, o);
+      r1 += __shfl_xor(r1, o);
+      r2 += __shfl_xor(r2, o);
+      r3 += __shfl_xor(r3, o);
     }
-    if (lane == 0) bsum[blockIdx.x] = make_double2(slp, sent);
+    if (lane == 0) a.bsum[blockIdx.x] = make_double4(r0, r1, r2, r3);
   }
 }
 
-// One block: sums the per-block partial sums in a fixed order and divides by
-// the number of valid tokens (0 when there are none).
-__global__ void __launch_bounds__(256) fwd_mean_kernel(const double2* __restrict__ bsum, int nb,
-                                                       const int32_t* __restrict__ header,
-                                                       float* __restrict__ lp_mean,
-                                                       float* __restrict__ ent_mean) {
+// One block: sums the per-block partial sums in a fixed order; under "mean"
+// divides by the number of valid tokens (0 when there are none). Writes each
+// of the four reduced outputs whose pointer is not null.
+__global__ void __launch_bounds__(256) fwd_reduce_kernel(const double4* __restrict__ bsum, int nb,
+                                                         const int32_t* __restrict__ header,
+                                                         int mean, float* out_lp, float* out_ent,
+                                                         float* out_uce, float* out_zl) {
   __shared__ double sh[256];
-  double a = 0.0, b = 0.0;
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
   for (int i = threadIdx.x; i < nb; i += 256) {
-    a += bsum[i].x;
-    b += bsum[i].y;
+    const double4 b = bsum[i];
+    a0 += b.x;
+    a1 += b.y;
+    a2 += b.z;
+    a3 += b.w;
   }
-  a = block_sum<double, 256>(a, sh);
-  b = block_sum<double, 256>(b, sh);
+  a0 = block_sum<double, 256>(a0, sh);
+  a1 = block_sum<double, 256>(a1, sh);
+  a2 = block_sum<double, 256>(a2, sh);
+  a3 = block_sum<double, 256>(a3, sh);
   if (threadIdx.x == 0) {
     const int n = header[1];
-    lp_mean[0] = n > 0 ? (float)(a / n) : 0.f;
-    ent_mean[0] = n > 0 ? (float)(b / n) : 0.f;
+    const double d = mean ? (n > 0 ? (double)n : 0.0) : 1.0;
+    const double f = d > 0.0 ? 1.0 / d : 0.0;
+    if (out_lp) out_lp[0] = (float)(a0 * f);
+    if (out_ent) out_ent[0] = (float)(a1 * f);
+    if (out_uce) out_uce[0] = (float)(a2 * f);
+    if (out_zl) out_zl[0] = (float)(a3 * f);
   }
 }
 
 // ---- backward: per-token coefficients ------------------------------------------
 
-// One block of 1024. coef[t] = {lse, S = lse - entropy, gbar, ebar} for valid
-// tokens; for others lse = 1e30 (so every p underflows to 0) and zeros.
-__global__ void __launch_bounds__(1024) bwd_prep_kernel(
-    const int64_t* __restrict__ labels, int64_t N, int64_t V, int64_t ignore_index, int mean,
-    const float* __restrict__ lse, const float* __restrict__ entropy,
-    const float* __restrict__ glp, const float* __restrict__ gent, float4* __restrict__ coef,
-    int32_t* __restrict__ lab32, int32_t* __restrict__ header) {
+// Per-token constants of the logit gradient (see bwd_dlogits_kernel):
+//   dz'_v = gbar [v == y] + k0 - p_v (ebar z'_v + cs),
+//   cs = gbar - ebar S - gu - 2 lam gz lse,  k0 = -gu / V,
+// from the upstream gradients gbar (logprob), ebar (entropy), gu
+// (uniform_ce) and gz (z_loss). Ignored tokens: lse = 1e30 (every p
+// underflows to 0) and zeros.
+struct DzToken {
+  float lse, ebar, cs, gbar;
+  float k0, pad0, pad1, pad2;
+};
+
+struct PrepArgs {
+  const int64_t* labels;
+  int64_t N, V, ignore_index;
+  int reduction;               // 0 none, 1 mean, 2 sum
+  float zl_scale;              // lam
+  const float *lse, *entropy;
+  const float *glp, *gent, *guce, *gzl;  // [N] (none), [1] (mean, sum) or null
+  DzToken* coef;
+  int32_t* lab32;
+  int32_t* header;
+};
+
+// One block of 1024: counts, per-token coefficients and int32 labels.
+__global__ void __launch_bounds__(1024) bwd_prep_kernel(PrepArgs a) {
   __shared__ int sh[1024];
   int inv = 0, nv = 0;
-  for (int64_t t = threadIdx.x; t < N; t += 1024) {
-    const int64_t y = labels[t];
-    if (y != ignore_index) {
-      if (y >= 0 && y < V) ++nv;
+  for (int64_t t = threadIdx.x; t < a.N; t += 1024) {
+    const int64_t y = a.labels[t];
+    if (y != a.ignore_index) {
+      if (y >= 0 && y < a.V) ++nv;
       else ++inv;
     }
   }
   inv = block_sum<int, 1024>(inv, sh);
   nv = block_sum<int, 1024>(nv, sh);
-  const float g0 = (mean && glp != nullptr && nv > 0) ? glp[0] / (float)nv : 0.f;
-  const float e0 = (mean && gent != nullptr && nv > 0) ? gent[0] / (float)nv : 0.f;
-  for (int64_t t = threadIdx.x; t < N; t += 1024) {
-    const int64_t y = labels[t];
-    if (y != ignore_index && y >= 0 && y < V) {
-      const float g = mean ? g0 : (glp != nullptr ? glp[t] : 0.f);
-      const float e = mean ? e0 : (gent != nullptr ? gent[t] : 0.f);
-      const float l = lse[t];
-      coef[t] = make_float4(l, l - entropy[t], g, e);
-      lab32[t] = (int32_t)y;
-    } else {
-      coef[t] = make_float4(1e30f, 0.f, 0.f, 0.f);
-      lab32[t] = -1;
+  // Scalar gradients of a mean are spread over the n valid tokens; those of
+  // a sum apply as they are.
+  const bool scalar = a.reduction != 0;
+  const float div = a.reduction == 1 ? (nv > 0 ? 1.f / (float)nv : 0.f) : 1.f;
+  auto scal = [&](const float* g) { return (scalar && g != nullptr) ? g[0] * div : 0.f; };
+  const float g0 = scal(a.glp), e0 = scal(a.gent), u0 = scal(a.guce), z0 = scal(a.gzl);
+  const float invV = 1.f / (float)a.V;
+  for (int64_t t = threadIdx.x; t < a.N; t += 1024) {
+    const int64_t y = a.labels[t];
+    DzToken c{1e30f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int32_t lab = -1;
+    if (y != a.ignore_index && y >= 0 && y < a.V) {
+      auto per = [&](const float* g, float s0) { return scalar ? s0 : (g != nullptr ? g[t] : 0.f); };
+      const float g = per(a.glp, g0), e = per(a.gent, e0), u = per(a.guce, u0), z = per(a.gzl, z0);
+      const float l = a.lse[t];
+      const float S = l - a.entropy[t];
+      c.lse = l;
+      c.ebar = e;
+      c.cs = g - e * S - u - 2.f * a.zl_scale * z * l;
+      c.gbar = g;
+      c.k0 = -u * invV;
+      lab = (int32_t)y;
     }
+    a.coef[t] = c;
+    a.lab32[t] = lab;
   }
   if (threadIdx.x == 0) {
-    header[0] = inv;
-    header[1] = nv;
+    a.header[0] = inv;
+    a.header[1] = nv;
   }
 }
 
@@ -441,10 +507,10 @@ __global__ void __launch_bounds__(1024) bwd_prep_kernel(
 struct DlogitsArgs {
   const uint16_t* weight;  // [H,V]
   const uint16_t* xb;      // blocked hidden
-  const float4* coef;      // [N]
+  const DzToken* coef;     // [N]
   const int32_t* lab;      // [N]
   int64_t N, H, V;
-  int hkb;                 // K blocks of the weight^T / hidden strips
+  int hkb;                 // K blocks of the hidden strips
   int64_t v0;              // first vocabulary column of this chunk (multiple of 256)
   int VTc, TB;             // vocabulary tiles in the chunk, token blocks
   int group;
@@ -459,8 +525,9 @@ struct DlogitsArgs {
 struct DzCoef {
   float nl;       // -lse * log2(e)
   float ebar;     // upstream entropy gradient
-  float cS;       // gbar - ebar * S
+  float cS;       // gbar - ebar S - gu - 2 lam gz lse
   float gbar;     // upstream logprob gradient (the label term)
+  float k0;       // -gu / V (the uniform cross-entropy term)
   float cap, cap_k, inv_cap;
 };
 
@@ -487,9 +554,9 @@ __device__ __forceinline__ void dz_column(const Acc& acc, int j, const DzCoef& k
         const float p = fast_exp2(fmaf(z, kLog2e, k.nl));
         float v;
         if constexpr (LABEL)
-          v = fmaf(-p, fmaf(k.ebar, z, k.cS), o == yl ? k.gbar : 0.f);
+          v = fmaf(-p, fmaf(k.ebar, z, k.cS), o == yl ? k.gbar + k.k0 : k.k0);
         else
-          v = -p * fmaf(k.ebar, z, k.cS);
+          v = fmaf(-p, fmaf(k.ebar, z, k.cS), k.k0);
         if constexpr (CAP) {
           const float qz = z * k.inv_cap;
           v *= fmaf(-qz, qz, 1.f);
@@ -511,7 +578,8 @@ __device__ __forceinline__ void dz_column(const Acc& acc, int j, const DzCoef& k
   }
 }
 
-// dz' = gbar ([v == y] - p) - ebar p (z' - S), dz = dz' (1 - (z'/c)^2) if
+// dz' = gbar ([v == y] - p) - ebar p (z' - S) + gu (p - 1/V) + 2 lam gz lse p
+// (the gradient of the four per-token outputs), dz = dz' (1 - (z'/c)^2) if
 // capped, rounded to bf16 and written into both blocked images of the chunk:
 // dtv (the A operand of dH = D W^T) and dvt (the B operand of dW = hidden^T D).
 // Tokens past N have coefficients that make dz = 0, vocabulary rows past V
@@ -555,7 +623,7 @@ bwd_dlogits_kernel(DlogitsArgs a) {
   for (int j = 0; j < 2; ++j) {
     const int n = acc_col(wn, j, lane);
     const int64_t t = n0 + n;
-    float4 c = make_float4(1e30f, 0.f, 0.f, 0.f);
+    DzToken c{1e30f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int y = -1;
     if (t < a.N) {
       c = a.coef[t];
@@ -564,7 +632,7 @@ bwd_dlogits_kernel(DlogitsArgs a) {
     // The label's row offset within this lane's rows, or -1.
     const int64_t yo = (int64_t)y - vg0 - wm * 128 - 4 * lh;
     const int yl = (y >= 0 && yo >= 0 && yo < 128) ? (int)yo : -1;
-    const DzCoef k{-c.x * kLog2e, c.w, c.z - c.w * c.y, c.z, a.cap, a.cap_k, a.inv_cap};
+    const DzCoef k{-c.lse * kLog2e, c.ebar, c.cs, c.gbar, c.k0, a.cap, a.cap_k, a.inv_cap};
     // Wave-uniform choice of the variant: the label term is needed by few
     // waves, the row mask only in the last vocabulary tile.
     const bool any_label = __builtin_amdgcn_ballot_w64(yl >= 0) != 0;
@@ -607,13 +675,14 @@ struct DxArgs {
   int TB, HT;              // token blocks, hidden tiles
   int group;
   float* acc;              // [N,H] fp32 accumulator over chunks
-  uint16_t* gh;            // [N,H] bf16 output
+  void* gh;                // [N,H] output, bf16 or fp32 (F32OUT)
 };
 
 // C[t][h] = sum_v D[t][v] W[h][v0 + v] over the chunk. MODE: DX_ONLY (single chunk: write
-// bf16), DX_FIRST (store fp32), DX_MID (add into fp32), DX_LAST (add and write
-// bf16). Out-of-range rows and columns fall outside the buffer resources.
-template <int MODE>
+// the output), DX_FIRST (store fp32), DX_MID (add into fp32), DX_LAST (add and
+// write the output). F32OUT: the output is fp32, else bf16. Out-of-range rows
+// and columns fall outside the buffer resources.
+template <int MODE, bool F32OUT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(2, 2)))
 bwd_dx_kernel(DxArgs a) {
@@ -631,7 +700,9 @@ bwd_dx_kernel(DxArgs a) {
   }
   const int64_t base = m0 * a.H + h0;
   const int64_t span = (a.N - m0) * a.H - h0;  // elements from the tile origin to the end
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gh + base, span * 2);
+  constexpr int kOut = F32OUT ? 4 : 2;  // bytes per output element
+  const __amdgpu_buffer_rsrc_t rg =
+      make_rsrc(static_cast<char*>(a.gh) + base * kOut, span * kOut);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.acc + base, span * 4);
   // Per 4 accumulator rows of a 32 x 32 block, a quad transpose hands lane
   // 4q+a row (first + a) at the quad's four columns: 16-byte fp32 and 8-byte
@@ -649,14 +720,18 @@ bwd_dx_kernel(DxArgs a) {
         const uint32_t e = (uint32_t)(row * a.H + hq);
         const float x[4] = {acc[i][j][rq * 4], acc[i][j][rq * 4 + 1], acc[i][j][rq * 4 + 2],
                             acc[i][j][rq * 4 + 3]};
-        if constexpr (MODE == DX_ONLY) {
+        if constexpr (MODE == DX_ONLY && !F32OUT) {
           const u32x2_t v = quad_transpose_bf16(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
           buf_store_u32x2(v, rg, hok ? e * 2 : kOOB);
+        } else if constexpr (MODE == DX_ONLY) {
+          buf_store_f32x4(quad_transpose_f32(x[0], x[1], x[2], x[3]), rg, hok ? e * 4 : kOOB);
         } else {
           f32x4_t v = quad_transpose_f32(x[0], x[1], x[2], x[3]);
           const uint32_t o = hok ? e * 4 : kOOB;
           if constexpr (MODE != DX_FIRST) v += buf_load_f32x4(ra, o);
-          if constexpr (MODE == DX_LAST)
+          if constexpr (MODE == DX_LAST && F32OUT)
+            buf_store_f32x4(v, rg, o);
+          else if constexpr (MODE == DX_LAST)
             buf_store_u32x2(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rg,
                             hok ? e * 2 : kOOB);
           else
@@ -679,12 +754,12 @@ struct DwArgs {
   int group;
   int kper;                // K blocks per split
   int64_t ldp;             // row stride of the split partials
-  uint16_t* gw;            // [H,V] bf16 output
+  void* gw;                // [H,V] output, bf16 or fp32 (F32OUT)
   float* part;             // [splits][H][ldp] fp32 (SPLIT only)
 };
 
 // C[h][v] = sum_t hidden[t][h] D[t][v] over the split's tokens.
-template <bool SPLIT>
+template <bool SPLIT, bool F32OUT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(2, 2)))
 bwd_dw_kernel(DwArgs a) {
@@ -715,8 +790,10 @@ bwd_dw_kernel(DwArgs a) {
     base = h0 * ld + a.v0 + vl0;
     span = (a.H - h0) * ld - (a.v0 + vl0);
   }
+  constexpr int kOut = (SPLIT || F32OUT) ? 4 : 2;  // bytes per stored element
   const __amdgpu_buffer_rsrc_t rs =
-      SPLIT ? make_rsrc(a.part + base, span * 4) : make_rsrc(a.gw + base, span * 2);
+      SPLIT ? make_rsrc(a.part + base, span * 4)
+            : make_rsrc(static_cast<char*>(a.gw) + base * kOut, span * kOut);
   // Quad transposes as in bwd_dx_kernel; vc is a multiple of 8.
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -730,7 +807,7 @@ bwd_dw_kernel(DwArgs a) {
         const uint32_t e = (uint32_t)(row * ld + vq);
         const float x[4] = {acc[i][j][rq * 4], acc[i][j][rq * 4 + 1], acc[i][j][rq * 4 + 2],
                             acc[i][j][rq * 4 + 3]};
-        if constexpr (SPLIT)
+        if constexpr (SPLIT || F32OUT)
           buf_store_f32x4(quad_transpose_f32(x[0], x[1], x[2], x[3]), rs, vok ? e * 4 : kOOB);
         else
           buf_store_u32x2(quad_transpose_bf16(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])), rs,
@@ -740,17 +817,21 @@ bwd_dw_kernel(DwArgs a) {
   }
 }
 
-// Sums the split partials in split order and writes bf16 dW for the chunk.
+// Sums the split partials in split order and writes dW for the chunk (bf16,
+// or fp32 with F32OUT).
+template <bool F32OUT>
 __global__ void __launch_bounds__(256) dw_reduce_kernel(const float* __restrict__ part, int splits,
                                                         int64_t H, int64_t vc, int64_t ldd,
-                                                        int64_t V, int64_t v0,
-                                                        uint16_t* __restrict__ gw) {
+                                                        int64_t V, int64_t v0, void* gw) {
   const int64_t n = H * vc;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
     const int64_t h = e / vc, v = e % vc;
     float s = 0.f;
     for (int k = 0; k < splits; ++k) s += part[((int64_t)k * H + h) * ldd + v];
-    gw[h * V + v0 + v] = (uint16_t)(pack_bf16x2(s, 0.f) & 0xFFFFu);
+    if constexpr (F32OUT)
+      static_cast<float*>(gw)[h * V + v0 + v] = s;
+    else
+      static_cast<uint16_t*>(gw)[h * V + v0 + v] = (uint16_t)(pack_bf16x2(s, 0.f) & 0xFFFFu);
   }
 }
 

@@ -3,9 +3,10 @@
 Two layers, both argument marshalling only:
 
 * ``flce_workspace_size``, ``flce_forward``, ``flce_backward``,
-  ``flce_get_status``, ... : one Python function per C entry point, same name,
-  same arguments (device pointers and streams as integers). A non-OK status
-  raises ``FlceError``.
+  ``flce_forward_ex``, ``flce_backward_ex``, ``flce_get_status``, ... : one
+  Python function per C entry point, same name, same arguments (device
+  pointers and streams as integers, the options as ``FlceOptions``). A non-OK
+  status raises ``FlceError``.
 * ``forward`` / ``backward``: take torch CUDA tensors, check dtypes and
   layouts, allocate outputs and the workspace with torch (so torch's caching
   allocator owns all memory), and call the C entry points on torch's current
@@ -21,8 +22,10 @@ import os
 
 __all__ = [
     "FlceError", "lib", "LIB_PATH",
-    "FLCE_REDUCTION_NONE", "FLCE_REDUCTION_MEAN",
-    "flce_workspace_size", "flce_forward", "flce_backward", "flce_get_status",
+    "FLCE_REDUCTION_NONE", "FLCE_REDUCTION_MEAN", "FLCE_REDUCTION_SUM",
+    "FLCE_GRAD_BF16", "FLCE_GRAD_F32", "FlceOptions",
+    "flce_workspace_size", "flce_forward", "flce_backward", "flce_forward_ex",
+    "flce_backward_ex", "flce_get_status",
     "flce_status_string", "flce_version", "flce_profile_enable", "flce_profile_reset",
     "flce_profile_kinds", "flce_profile_read", "profile_table",
     "forward", "backward", "workspace_bytes",
@@ -32,14 +35,26 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflce.so"
 
 FLCE_REDUCTION_NONE = 0
 FLCE_REDUCTION_MEAN = 1
-_REDUCTIONS = {"none": FLCE_REDUCTION_NONE, "mean": FLCE_REDUCTION_MEAN}
+FLCE_REDUCTION_SUM = 2
+_REDUCTIONS = {"none": FLCE_REDUCTION_NONE, "mean": FLCE_REDUCTION_MEAN,
+               "sum": FLCE_REDUCTION_SUM}
+FLCE_GRAD_BF16 = 0
+FLCE_GRAD_F32 = 1
+_GRAD_DTYPES = {"bf16": FLCE_GRAD_BF16, "f32": FLCE_GRAD_F32}
 
 STATUS_NAMES = {
     0: "FLCE_OK", 1: "FLCE_ERR_NULL_POINTER", 2: "FLCE_ERR_BAD_SHAPE",
     3: "FLCE_ERR_BAD_REDUCTION", 4: "FLCE_ERR_MISALIGNED",
     5: "FLCE_ERR_WORKSPACE_TOO_SMALL", 6: "FLCE_ERR_BAD_SOFTCAP", 7: "FLCE_ERR_HIP",
-    8: "FLCE_ERR_INVALID_LABEL",
+    8: "FLCE_ERR_INVALID_LABEL", 9: "FLCE_ERR_BAD_OPTION",
 }
+
+
+class FlceOptions(ctypes.Structure):
+    """flce_options_t."""
+    _fields_ = [("ignore_index", ctypes.c_int64), ("softcap", ctypes.c_float),
+                ("reduction", ctypes.c_int), ("z_loss_scale", ctypes.c_float),
+                ("grad_dtype", ctypes.c_int)]
 
 # Every exported symbol with its (restype, argtypes).
 _P = ctypes.c_void_p
@@ -53,6 +68,10 @@ _SIG = {
     "flce_backward": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
                                      ctypes.c_int, _P, _P, _P, _P, _P, _P, _P,
                                      ctypes.c_size_t, _P]),
+    "flce_forward_ex": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, ctypes.POINTER(FlceOptions),
+                                       _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "flce_backward_ex": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, ctypes.POINTER(FlceOptions),
+                                        _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "flce_get_status": (ctypes.c_int, [_P, ctypes.POINTER(_I64), _P]),
     "flce_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "flce_version": (ctypes.c_int, []),
@@ -124,6 +143,22 @@ def flce_backward(hidden, weight, labels, N, H, V, ignore_index, softcap, reduct
                                reduction, lse, entropy, grad_logprob, grad_entropy,
                                grad_hidden, grad_weight, workspace, workspace_bytes, stream),
            "flce_backward")
+
+
+def flce_forward_ex(hidden, weight, labels, N, H, V, opt, lse, logprob, entropy, uniform_ce,
+                    z_loss, reduced, workspace, workspace_bytes, stream):
+    _check(lib().flce_forward_ex(hidden, weight, labels, N, H, V, ctypes.byref(opt), lse,
+                                 logprob, entropy, uniform_ce, z_loss, reduced, workspace,
+                                 workspace_bytes, stream), "flce_forward_ex")
+
+
+def flce_backward_ex(hidden, weight, labels, N, H, V, opt, lse, entropy, grad_logprob,
+                     grad_entropy, grad_uniform_ce, grad_z_loss, grad_hidden, grad_weight,
+                     workspace, workspace_bytes, stream):
+    _check(lib().flce_backward_ex(hidden, weight, labels, N, H, V, ctypes.byref(opt), lse,
+                                  entropy, grad_logprob, grad_entropy, grad_uniform_ce,
+                                  grad_z_loss, grad_hidden, grad_weight, workspace,
+                                  workspace_bytes, stream), "flce_backward_ex")
 
 
 def flce_get_status(workspace, stream) -> int:
@@ -199,11 +234,22 @@ def workspace_bytes(N: int, H: int, V: int, reduction: str = "none"):
     return flce_workspace_size(N, H, V, _REDUCTIONS[reduction])
 
 
-def forward(hidden, weight, labels, ignore_index: int = -100, softcap: float = 0.0,
-            reduction: str = "none", workspace=None) -> dict:
-    """lse, logprob, entropy [N] (fp32) and, under "mean", the two means.
+_OUT_NAMES = ("logprob", "entropy", "uniform_ce", "z_loss")
 
-    hidden: bf16 [N,H]; weight: bf16 [H,V]; labels: int64 [N].
+
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
+def forward(hidden, weight, labels, ignore_index: int = -100, softcap: float = 0.0,
+            reduction: str = "none", z_loss_scale: float = 0.0, aux: bool = False,
+            workspace=None) -> dict:
+    """lse, logprob, entropy [N] (fp32); with ``aux`` also uniform_ce and
+    z_loss [N]; under "mean" / "sum" the reductions as ``<name>_mean`` /
+    ``<name>_sum`` (fp32 [1]).
+
+    hidden: bf16 [N,H]; weight: bf16 [H,V]; labels: int64 [N]. Without aux,
+    z-loss and "sum" this calls flce_forward, else flce_forward_ex.
     """
     torch = _torch()
     _require(hidden, torch.bfloat16, 2, "hidden")
@@ -215,34 +261,52 @@ def forward(hidden, weight, labels, ignore_index: int = -100, softcap: float = 0
         raise ValueError("shape mismatch among hidden [N,H], weight [H,V], labels [N]")
     red = _REDUCTIONS[reduction]
     fbytes, _ = flce_workspace_size(N, H, V, red)
-    if workspace is None:
+    if workspace is None or workspace.numel() < fbytes:
         workspace = torch.empty(max(fbytes, 256), dtype=torch.uint8, device=hidden.device)
     dev = hidden.device
-    lse = torch.empty(N, dtype=torch.float32, device=dev)
-    lp = torch.empty(N, dtype=torch.float32, device=dev)
-    ent = torch.empty(N, dtype=torch.float32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    lse = torch.empty(N, **f32)
+    lp = torch.empty(N, **f32)
+    ent = torch.empty(N, **f32)
     out = {"lse": lse, "logprob": lp, "entropy": ent, "workspace": workspace}
-    lpm = entm = None
-    if red == FLCE_REDUCTION_MEAN:
-        lpm = torch.empty(1, dtype=torch.float32, device=dev)
-        entm = torch.empty(1, dtype=torch.float32, device=dev)
-        out["logprob_mean"] = lpm
-        out["entropy_mean"] = entm
-    flce_forward(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), N, H, V,
-                 int(ignore_index), float(softcap), red, lse.data_ptr(), lp.data_ptr(),
-                 ent.data_ptr(), lpm.data_ptr() if lpm is not None else None,
-                 entm.data_ptr() if entm is not None else None, workspace.data_ptr(),
-                 workspace.numel(), _stream())
+    extended = aux or z_loss_scale != 0.0 or red == FLCE_REDUCTION_SUM
+    if not extended:
+        lpm = entm = None
+        if red == FLCE_REDUCTION_MEAN:
+            lpm = torch.empty(1, **f32)
+            entm = torch.empty(1, **f32)
+            out["logprob_mean"] = lpm
+            out["entropy_mean"] = entm
+        flce_forward(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), N, H, V,
+                     int(ignore_index), float(softcap), red, lse.data_ptr(), lp.data_ptr(),
+                     ent.data_ptr(), _ptr(lpm), _ptr(entm), workspace.data_ptr(),
+                     workspace.numel(), _stream())
+        return out
+    uce = torch.empty(N, **f32) if aux else None
+    zl = torch.empty(N, **f32) if aux else None
+    reduced = torch.empty(4, **f32) if red != FLCE_REDUCTION_NONE else None
+    opt = FlceOptions(int(ignore_index), float(softcap), red, float(z_loss_scale), FLCE_GRAD_BF16)
+    flce_forward_ex(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), N, H, V, opt,
+                    lse.data_ptr(), lp.data_ptr(), ent.data_ptr(), _ptr(uce), _ptr(zl),
+                    _ptr(reduced), workspace.data_ptr(), workspace.numel(), _stream())
+    if aux:
+        out["uniform_ce"] = uce
+        out["z_loss"] = zl
+    if reduced is not None:
+        for k, name in enumerate(_OUT_NAMES):
+            out[f"{name}_{reduction}"] = reduced[k:k + 1]
     return out
 
 
 def backward(hidden, weight, labels, lse, entropy, grad_logprob=None, grad_entropy=None,
              ignore_index: int = -100, softcap: float = 0.0, reduction: str = "none",
-             workspace=None):
-    """(grad_hidden bf16 [N,H], grad_weight bf16 [H,V]).
+             grad_uniform_ce=None, grad_z_loss=None, z_loss_scale: float = 0.0,
+             grad_dtype: str = "bf16", workspace=None):
+    """(grad_hidden [N,H], grad_weight [H,V]), bf16 or fp32 (``grad_dtype``).
 
-    grad_logprob / grad_entropy: fp32 [N] under "none", fp32 [1] under "mean",
-    or None for zero.
+    Upstream gradients: fp32 [N] under "none", fp32 [1] under "mean" and
+    "sum", or None for zero. Without the auxiliary gradients, z-loss, "sum"
+    and fp32 outputs this calls flce_backward, else flce_backward_ex.
     """
     torch = _torch()
     _require(hidden, torch.bfloat16, 2, "hidden")
@@ -253,8 +317,11 @@ def backward(hidden, weight, labels, lse, entropy, grad_logprob=None, grad_entro
     N, H = hidden.shape
     V = weight.shape[1]
     red = _REDUCTIONS[reduction]
+    gdt = _GRAD_DTYPES[grad_dtype]
     want = N if red == FLCE_REDUCTION_NONE else 1
-    for g, name in ((grad_logprob, "grad_logprob"), (grad_entropy, "grad_entropy")):
+    grads = ((grad_logprob, "grad_logprob"), (grad_entropy, "grad_entropy"),
+             (grad_uniform_ce, "grad_uniform_ce"), (grad_z_loss, "grad_z_loss"))
+    for g, name in grads:
         if g is not None:
             _require(g, torch.float32, 1, name)
             if g.shape[0] != want:
@@ -262,12 +329,20 @@ def backward(hidden, weight, labels, lse, entropy, grad_logprob=None, grad_entro
     _, bbytes = flce_workspace_size(N, H, V, red)
     if workspace is None or workspace.numel() < bbytes:
         workspace = torch.empty(max(bbytes, 256), dtype=torch.uint8, device=hidden.device)
-    gh = torch.empty((N, H), dtype=torch.bfloat16, device=hidden.device)
-    gw = torch.empty((H, V), dtype=torch.bfloat16, device=hidden.device)
-    flce_backward(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), N, H, V,
-                  int(ignore_index), float(softcap), red, lse.data_ptr(), entropy.data_ptr(),
-                  grad_logprob.data_ptr() if grad_logprob is not None else None,
-                  grad_entropy.data_ptr() if grad_entropy is not None else None,
-                  gh.data_ptr(), gw.data_ptr(), workspace.data_ptr(), workspace.numel(),
-                  _stream())
+    odt = torch.float32 if gdt == FLCE_GRAD_F32 else torch.bfloat16
+    gh = torch.empty((N, H), dtype=odt, device=hidden.device)
+    gw = torch.empty((H, V), dtype=odt, device=hidden.device)
+    extended = (grad_uniform_ce is not None or grad_z_loss is not None or z_loss_scale != 0.0
+                or red == FLCE_REDUCTION_SUM or gdt != FLCE_GRAD_BF16)
+    if not extended:
+        flce_backward(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), N, H, V,
+                      int(ignore_index), float(softcap), red, lse.data_ptr(), entropy.data_ptr(),
+                      _ptr(grad_logprob), _ptr(grad_entropy), gh.data_ptr(), gw.data_ptr(),
+                      workspace.data_ptr(), workspace.numel(), _stream())
+        return gh, gw
+    opt = FlceOptions(int(ignore_index), float(softcap), red, float(z_loss_scale), gdt)
+    flce_backward_ex(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), N, H, V, opt,
+                     lse.data_ptr(), entropy.data_ptr(), _ptr(grad_logprob), _ptr(grad_entropy),
+                     _ptr(grad_uniform_ce), _ptr(grad_z_loss), gh.data_ptr(), gw.data_ptr(),
+                     workspace.data_ptr(), workspace.numel(), _stream())
     return gh, gw

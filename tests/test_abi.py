@@ -42,7 +42,7 @@ def test_exports_match_header():
 
 
 def test_status_strings():
-    for code in range(9):
+    for code in range(10):
         assert flce.flce_status_string(code)
     assert "unknown" in flce.flce_status_string(99)
 
@@ -75,11 +75,11 @@ def _bwd(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(hidden=None), 1), (dict(weight=None), 1), (dict(labels=None), 1), (dict(lse=None), 1),
-    (dict(ws=None), 1), (dict(red=1), 1),                      # mean needs the mean outputs
+    (dict(ws=None), 1), (dict(red=1), 1), (dict(red=2), 1),    # mean / sum need the outputs
     (dict(N=-1), 2), (dict(N=(1 << 21) + 1), 2), (dict(H=0), 2), (dict(V=0), 2),
     (dict(H=(1 << 20) + 8), 2),
     (dict(V=(1 << 22) + 8), 2),
-    (dict(red=2), 3), (dict(red=-1), 3),
+    (dict(red=3), 3), (dict(red=-1), 3),
     (dict(H=12), 4), (dict(V=1001), 4), (dict(hidden=A + 2), 4), (dict(weight=A + 8), 4),
     (dict(ws=A + 4), 4),
     (dict(wsb=16), 5),
@@ -121,3 +121,68 @@ def test_profile_hooks_host_only():
     assert name == "fwd_tile" and n == 0 and ms == 0.0
     with pytest.raises(flce.FlceError):
         flce.flce_profile_read(99)
+
+
+def _opt(**kw):
+    o = dict(ignore_index=-100, softcap=0.0, reduction=0, z_loss_scale=0.0, grad_dtype=0)
+    o.update(kw)
+    return flce.FlceOptions(o["ignore_index"], o["softcap"], o["reduction"], o["z_loss_scale"],
+                            o["grad_dtype"])
+
+
+def _fwd_ex(opt=None, **kw):
+    args = dict(hidden=A, weight=A, labels=A, N=4, H=8, V=8, lse=A, lp=A, ent=A, uce=None,
+                zl=None, red=None, ws=A, wsb=BIG, st=None)
+    args.update(kw)
+    o = ctypes.byref(opt) if opt is not None else None
+    return flce.lib().flce_forward_ex(args["hidden"], args["weight"], args["labels"], args["N"],
+                                      args["H"], args["V"], o, args["lse"], args["lp"],
+                                      args["ent"], args["uce"], args["zl"], args["red"],
+                                      args["ws"], args["wsb"], args["st"])
+
+
+def _bwd_ex(opt=None, **kw):
+    args = dict(hidden=A, weight=A, labels=A, N=4, H=8, V=8, lse=A, ent=A, g=A, e=A, gu=None,
+                gz=None, gh=A, gw=A, ws=A, wsb=BIG, st=None)
+    args.update(kw)
+    o = ctypes.byref(opt) if opt is not None else None
+    return flce.lib().flce_backward_ex(args["hidden"], args["weight"], args["labels"], args["N"],
+                                       args["H"], args["V"], o, args["lse"], args["ent"],
+                                       args["g"], args["e"], args["gu"], args["gz"], args["gh"],
+                                       args["gw"], args["ws"], args["wsb"], args["st"])
+
+
+@pytest.mark.parametrize("okw,kw,code", [
+    (None, {}, 1),                                          # no options
+    (dict(reduction=1), {}, 1), (dict(reduction=2), {}, 1),  # reduced outputs required
+    (dict(reduction=5), {}, 3),
+    (dict(softcap=float("nan")), {}, 6),
+    (dict(z_loss_scale=-0.5), {}, 9), (dict(z_loss_scale=float("inf")), {}, 9),
+    (dict(grad_dtype=3), {}, 9),
+    (dict(), dict(N=-2), 2), (dict(), dict(V=12), 4), (dict(), dict(wsb=8), 5),
+])
+def test_forward_ex_rejects(okw, kw, code):
+    assert _fwd_ex(_opt(**okw) if okw is not None else None, **kw) == code
+
+
+@pytest.mark.parametrize("okw,kw,code", [
+    (None, {}, 1),
+    (dict(reduction=-3), {}, 3),
+    (dict(z_loss_scale=float("nan")), {}, 9), (dict(grad_dtype=-1), {}, 9),
+    (dict(grad_dtype=1), dict(V=(1 << 21) + 8), 2),           # fp32 gradients: V <= 2^21
+    (dict(), dict(gw=None), 1), (dict(), dict(gh=A + 4), 4), (dict(), dict(wsb=8), 5),
+])
+def test_backward_ex_rejects(okw, kw, code):
+    assert _bwd_ex(_opt(**okw) if okw is not None else None, **kw) == code
+
+
+def test_options_layout():
+    # flce_options_t: int64, float, int, float, int -> 24 bytes with natural alignment.
+    assert ctypes.sizeof(flce.FlceOptions) == 24
+    assert flce.FlceOptions.reduction.offset == 12 and flce.FlceOptions.grad_dtype.offset == 20
+
+
+def test_workspace_size_sum():
+    f0, b0 = flce.flce_workspace_size(4096, 4096, 32000, 0)
+    f2, b2 = flce.flce_workspace_size(4096, 4096, 32000, 2)
+    assert f2 > f0 and b2 == b0
