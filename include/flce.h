@@ -190,6 +190,69 @@ flce_status_t flce_backward_ex(const void* hidden, const void* weight, const int
                                void* grad_hidden, void* grad_weight,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Vocabulary-sharded head ------------------------------------------------
+ * The vocabulary is split into slices [v_begin, v_begin + Vs) of V_total
+ * classes, each with its own weight slice weight_shard [H,Vs] (row-major, the
+ * columns v_begin .. v_begin+Vs-1 of the full [H,V_total] weight), e.g. one per
+ * GPU under tensor parallelism. Labels stay global class ids.
+ *
+ *   1. flce_forward_shard per slice: the per-token online-softmax state of the
+ *      slice, {m, s, u, sum z'} with lse_slice = m + ln s, and the label logit
+ *      (0 when the label lies in another slice). 20 bytes per token.
+ *   2. Gather the S slices' states into [S,N,4] and label logits into [S,N]
+ *      (an all-gather across GPUs) and call flce_merge_shards once: it merges
+ *      them in slice order with the same combine as the unsharded forward and
+ *      writes the outputs of flce_forward_ex.
+ *   3. flce_backward_shard per slice with the merged lse and entropy: the
+ *      slice's grad_weight [H,Vs] and its partial grad_hidden [N,H]; the sum
+ *      over slices of the partials is grad_hidden (an all-reduce across GPUs;
+ *      fp32 partials, opt->grad_dtype = FLCE_GRAD_F32, keep that sum exact to
+ *      fp32 rounding).
+ * The slice calls need Vs, v_begin within V_total (FLCE_ERR_BAD_SHAPE
+ * otherwise); Vs follows the rules of V above; v_begin has no alignment rule.
+ */
+
+/* Slice forward. hidden, labels as flce_forward_ex; opt->reduction is ignored.
+ *   state        device fp32 [N,4], 16-byte aligned: per token {m, s, u, sum z'}
+ *                of the slice (natural-log units; {-1e30, 0, 0, 0} for ignored
+ *                tokens)
+ *   label_logit  device fp32 [N]: the capped label logit if the label lies in
+ *                this slice, else 0
+ * Workspace: the forward size of flce_workspace_size(N, H, Vs, ...). */
+flce_status_t flce_forward_shard(const void* hidden, const void* weight_shard,
+                                 const int64_t* labels, int64_t N, int64_t H, int64_t Vs,
+                                 int64_t v_begin, int64_t V_total, const flce_options_t* opt,
+                                 float* state, float* label_logit, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of flce_merge_shards for N tokens (host only). */
+flce_status_t flce_merge_workspace_size(int64_t N, size_t* bytes);
+
+/* Merge of S slices: states device fp32 [S,N,4] and label_logits device fp32
+ * [S,N] from flce_forward_shard (slice s at offset s*N*4 / s*N; any slice
+ * order, merged in array order). Outputs as flce_forward_ex (lse, logprob,
+ * entropy required when N > 0; uniform_ce, z_loss optional; reduced [4]
+ * required unless reduction is NONE). 1 <= S <= 65536. */
+flce_status_t flce_merge_shards(const float* states, const float* label_logits, int64_t S,
+                                const int64_t* labels, int64_t N, int64_t V_total,
+                                const flce_options_t* opt, float* lse, float* logprob,
+                                float* entropy, float* uniform_ce, float* z_loss, float* reduced,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Slice backward: arguments as flce_backward_ex with lse and entropy from
+ * flce_merge_shards; writes grad_weight_shard [H,Vs] (the slice's columns of
+ * grad_weight) and grad_hidden_partial [N,H], this slice's share of
+ * grad_hidden. Workspace: the backward size of flce_workspace_size(N, H, Vs,
+ * ...). */
+flce_status_t flce_backward_shard(const void* hidden, const void* weight_shard,
+                                  const int64_t* labels, int64_t N, int64_t H, int64_t Vs,
+                                  int64_t v_begin, int64_t V_total, const flce_options_t* opt,
+                                  const float* lse, const float* entropy,
+                                  const float* grad_logprob, const float* grad_entropy,
+                                  const float* grad_uniform_ce, const float* grad_z_loss,
+                                  void* grad_hidden_partial, void* grad_weight_shard,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Reads the status word that the last flce_forward / flce_backward on this
  * workspace left, after synchronising `stream`. *invalid_labels (may be NULL)
  * receives the number of labels that were neither ignore_index nor in [0, V);

@@ -135,6 +135,13 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   return p;
 }
 
+// Workspace of flce_merge_shards: header, int32 labels, label logits, block sums.
+size_t merge_zlab_off(int64_t N) { return align_up(kHeaderBytes + 4 * (size_t)N); }
+size_t merge_bsum_off(int64_t N) { return align_up(merge_zlab_off(N) + 4 * (size_t)N); }
+size_t merge_bytes(int64_t N) {
+  return align_up(merge_bsum_off(N) + 32 * (size_t)ceil_div(N > 0 ? N : 1, kCombineTokens));
+}
+
 flce_status_t check_shape(int64_t N, int64_t H, int64_t V) {
   if (N < 0 || H < 1 || V < 1) return FLCE_ERR_BAD_SHAPE;
   if (N > kMaxN || H > kMaxH || V > kMaxV) return FLCE_ERR_BAD_SHAPE;
@@ -286,17 +293,26 @@ flce_status_t check_options(const flce_options_t* o) {
 
 // reduced[k] receives the reduction of output k (logprob, entropy,
 // uniform_ce, z_loss); each may be null.
+// V is the vocabulary of `weight` ([H,V]), the slice [v_begin, v_begin + V)
+// of a vocabulary of V_total classes (V_total = V, v_begin = 0 unless
+// sharded). With state_out set (a slice), the per-token merged state and the
+// label logit (label_logit, 0 when the label lies elsewhere) are the outputs
+// instead of the statistics.
 flce_status_t forward_impl(const void* hidden, const void* weight, const int64_t* labels,
-                           int64_t N, int64_t H, int64_t V, const flce_options_t& o, float* lse,
-                           float* logprob, float* entropy, float* uniform_ce, float* z_loss,
-                           float* const (&reduced)[4], void* workspace, size_t workspace_bytes,
-                           void* stream) {
-  const int reduction = o.reduction;
+                           int64_t N, int64_t H, int64_t V, int64_t v_begin, int64_t V_total,
+                           const flce_options_t& o, float* lse, float* logprob, float* entropy,
+                           float* uniform_ce, float* z_loss, float* const (&reduced)[4],
+                           float4* state_out, float* label_logit, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const bool shard = state_out != nullptr;
+  const int reduction = shard ? FLCE_REDUCTION_NONE : o.reduction;
   const bool reduce = reduction != FLCE_REDUCTION_NONE;
   if (workspace == nullptr) return FLCE_ERR_NULL_POINTER;
-  if (N > 0 && (hidden == nullptr || weight == nullptr || labels == nullptr || lse == nullptr ||
-                logprob == nullptr || entropy == nullptr))
+  if (N > 0 && (hidden == nullptr || weight == nullptr || labels == nullptr))
     return FLCE_ERR_NULL_POINTER;
+  if (N > 0 && !shard && (lse == nullptr || logprob == nullptr || entropy == nullptr))
+    return FLCE_ERR_NULL_POINTER;
+  if (N > 0 && shard && label_logit == nullptr) return FLCE_ERR_NULL_POINTER;
   if (!aligned16(hidden) || !aligned16(weight) || !aligned16(workspace)) return FLCE_ERR_MISALIGNED;
   const Plan p = make_plan(N, H, V, reduction);
   if (workspace_bytes < p.f_total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
@@ -306,11 +322,12 @@ flce_status_t forward_impl(const void* hidden, const void* weight, const int64_t
   int32_t* header = reinterpret_cast<int32_t*>(workspace);
   int32_t* lab32 = reinterpret_cast<int32_t*>(wsp(workspace, p.f_lab));
   float4* part = reinterpret_cast<float4*>(wsp(workspace, p.f_part));
-  float* zlab = reinterpret_cast<float*>(wsp(workspace, p.f_zlab));
+  float* zlab = shard ? label_logit : reinterpret_cast<float*>(wsp(workspace, p.f_zlab));
   double4* bsum = reduce ? reinterpret_cast<double4*>(wsp(workspace, p.f_bsum)) : nullptr;
 
   FLCE_TRY(launch(K_FWD_PREP, st, [&] {
-    fwd_prep_kernel<<<1, 1024, 0, st>>>(labels, N, V, o.ignore_index, lab32, header);
+    fwd_prep_kernel<<<1, 1024, 0, st>>>(labels, N, V_total, v_begin, V, o.ignore_index, lab32,
+                                        zlab, header);
   }));
   const int nb = (int)ceil_div(N, kCombineTokens);
   if (N > 0) {
@@ -342,9 +359,11 @@ flce_status_t forward_impl(const void* hidden, const void* weight, const int64_t
     c.part = part;
     c.S = p.VT;
     c.zlab = zlab;
+    c.nz = 1;
     c.lab32 = lab32;
     c.N = N;
-    c.V = V;
+    c.V = V_total;
+    c.state_out = state_out;
     c.zl_scale = o.z_loss_scale;
     c.lse = lse;
     c.logprob = logprob;
@@ -366,8 +385,10 @@ flce_status_t forward_impl(const void* hidden, const void* weight, const int64_t
   return FLCE_OK;
 }
 
+// V, v_begin, V_total as for forward_impl.
 flce_status_t backward_impl(const void* hidden, const void* weight, const int64_t* labels,
-                            int64_t N, int64_t H, int64_t V, const flce_options_t& o,
+                            int64_t N, int64_t H, int64_t V, int64_t v_begin, int64_t V_total,
+                            const flce_options_t& o,
                             const float* lse, const float* entropy, const float* grad_logprob,
                             const float* grad_entropy, const float* grad_uniform_ce,
                             const float* grad_z_loss, void* grad_hidden, void* grad_weight,
@@ -404,8 +425,10 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
   PrepArgs pa{};
   pa.labels = labels;
   pa.N = N;
-  pa.V = V;
+  pa.V = V_total;
   pa.ignore_index = o.ignore_index;
+  pa.v_begin = v_begin;
+  pa.Vs = V;
   pa.reduction = reduction;
   pa.zl_scale = o.z_loss_scale;
   pa.lse = lse;
@@ -551,8 +574,8 @@ flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t
   if (reduction != FLCE_REDUCTION_NONE && (logprob_mean == nullptr || entropy_mean == nullptr))
     return FLCE_ERR_NULL_POINTER;
   float* const red[4] = {logprob_mean, entropy_mean, nullptr, nullptr};
-  return forward_impl(hidden, weight, labels, N, H, V, o, lse, logprob, entropy, nullptr, nullptr,
-                      red, workspace, workspace_bytes, stream);
+  return forward_impl(hidden, weight, labels, N, H, V, 0, V, o, lse, logprob, entropy, nullptr,
+                      nullptr, red, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
 flce_status_t flce_forward_ex(const void* hidden, const void* weight, const int64_t* labels,
@@ -565,8 +588,9 @@ flce_status_t flce_forward_ex(const void* hidden, const void* weight, const int6
   if (opt->reduction != FLCE_REDUCTION_NONE && reduced == nullptr) return FLCE_ERR_NULL_POINTER;
   float* const red[4] = {reduced, reduced ? reduced + 1 : nullptr, reduced ? reduced + 2 : nullptr,
                          reduced ? reduced + 3 : nullptr};
-  return forward_impl(hidden, weight, labels, N, H, V, *opt, lse, logprob, entropy, uniform_ce,
-                      z_loss, red, workspace, workspace_bytes, stream);
+  return forward_impl(hidden, weight, labels, N, H, V, 0, V, *opt, lse, logprob, entropy,
+                      uniform_ce, z_loss, red, nullptr, nullptr, workspace, workspace_bytes,
+                      stream);
 }
 
 flce_status_t flce_backward(const void* hidden, const void* weight, const int64_t* labels,
@@ -578,7 +602,7 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
   FLCE_TRY(check_shape(N, H, V));
   const flce_options_t o{ignore_index, softcap, reduction, 0.f, FLCE_GRAD_BF16};
   FLCE_TRY(check_options(&o));
-  return backward_impl(hidden, weight, labels, N, H, V, o, lse, entropy, grad_logprob,
+  return backward_impl(hidden, weight, labels, N, H, V, 0, V, o, lse, entropy, grad_logprob,
                        grad_entropy, nullptr, nullptr, grad_hidden, grad_weight, workspace,
                        workspace_bytes, stream);
 }
@@ -592,9 +616,118 @@ flce_status_t flce_backward_ex(const void* hidden, const void* weight, const int
                                size_t workspace_bytes, void* stream) {
   FLCE_TRY(check_shape(N, H, V));
   FLCE_TRY(check_options(opt));
-  return backward_impl(hidden, weight, labels, N, H, V, *opt, lse, entropy, grad_logprob,
+  return backward_impl(hidden, weight, labels, N, H, V, 0, V, *opt, lse, entropy, grad_logprob,
                        grad_entropy, grad_uniform_ce, grad_z_loss, grad_hidden, grad_weight,
                        workspace, workspace_bytes, stream);
+}
+
+// ---- vocabulary-sharded head ---------------------------------------------------
+
+static flce_status_t check_slice(int64_t Vs, int64_t v_begin, int64_t V_total) {
+  if (v_begin < 0 || V_total < 1 || V_total > kMaxV || v_begin + Vs > V_total)
+    return FLCE_ERR_BAD_SHAPE;
+  return FLCE_OK;
+}
+
+flce_status_t flce_forward_shard(const void* hidden, const void* weight_shard,
+                                 const int64_t* labels, int64_t N, int64_t H, int64_t Vs,
+                                 int64_t v_begin, int64_t V_total, const flce_options_t* opt,
+                                 float* state, float* label_logit, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  FLCE_TRY(check_shape(N, H, Vs));
+  FLCE_TRY(check_slice(Vs, v_begin, V_total));
+  FLCE_TRY(check_options(opt));
+  if (N > 0 && state == nullptr) return FLCE_ERR_NULL_POINTER;
+  if (state != nullptr && !aligned16(state)) return FLCE_ERR_MISALIGNED;
+  float* const red[4] = {nullptr, nullptr, nullptr, nullptr};
+  flce_options_t o = *opt;
+  o.reduction = FLCE_REDUCTION_NONE;
+  // A non-null state pointer selects the slice outputs, also for N = 0.
+  float4* st4 = reinterpret_cast<float4*>(state != nullptr ? state : workspace);
+  return forward_impl(hidden, weight_shard, labels, N, H, Vs, v_begin, V_total, o, nullptr,
+                      nullptr, nullptr, nullptr, nullptr, red, st4, label_logit, workspace,
+                      workspace_bytes, stream);
+}
+
+flce_status_t flce_merge_workspace_size(int64_t N, size_t* bytes) {
+  if (N < 0 || N > kMaxN) return FLCE_ERR_BAD_SHAPE;
+  if (bytes) *bytes = merge_bytes(N);
+  return FLCE_OK;
+}
+
+flce_status_t flce_merge_shards(const float* states, const float* label_logits, int64_t S,
+                                const int64_t* labels, int64_t N, int64_t V_total,
+                                const flce_options_t* opt, float* lse, float* logprob,
+                                float* entropy, float* uniform_ce, float* z_loss, float* reduced,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (N < 0 || N > kMaxN || S < 1 || S > (int64_t)1 << 16 || V_total < 1 || V_total > kMaxV)
+    return FLCE_ERR_BAD_SHAPE;
+  FLCE_TRY(check_options(opt));
+  const bool reduce = opt->reduction != FLCE_REDUCTION_NONE;
+  if (workspace == nullptr) return FLCE_ERR_NULL_POINTER;
+  if (reduce && reduced == nullptr) return FLCE_ERR_NULL_POINTER;
+  if (N > 0 && (states == nullptr || label_logits == nullptr || labels == nullptr ||
+                lse == nullptr || logprob == nullptr || entropy == nullptr))
+    return FLCE_ERR_NULL_POINTER;
+  if (!aligned16(states) || !aligned16(workspace)) return FLCE_ERR_MISALIGNED;
+  if (workspace_bytes < merge_bytes(N)) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* header = reinterpret_cast<int32_t*>(workspace);
+  int32_t* lab32 = reinterpret_cast<int32_t*>(wsp(workspace, kHeaderBytes));
+  float* zlab = reinterpret_cast<float*>(wsp(workspace, merge_zlab_off(N)));
+  double4* bsum = reduce ? reinterpret_cast<double4*>(wsp(workspace, merge_bsum_off(N))) : nullptr;
+  FLCE_TRY(launch(K_FWD_PREP, st, [&] {
+    fwd_prep_kernel<<<1, 1024, 0, st>>>(labels, N, V_total, 0, V_total, opt->ignore_index, lab32,
+                                        zlab, header);
+  }));
+  const int nb = (int)ceil_div(N, kCombineTokens);
+  if (N > 0) {
+    CombineArgs c{};
+    c.part = reinterpret_cast<const float4*>(states);
+    c.S = (int)S;
+    c.zlab = label_logits;
+    c.nz = (int)S;
+    c.lab32 = lab32;
+    c.N = N;
+    c.V = V_total;
+    c.zl_scale = opt->z_loss_scale;
+    c.lse = lse;
+    c.logprob = logprob;
+    c.entropy = entropy;
+    c.uniform_ce = uniform_ce;
+    c.z_loss = z_loss;
+    c.bsum = bsum;
+    FLCE_TRY(launch(K_FWD_COMBINE, st, [&] {
+      fwd_combine_kernel<<<nb, 64 * kCombineWaves, 0, st>>>(c);
+    }));
+  }
+  if (reduce) {
+    const int mean = opt->reduction == FLCE_REDUCTION_MEAN;
+    FLCE_TRY(launch(K_FWD_REDUCE, st, [&] {
+      fwd_reduce_kernel<<<1, 256, 0, st>>>(bsum, N > 0 ? nb : 0, header, mean, reduced,
+                                           reduced ? reduced + 1 : nullptr,
+                                           reduced ? reduced + 2 : nullptr,
+                                           reduced ? reduced + 3 : nullptr);
+    }));
+  }
+  return FLCE_OK;
+}
+
+flce_status_t flce_backward_shard(const void* hidden, const void* weight_shard,
+                                  const int64_t* labels, int64_t N, int64_t H, int64_t Vs,
+                                  int64_t v_begin, int64_t V_total, const flce_options_t* opt,
+                                  const float* lse, const float* entropy,
+                                  const float* grad_logprob, const float* grad_entropy,
+                                  const float* grad_uniform_ce, const float* grad_z_loss,
+                                  void* grad_hidden_partial, void* grad_weight_shard,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  FLCE_TRY(check_shape(N, H, Vs));
+  FLCE_TRY(check_slice(Vs, v_begin, V_total));
+  FLCE_TRY(check_options(opt));
+  return backward_impl(hidden, weight_shard, labels, N, H, Vs, v_begin, V_total, *opt, lse,
+                       entropy, grad_logprob, grad_entropy, grad_uniform_ce, grad_z_loss,
+                       grad_hidden_partial, grad_weight_shard, workspace, workspace_bytes,
+                       stream);
 }
 
 flce_status_t flce_get_status(const void* workspace, int64_t* invalid_labels, void* stream) {

@@ -44,12 +44,21 @@ __device__ __forceinline__ T block_sum(T v, T* sh) {
 
 // ---- forward: labels -> int32, counts ---------------------------------------
 
-// One block of 1024 threads. lab32[t] = label if it is a valid class id, else
-// -1 (ignored or out of range). header[0] = #labels neither ignore_index nor in
-// [0, V); header[1] = #valid tokens.
+// One block of 1024 threads. The vocabulary slice handled by this call is
+// [v_begin, v_begin + Vs) of V_total classes (the whole vocabulary unless
+// the head is sharded). lab32[t] = y - v_begin for a valid label inside the
+// slice, kLabelElsewhere for a valid label outside it, -1 for an ignored or
+// out-of-range label. zlab[t] = 0 (the logit tiles overwrite it where the
+// label lies in the slice). header[0] = #labels neither ignore_index nor in
+// [0, V_total); header[1] = #valid tokens.
+constexpr int32_t kLabelElsewhere = -2;
+
 __global__ void __launch_bounds__(1024) fwd_prep_kernel(const int64_t* __restrict__ labels,
-                                                        int64_t N, int64_t V, int64_t ignore_index,
+                                                        int64_t N, int64_t V_total,
+                                                        int64_t v_begin, int64_t Vs,
+                                                        int64_t ignore_index,
                                                         int32_t* __restrict__ lab32,
+                                                        float* __restrict__ zlab,
                                                         int32_t* __restrict__ header) {
   __shared__ int sh[1024];
   int inv = 0, nv = 0;
@@ -57,14 +66,15 @@ __global__ void __launch_bounds__(1024) fwd_prep_kernel(const int64_t* __restric
     const int64_t y = labels[t];
     int32_t o = -1;
     if (y != ignore_index) {
-      if (y >= 0 && y < V) {
-        o = (int32_t)y;
+      if (y >= 0 && y < V_total) {
+        o = (y >= v_begin && y < v_begin + Vs) ? (int32_t)(y - v_begin) : kLabelElsewhere;
         ++nv;
       } else {
         ++inv;
       }
     }
     lab32[t] = o;
+    zlab[t] = 0.f;
   }
   inv = block_sum<int, 1024>(inv, sh);
   nv = block_sum<int, 1024>(nv, sh);
@@ -333,22 +343,24 @@ constexpr int kCombineWaves = 16;    // vocabulary-tile groups per combine block
 // over valid tokens. Fixed merge and summation orders: the result does not
 // depend on timing.
 struct CombineArgs {
-  const float4* part;
-  int S;                   // vocabulary tiles
-  const float* zlab;
-  const int32_t* lab32;
-  int64_t N, V;
+  const float4* part;      // [S][N] partial states
+  int S;                   // vocabulary tiles (or slices)
+  const float* zlab;       // [nz][N] label logits, summed (one of them holds each label)
+  int nz;
+  const int32_t* lab32;    // -1: ignored token
+  int64_t N, V;            // V: the whole vocabulary
   float zl_scale;          // lam
   float *lse, *logprob, *entropy;
   float *uniform_ce, *z_loss;  // optional
   double4* bsum;               // optional: {logprob, entropy, uniform_ce, z_loss} per block
+  float4* state_out;           // if set: write the merged state {m, s, u, sum z'} instead
 };
 
 __global__ void __launch_bounds__(1024) fwd_combine_kernel(CombineArgs a) {
   __shared__ float4 st[kCombineWaves][kCombineTokens];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * kCombineTokens + lane;
-  const bool valid = t < a.N && a.lab32[t] >= 0;
+  const bool valid = t < a.N && a.lab32[t] != -1;
   float m = kNegBig, s = 0.f, u = 0.f, zs = 0.f;
   if (valid)
     for (int k = w; k < a.S; k += kCombineWaves) {
@@ -365,12 +377,18 @@ __global__ void __launch_bounds__(1024) fwd_combine_kernel(CombineArgs a) {
     merge_state(m, s, u, q.x, q.y, q.z);
     zs += q.w;
   }
+  if (a.state_out != nullptr) {
+    if (t < a.N) a.state_out[t] = valid ? make_float4(m, s, u, zs) : make_float4(kNegBig, 0.f, 0.f, 0.f);
+    return;
+  }
   double r0 = 0.0, r1 = 0.0, r2 = 0.0, r3 = 0.0;
   if (valid) {
     const float ls = logf(s);
     const float l = m + ls;
     const float e = ls - u / s;
-    const float lp = a.zlab[t] - l;
+    float zy = 0.f;
+    for (int k = 0; k < a.nz; ++k) zy += a.zlab[(int64_t)k * a.N + t];
+    const float lp = zy - l;
     const float uc = l - zs / (float)a.V;
     const float zl = a.zl_scale * l * l;
     a.lse[t] = l;
@@ -447,7 +465,8 @@ struct DzToken {
 
 struct PrepArgs {
   const int64_t* labels;
-  int64_t N, V, ignore_index;
+  int64_t N, V, ignore_index;  // V: the whole vocabulary
+  int64_t v_begin, Vs;         // vocabulary slice of this call
   int reduction;               // 0 none, 1 mean, 2 sum
   float zl_scale;              // lam
   const float *lse, *entropy;
@@ -457,7 +476,9 @@ struct PrepArgs {
   int32_t* header;
 };
 
-// One block of 1024: counts, per-token coefficients and int32 labels.
+// One block of 1024: counts, per-token coefficients and int32 labels
+// (relative to the slice; -1 when the label is ignored or outside the slice,
+// which drops the label term but keeps the token's other terms).
 __global__ void __launch_bounds__(1024) bwd_prep_kernel(PrepArgs a) {
   __shared__ int sh[1024];
   int inv = 0, nv = 0;
@@ -483,15 +504,16 @@ __global__ void __launch_bounds__(1024) bwd_prep_kernel(PrepArgs a) {
     int32_t lab = -1;
     if (y != a.ignore_index && y >= 0 && y < a.V) {
       auto per = [&](const float* g, float s0) { return scalar ? s0 : (g != nullptr ? g[t] : 0.f); };
+      const bool here = y >= a.v_begin && y < a.v_begin + a.Vs;
       const float g = per(a.glp, g0), e = per(a.gent, e0), u = per(a.guce, u0), z = per(a.gzl, z0);
       const float l = a.lse[t];
       const float S = l - a.entropy[t];
       c.lse = l;
       c.ebar = e;
       c.cs = g - e * S - u - 2.f * a.zl_scale * z * l;
-      c.gbar = g;
+      c.gbar = here ? g : 0.f;
       c.k0 = -u * invV;
-      lab = (int32_t)y;
+      lab = here ? (int32_t)(y - a.v_begin) : -1;
     }
     a.coef[t] = c;
     a.lab32[t] = lab;

@@ -72,6 +72,15 @@ _SIG = {
                                        _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "flce_backward_ex": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, ctypes.POINTER(FlceOptions),
                                         _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "flce_forward_shard": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64,
+                                          ctypes.POINTER(FlceOptions), _P, _P, _P,
+                                          ctypes.c_size_t, _P]),
+    "flce_merge_workspace_size": (ctypes.c_int, [_I64, ctypes.POINTER(ctypes.c_size_t)]),
+    "flce_merge_shards": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _I64, ctypes.POINTER(FlceOptions),
+                                         _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "flce_backward_shard": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64,
+                                           ctypes.POINTER(FlceOptions), _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _P, ctypes.c_size_t, _P]),
     "flce_get_status": (ctypes.c_int, [_P, ctypes.POINTER(_I64), _P]),
     "flce_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "flce_version": (ctypes.c_int, []),
@@ -159,6 +168,37 @@ def flce_backward_ex(hidden, weight, labels, N, H, V, opt, lse, entropy, grad_lo
                                   entropy, grad_logprob, grad_entropy, grad_uniform_ce,
                                   grad_z_loss, grad_hidden, grad_weight, workspace,
                                   workspace_bytes, stream), "flce_backward_ex")
+
+
+def flce_forward_shard(hidden, weight_shard, labels, N, H, Vs, v_begin, V_total, opt, state,
+                       label_logit, workspace, workspace_bytes, stream):
+    _check(lib().flce_forward_shard(hidden, weight_shard, labels, N, H, Vs, v_begin, V_total,
+                                    ctypes.byref(opt), state, label_logit, workspace,
+                                    workspace_bytes, stream), "flce_forward_shard")
+
+
+def flce_merge_workspace_size(N: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check(lib().flce_merge_workspace_size(N, ctypes.byref(b)), "flce_merge_workspace_size")
+    return b.value
+
+
+def flce_merge_shards(states, label_logits, S, labels, N, V_total, opt, lse, logprob, entropy,
+                      uniform_ce, z_loss, reduced, workspace, workspace_bytes, stream):
+    _check(lib().flce_merge_shards(states, label_logits, S, labels, N, V_total, ctypes.byref(opt),
+                                   lse, logprob, entropy, uniform_ce, z_loss, reduced, workspace,
+                                   workspace_bytes, stream), "flce_merge_shards")
+
+
+def flce_backward_shard(hidden, weight_shard, labels, N, H, Vs, v_begin, V_total, opt, lse,
+                        entropy, grad_logprob, grad_entropy, grad_uniform_ce, grad_z_loss,
+                        grad_hidden_partial, grad_weight_shard, workspace, workspace_bytes,
+                        stream):
+    _check(lib().flce_backward_shard(hidden, weight_shard, labels, N, H, Vs, v_begin, V_total,
+                                     ctypes.byref(opt), lse, entropy, grad_logprob, grad_entropy,
+                                     grad_uniform_ce, grad_z_loss, grad_hidden_partial,
+                                     grad_weight_shard, workspace, workspace_bytes, stream),
+           "flce_backward_shard")
 
 
 def flce_get_status(workspace, stream) -> int:

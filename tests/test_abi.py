@@ -186,3 +186,33 @@ def test_workspace_size_sum():
     f0, b0 = flce.flce_workspace_size(4096, 4096, 32000, 0)
     f2, b2 = flce.flce_workspace_size(4096, 4096, 32000, 2)
     assert f2 > f0 and b2 == b0
+
+
+def _fwd_shard(opt, **kw):
+    args = dict(hidden=A, weight=A, labels=A, N=4, H=8, Vs=8, v0=0, VT=16, state=A, zl=A, ws=A,
+                wsb=BIG, st=None)
+    args.update(kw)
+    return flce.lib().flce_forward_shard(args["hidden"], args["weight"], args["labels"], args["N"],
+                                         args["H"], args["Vs"], args["v0"], args["VT"],
+                                         ctypes.byref(opt), args["state"], args["zl"], args["ws"],
+                                         args["wsb"], args["st"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v0=-8), 2), (dict(v0=12), 2), (dict(VT=4), 2),    # slice outside [0, V_total)
+    (dict(state=None), 1), (dict(zl=None), 1), (dict(state=A + 4), 4), (dict(Vs=12), 4),
+])
+def test_forward_shard_rejects(kw, code):
+    assert _fwd_shard(_opt(), **kw) == code
+
+
+def test_merge_rejects_and_size():
+    L = flce.lib()
+    o = _opt(reduction=1)
+    assert L.flce_merge_shards(A, A, 0, A, 4, 16, ctypes.byref(o), A, A, A, None, None, A, A, BIG,
+                               None) == 2
+    assert L.flce_merge_shards(A, A, 2, A, 4, 16, ctypes.byref(o), A, A, A, None, None, None, A,
+                               BIG, None) == 1
+    assert L.flce_merge_shards(A, A, 2, A, 4, 16, ctypes.byref(o), A, A, A, None, None, A, A, 8,
+                               None) == 5
+    assert flce.flce_merge_workspace_size(8192) >= 8192 * 8
