@@ -26,7 +26,12 @@ constexpr int64_t kMaxH = (int64_t)1 << 20;
 constexpr int64_t kMaxV = ((int64_t)1 << 22) - 256;
 constexpr int64_t kMaxVc = (int64_t)1 << 18;
 constexpr int kNumCUs = 256;                              // MI355X
-constexpr size_t kDefaultDBudget = (size_t)1 << 30;       // bytes of both bf16 logit-gradient images
+// Bytes of both bf16 logit-gradient images: enough for 16384 columns per
+// chunk (fewer passes over the fp32 dH accumulator, full tile rounds), within
+// [1 GiB, 4 GiB].
+constexpr size_t kMinDBudget = (size_t)1 << 30;
+constexpr size_t kMaxDBudget = (size_t)4 << 30;
+constexpr int64_t kTargetVc = 16384;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -45,9 +50,9 @@ struct Plan {
   int dw_kper;         // K blocks per dW split
   int group;           // tile rows per XCD patch of the block -> tile map
   // forward workspace
-  size_t f_lab, f_part, f_zlab, f_bsum, f_xb, f_total;
+  size_t f_idx, f_labc, f_part, f_zlab, f_bsum, f_xb, f_total;
   // backward workspace
-  size_t b_lab, b_coef, b_wb, b_xb, b_xtb, b_dtv, b_dvt, b_acc, b_part, b_total;
+  size_t b_lab, b_idx, b_coef, b_wb, b_xb, b_xtb, b_dtv, b_dvt, b_acc, b_part, b_total;
 };
 
 size_t env_size(const char* name, size_t dflt) {
@@ -75,8 +80,12 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   // applies to the default budget.
   const size_t budget = env_size("FLCE_D_BUDGET", 0);
   const int64_t vfull = (int64_t)p.VT * kTile;
-  const size_t bud = budget > 0 ? budget : kDefaultDBudget;
   const int64_t npad = (int64_t)(p.TB > 0 ? p.TB : 1) * kTile;
+  size_t bud = budget;
+  if (bud == 0) {
+    bud = 4 * (size_t)npad * (size_t)kTargetVc;
+    bud = bud < kMinDBudget ? kMinDBudget : (bud > kMaxDBudget ? kMaxDBudget : bud);
+  }
   int64_t vc = (int64_t)(bud / (4 * (size_t)npad)) / kTile * kTile;
   if (vc < (budget > 0 ? kTile : 2048)) vc = budget > 0 ? kTile : 2048;
   if (vc > kMaxVc) vc = kMaxVc;
@@ -100,7 +109,9 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
 
   const size_t blk = (size_t)kBlockBytes;
   size_t off = kHeaderBytes;
-  p.f_lab = off;
+  p.f_idx = off;
+  off = align_up(off + 4 * (size_t)N);
+  p.f_labc = off;
   off = align_up(off + 4 * (size_t)N);
   p.f_part = off;
   off = align_up(off + 16 * (size_t)p.VT * (size_t)N);
@@ -114,6 +125,8 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
 
   off = kHeaderBytes;
   p.b_lab = off;
+  off = align_up(off + 4 * (size_t)N);
+  p.b_idx = off;
   off = align_up(off + 4 * (size_t)N);
   p.b_coef = off;
   off = align_up(off + sizeof(DzToken) * (size_t)N);
@@ -135,8 +148,11 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   return p;
 }
 
-// Workspace of flce_merge_shards: header, int32 labels, label logits, block sums.
-size_t merge_zlab_off(int64_t N) { return align_up(kHeaderBytes + 4 * (size_t)N); }
+// Workspace of flce_merge_shards: header, compaction index and codes (the prep
+// kernel's scratch), label logits, block sums.
+size_t merge_idx_off(int64_t N) { return align_up(kHeaderBytes); }
+size_t merge_labc_off(int64_t N) { return align_up(merge_idx_off(N) + 4 * (size_t)N); }
+size_t merge_zlab_off(int64_t N) { return align_up(merge_labc_off(N) + 4 * (size_t)N); }
 size_t merge_bsum_off(int64_t N) { return align_up(merge_zlab_off(N) + 4 * (size_t)N); }
 size_t merge_bytes(int64_t N) {
   return align_up(merge_bsum_off(N) + 32 * (size_t)ceil_div(N > 0 ? N : 1, kCombineTokens));
@@ -246,21 +262,27 @@ flce_status_t zero_fill(void* p, size_t bytes, hipStream_t st) {
   });
 }
 
-// Blocked image of a K-contiguous source (element (r, k) at src[r * ld + k]).
+// Blocked image of a K-contiguous source (element (r, k) at src[r * ld + k]);
+// with `gather`, row r is source row gather[r] for r < *count.
 flce_status_t pack_rows(int kind, const void* src, int64_t R, int64_t K, int64_t ld, int nkb,
-                        uint16_t* dst, hipStream_t st) {
+                        const int32_t* gather, const int32_t* count, uint16_t* dst,
+                        hipStream_t st) {
   const dim3 grid((unsigned)ceil_div(nkb, 8), (unsigned)ceil_div(R, kTile));
   return launch(kind, st, [&] {
-    pack_rows_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(src), R, K, ld, nkb, dst);
+    pack_rows_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(src), R, K, ld, nkb,
+                                           gather, count, dst);
   });
 }
 
-// Blocked image of a row-contiguous source (element (r, k) at src[k * ld + r]).
+// Blocked image of a row-contiguous source (element (r, k) at src[k * ld + r]);
+// with `gather`, K index k reads source row gather[k] for k < *count.
 flce_status_t pack_cols(int kind, const void* src, int64_t R, int64_t K, int64_t ld, int nkb,
-                        uint16_t* dst, hipStream_t st) {
+                        const int32_t* gather, const int32_t* count, uint16_t* dst,
+                        hipStream_t st) {
   const dim3 grid((unsigned)ceil_div(nkb, 2), (unsigned)ceil_div(R, kTile));
   return launch(kind, st, [&] {
-    pack_cols_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(src), R, K, ld, nkb, dst);
+    pack_cols_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(src), R, K, ld, nkb,
+                                           gather, count, dst);
   });
 }
 
@@ -320,23 +342,42 @@ flce_status_t forward_impl(const void* hidden, const void* weight, const int64_t
   const float softcap = o.softcap;
 
   int32_t* header = reinterpret_cast<int32_t*>(workspace);
-  int32_t* lab32 = reinterpret_cast<int32_t*>(wsp(workspace, p.f_lab));
+  const int32_t* nvalid = header + 1;
+  int32_t* idx = reinterpret_cast<int32_t*>(wsp(workspace, p.f_idx));
+  int32_t* labc = reinterpret_cast<int32_t*>(wsp(workspace, p.f_labc));
   float4* part = reinterpret_cast<float4*>(wsp(workspace, p.f_part));
-  float* zlab = shard ? label_logit : reinterpret_cast<float*>(wsp(workspace, p.f_zlab));
+  float* zlab = reinterpret_cast<float*>(wsp(workspace, p.f_zlab));
   double4* bsum = reduce ? reinterpret_cast<double4*>(wsp(workspace, p.f_bsum)) : nullptr;
 
-  FLCE_TRY(launch(K_FWD_PREP, st, [&] {
-    fwd_prep_kernel<<<1, 1024, 0, st>>>(labels, N, V_total, v_begin, V, o.ignore_index, lab32,
-                                        zlab, header);
-  }));
+  FwdPrepArgs pr{};
+  pr.labels = labels;
+  pr.N = N;
+  pr.V_total = V_total;
+  pr.v_begin = v_begin;
+  pr.Vs = V;
+  pr.ignore_index = o.ignore_index;
+  pr.idx = idx;
+  pr.labc = labc;
+  pr.zlab = zlab;
+  pr.lse = lse;
+  pr.logprob = logprob;
+  pr.entropy = entropy;
+  pr.uniform_ce = uniform_ce;
+  pr.z_loss = z_loss;
+  pr.state_out = state_out;
+  pr.label_logit = shard ? label_logit : nullptr;
+  pr.header = header;
+  FLCE_TRY(launch(K_FWD_PREP, st, [&] { fwd_prep_kernel<<<1, 1024, 0, st>>>(pr); }));
   const int nb = (int)ceil_div(N, kCombineTokens);
   if (N > 0) {
     uint16_t* xb = reinterpret_cast<uint16_t*>(wsp(workspace, p.f_xb));
-    FLCE_TRY(pack_rows(K_PACK_HIDDEN, hidden, N, H, H, p.hkb, xb, st));
+    // Only the valid tokens, compacted in token order, enter the contractions.
+    FLCE_TRY(pack_rows(K_PACK_HIDDEN, hidden, N, H, H, p.hkb, idx, nvalid, xb, st));
     FwdTileArgs a{};
     a.weight = static_cast<const uint16_t*>(weight);
     a.xb = xb;
-    a.lab = lab32;
+    a.lab = labc;
+    a.nvalid = nvalid;
     a.N = N;
     a.H = H;
     a.V = V;
@@ -360,10 +401,12 @@ flce_status_t forward_impl(const void* hidden, const void* weight, const int64_t
     c.S = p.VT;
     c.zlab = zlab;
     c.nz = 1;
-    c.lab32 = lab32;
+    c.idx = idx;
+    c.nvalid = nvalid;
     c.N = N;
     c.V = V_total;
     c.state_out = state_out;
+    c.label_logit = label_logit;
     c.zl_scale = o.z_loss_scale;
     c.lse = lse;
     c.logprob = logprob;
@@ -412,7 +455,9 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
   if (N == 0) return zero_fill(grad_weight, out_elem * (size_t)H * (size_t)V, st);
 
   int32_t* header = reinterpret_cast<int32_t*>(workspace);
+  const int32_t* nvalid = header + 1;
   int32_t* lab32 = reinterpret_cast<int32_t*>(wsp(workspace, p.b_lab));
+  int32_t* idx = reinterpret_cast<int32_t*>(wsp(workspace, p.b_idx));
   DzToken* coef = reinterpret_cast<DzToken*>(wsp(workspace, p.b_coef));
   uint16_t* wb = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_wb));
   uint16_t* xb = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_xb));
@@ -439,14 +484,23 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
   pa.gzl = grad_z_loss;
   pa.coef = coef;
   pa.lab32 = lab32;
+  pa.idx = idx;
   pa.header = header;
   FLCE_TRY(launch(K_BWD_PREP, st, [&] { bwd_prep_kernel<<<1, 1024, 0, st>>>(pa); }));
+  // Rows of ignored tokens are never written by the compacted contractions.
+  const int zb = (int)(N < 16384 ? N : 16384);
+  FLCE_TRY(launch(K_FILL, st, [&] {
+    zero_ignored_rows_kernel<<<zb, 256, 0, st>>>(labels, N, V_total, o.ignore_index,
+                                                 static_cast<char*>(grad_hidden),
+                                                 (int64_t)out_elem * H);
+  }));
 
-  // Blocked operands: hidden (tokens x H) for the recompute, hidden^T
-  // (H x tokens) for dW, and per chunk the weight (H x vocabulary) for dH.
-  // The recompute reads the weight (vocabulary x H) row-contiguous.
-  FLCE_TRY(pack_rows(K_PACK_HIDDEN, hidden, N, H, H, p.hkb, xb, st));
-  FLCE_TRY(pack_cols(K_PACK_HIDDEN, hidden, H, N, H, p.nkb, xtb, st));
+  // Blocked operands, over the valid tokens compacted in token order: hidden
+  // (tokens x H) for the recompute, hidden^T (H x tokens) for dW, and per
+  // chunk the weight (H x vocabulary) for dH. The recompute reads the weight
+  // (vocabulary x H) row-contiguous.
+  FLCE_TRY(pack_rows(K_PACK_HIDDEN, hidden, N, H, H, p.hkb, idx, nvalid, xb, st));
+  FLCE_TRY(pack_cols(K_PACK_HIDDEN, hidden, H, N, H, p.nkb, idx, nvalid, xtb, st));
   const float softcap = o.softcap;
   const bool capped = softcap > 0.f;
   for (int c = 0; c < p.nchunks; ++c) {
@@ -454,13 +508,14 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
     const int64_t vc = V - v0 < p.Vc ? V - v0 : p.Vc;
     const int vtc = (int)ceil_div(vc, kTile);
     const uint16_t* wchunk = static_cast<const uint16_t*>(weight) + v0;
-    FLCE_TRY(pack_rows(K_PACK_WEIGHT, wchunk, H, vc, V, p.kbv, wb, st));
+    FLCE_TRY(pack_rows(K_PACK_WEIGHT, wchunk, H, vc, V, p.kbv, nullptr, nullptr, wb, st));
 
     DlogitsArgs d{};
     d.weight = static_cast<const uint16_t*>(weight);
     d.xb = xb;
     d.coef = coef;
     d.lab = lab32;
+    d.nvalid = nvalid;
     d.N = N;
     d.H = H;
     d.V = V;
@@ -496,6 +551,8 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
     x.group = p.group;
     x.acc = acc;
     x.gh = grad_hidden;
+    x.idx = idx;
+    x.nvalid = nvalid;
     const int mode =
         p.nchunks == 1 ? DX_ONLY : (c == 0 ? DX_FIRST : (c == p.nchunks - 1 ? DX_LAST : DX_MID));
     const int gx = p.TB * p.HT;
@@ -526,6 +583,7 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
     w.v0 = v0;
     w.vc = vc;
     w.kbn = p.nkb;
+    w.nvalid = nvalid;
     w.ldp = p.Vc;
     w.HT = p.HT;
     w.VTc = vtc;
@@ -673,13 +731,21 @@ flce_status_t flce_merge_shards(const float* states, const float* label_logits, 
   if (workspace_bytes < merge_bytes(N)) return FLCE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* header = reinterpret_cast<int32_t*>(workspace);
-  int32_t* lab32 = reinterpret_cast<int32_t*>(wsp(workspace, kHeaderBytes));
-  float* zlab = reinterpret_cast<float*>(wsp(workspace, merge_zlab_off(N)));
   double4* bsum = reduce ? reinterpret_cast<double4*>(wsp(workspace, merge_bsum_off(N))) : nullptr;
-  FLCE_TRY(launch(K_FWD_PREP, st, [&] {
-    fwd_prep_kernel<<<1, 1024, 0, st>>>(labels, N, V_total, 0, V_total, opt->ignore_index, lab32,
-                                        zlab, header);
-  }));
+  // The prep kernel counts the valid tokens for the mean (its compaction is
+  // unused here: the slice states are indexed by token).
+  FwdPrepArgs pr{};
+  pr.labels = labels;
+  pr.N = N;
+  pr.V_total = V_total;
+  pr.v_begin = 0;
+  pr.Vs = V_total;
+  pr.ignore_index = opt->ignore_index;
+  pr.idx = reinterpret_cast<int32_t*>(wsp(workspace, merge_idx_off(N)));
+  pr.labc = reinterpret_cast<int32_t*>(wsp(workspace, merge_labc_off(N)));
+  pr.zlab = reinterpret_cast<float*>(wsp(workspace, merge_zlab_off(N)));
+  pr.header = header;
+  FLCE_TRY(launch(K_FWD_PREP, st, [&] { fwd_prep_kernel<<<1, 1024, 0, st>>>(pr); }));
   const int nb = (int)ceil_div(N, kCombineTokens);
   if (N > 0) {
     CombineArgs c{};
@@ -687,7 +753,9 @@ flce_status_t flce_merge_shards(const float* states, const float* label_logits, 
     c.S = (int)S;
     c.zlab = label_logits;
     c.nz = (int)S;
-    c.lab32 = lab32;
+    c.idx = nullptr;
+    c.labels = labels;
+    c.ignore_index = opt->ignore_index;
     c.N = N;
     c.V = V_total;
     c.zl_scale = opt->z_loss_scale;

@@ -44,43 +44,95 @@ __device__ __forceinline__ T block_sum(T v, T* sh) {
 
 // ---- forward: labels -> int32, counts ---------------------------------------
 
-// One block of 1024 threads. The vocabulary slice handled by this call is
-// [v_begin, v_begin + Vs) of V_total classes (the whole vocabulary unless
-// the head is sharded). lab32[t] = y - v_begin for a valid label inside the
-// slice, kLabelElsewhere for a valid label outside it, -1 for an ignored or
-// out-of-range label. zlab[t] = 0 (the logit tiles overwrite it where the
-// label lies in the slice). header[0] = #labels neither ignore_index nor in
-// [0, V_total); header[1] = #valid tokens.
-constexpr int32_t kLabelElsewhere = -2;
-
-__global__ void __launch_bounds__(1024) fwd_prep_kernel(const int64_t* __restrict__ labels,
-                                                        int64_t N, int64_t V_total,
-                                                        int64_t v_begin, int64_t Vs,
-                                                        int64_t ignore_index,
-                                                        int32_t* __restrict__ lab32,
-                                                        float* __restrict__ zlab,
-                                                        int32_t* __restrict__ header) {
-  __shared__ int sh[1024];
-  int inv = 0, nv = 0;
-  for (int64_t t = threadIdx.x; t < N; t += 1024) {
-    const int64_t y = labels[t];
-    int32_t o = -1;
-    if (y != ignore_index) {
-      if (y >= 0 && y < V_total) {
-        o = (y >= v_begin && y < v_begin + Vs) ? (int32_t)(y - v_begin) : kLabelElsewhere;
-        ++nv;
-      } else {
-        ++inv;
-      }
-    }
-    lab32[t] = o;
-    zlab[t] = 0.f;
+// Order-preserving compaction step inside one block of 1024 threads (16
+// waves): every thread passes its flag for the current chunk of 1024 items;
+// returns the rank of the thread's item among the flagged items of the chunk
+// (meaningful when flagged) and sets `total` to the chunk's flagged count.
+// Wave ballots and a fixed-order sum of the 16 wave counts: deterministic.
+__device__ __forceinline__ int chunk_rank(bool flag, int* sh, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t b = __builtin_amdgcn_ballot_w64(flag);
+  const int pre = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+  if (lane == 0) sh[w] = __popcll(b);
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int c = sh[k];
+    off += k < w ? c : 0;
+    tot += c;
   }
+  __syncthreads();  // sh is reused by the next chunk
+  total = tot;
+  return off + pre;
+}
+
+// Label code of one token: -1 when ignored or outside [0, V_total) (an
+// invalid label), y - v_begin when inside the slice [v_begin, v_begin + Vs),
+// kLabelElsewhere when valid but outside the slice.
+constexpr int32_t kLabelElsewhere = -2;
+__device__ __forceinline__ int32_t label_code(int64_t y, int64_t ignore_index, int64_t V_total,
+                                              int64_t v_begin, int64_t Vs, bool& invalid) {
+  invalid = false;
+  if (y == ignore_index) return -1;
+  if (y < 0 || y >= V_total) {
+    invalid = true;
+    return -1;
+  }
+  return (y >= v_begin && y < v_begin + Vs) ? (int32_t)(y - v_begin) : kLabelElsewhere;
+}
+
+struct FwdPrepArgs {
+  const int64_t* labels;
+  int64_t N, V_total, v_begin, Vs, ignore_index;  // the slice of this call (whole vocabulary unsharded)
+  int32_t* idx;            // [N] compacted: original index of the r-th valid token
+  int32_t* labc;           // [N] compacted label codes; -1 past the valid tokens
+  float* zlab;             // [N] compacted label logits, zeroed here
+  float *lse, *logprob, *entropy, *uniform_ce, *z_loss;  // zeroed at ignored tokens (may be null)
+  float4* state_out;       // slice mode: the empty state at ignored tokens
+  float* label_logit;      // slice mode: zeroed for every token
+  int32_t* header;         // [0] invalid labels, [1] valid tokens n
+};
+
+// One block of 1024 threads: compacts the valid tokens (in token order) and
+// writes the per-token outputs of ignored tokens, which no later kernel
+// touches.
+__global__ void __launch_bounds__(1024) fwd_prep_kernel(FwdPrepArgs a) {
+  __shared__ int sh[1024];
+  int inv = 0, base = 0;
+  for (int64_t c0 = 0; c0 < a.N; c0 += 1024) {
+    const int64_t t = c0 + threadIdx.x;
+    bool bad = false;
+    const int32_t code = t < a.N ? label_code(a.labels[t], a.ignore_index, a.V_total, a.v_begin,
+                                              a.Vs, bad)
+                                 : -1;
+    inv += bad ? 1 : 0;
+    const bool valid = code != -1;
+    int total;
+    const int r = base + chunk_rank(valid, sh, total);
+    if (valid) {
+      a.idx[r] = (int32_t)t;
+      a.labc[r] = code;
+    } else if (t < a.N) {
+      if (a.lse) a.lse[t] = 0.f;
+      if (a.logprob) a.logprob[t] = 0.f;
+      if (a.entropy) a.entropy[t] = 0.f;
+      if (a.uniform_ce) a.uniform_ce[t] = 0.f;
+      if (a.z_loss) a.z_loss[t] = 0.f;
+      if (a.state_out) a.state_out[t] = make_float4(kNegBig, 0.f, 0.f, 0.f);
+    }
+    if (t < a.N) {
+      a.zlab[t] = 0.f;
+      if (a.label_logit) a.label_logit[t] = 0.f;
+    }
+    base += total;
+  }
+  for (int64_t r = base + threadIdx.x; r < a.N; r += 1024) a.labc[r] = -1;
   inv = block_sum<int, 1024>(inv, sh);
-  nv = block_sum<int, 1024>(nv, sh);
   if (threadIdx.x == 0) {
-    header[0] = inv;
-    header[1] = nv;
+    a.header[0] = inv;
+    a.header[1] = base;
   }
 }
 
@@ -89,15 +141,20 @@ __global__ void __launch_bounds__(1024) fwd_prep_kernel(const int64_t* __restric
 // Operand (R rows, K values per row) whose source is K-contiguous:
 // element (r, k) at src[r * ld + k]. Writes the blocked image `dst` of
 // ceil(R/256) strips x nkb K blocks; rows >= R and K values >= K are zero.
-// A workgroup fills 8 consecutive K blocks of one strip; consecutive threads
-// read consecutive 16-byte pieces of one source row (512 bytes per row).
-// K must be a multiple of 8 and ld a multiple of 8.
+// With `gather`, operand row r is source row gather[r] for r < *count and
+// zero beyond (the compacted valid tokens). A workgroup fills 8 consecutive K
+// blocks of one strip; consecutive threads read consecutive 16-byte pieces of
+// one source row (512 bytes per row). K must be a multiple of 8 and ld a
+// multiple of 8.
 __global__ void __launch_bounds__(256) pack_rows_kernel(const uint16_t* __restrict__ src,
                                                         int64_t R, int64_t K, int64_t ld, int nkb,
+                                                        const int32_t* __restrict__ gather,
+                                                        const int32_t* __restrict__ count,
                                                         uint16_t* __restrict__ dst) {
   const int64_t strip = blockIdx.y;
   const int kb0 = blockIdx.x * 8;
   const int t = threadIdx.x;
+  const int64_t rows = gather != nullptr ? *count : R;
 #pragma unroll 4
   for (int p = 0; p < 32; ++p) {
     const int i = p * 256 + t;
@@ -107,7 +164,10 @@ __global__ void __launch_bounds__(256) pack_rows_kernel(const uint16_t* __restri
     const int64_t row = strip * kTile + r;
     const int64_t k = (int64_t)kb * kBK + c * 8;
     u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-    if (row < R && k < K) v = *reinterpret_cast<const u32x4_t*>(src + row * ld + k);
+    if (row < rows && k < K) {
+      const int64_t srow = gather != nullptr ? gather[row] : row;
+      v = *reinterpret_cast<const u32x4_t*>(src + srow * ld + k);
+    }
     char* blk = reinterpret_cast<char*>(dst) + (strip * nkb + kb) * (int64_t)kBlockBytes;
     *reinterpret_cast<u32x4_t*>(blk + blk_byte(r, c * 8)) = v;
   }
@@ -115,16 +175,21 @@ __global__ void __launch_bounds__(256) pack_rows_kernel(const uint16_t* __restri
 
 // Operand (R rows, K values per row) whose source is row-contiguous:
 // element (r, k) at src[k * ld + r] (a transposing pack). Writes the blocked
-// image `dst` of ceil(R/256) strips x nkb K blocks, zero past R and K. A
-// workgroup fills K blocks (2 bx, 2 bx + 1) of one strip: thread (g, q) reads
-// rows r = 8g .. 8g+7 of the 8 source rows k = 8q .. 8q+7 (16 bytes each;
-// 32 consecutive threads read 512 contiguous bytes), transposes the 8 x 8
-// piece in registers and writes eight 16-byte chunks. R must be a multiple of
-// 8 and ld a multiple of 8.
+// image `dst` of ceil(R/256) strips x nkb K blocks, zero past R and K. With
+// `gather`, K index k reads source row gather[k] for k < *count and zero
+// beyond (the compacted valid tokens). A workgroup fills K blocks
+// (2 bx, 2 bx + 1) of one strip: thread (g, q) reads rows r = 8g .. 8g+7 of
+// the 8 source rows k = 8q .. 8q+7 (16 bytes each; 32 consecutive threads
+// read 512 contiguous bytes), transposes the 8 x 8 piece in registers and
+// writes eight 16-byte chunks. R must be a multiple of 8 and ld a multiple of
+// 8.
 __global__ void __launch_bounds__(256) pack_cols_kernel(const uint16_t* __restrict__ src,
                                                         int64_t R, int64_t K, int64_t ld, int nkb,
+                                                        const int32_t* __restrict__ gather,
+                                                        const int32_t* __restrict__ count,
                                                         uint16_t* __restrict__ dst) {
   const int64_t strip = blockIdx.y;
+  const int64_t kval = gather != nullptr ? *count : K;
   const int t = threadIdx.x;
   const int g = t & 31, q = t >> 5;                 // row group, K chunk (0..7)
   const int kb = blockIdx.x * 2 + (q >> 2);
@@ -136,7 +201,10 @@ __global__ void __launch_bounds__(256) pack_cols_kernel(const uint16_t* __restri
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     in[e] = u32x4_t{0u, 0u, 0u, 0u};
-    if (r0 < R && k0 + e < K) in[e] = *reinterpret_cast<const u32x4_t*>(src + (k0 + e) * ld + r0);
+    if (r0 < R && k0 + e < kval) {
+      const int64_t srow = gather != nullptr ? gather[k0 + e] : k0 + e;
+      in[e] = *reinterpret_cast<const u32x4_t*>(src + srow * ld + r0);
+    }
   }
   char* blk = reinterpret_cast<char*>(dst) + (strip * nkb + kb) * (int64_t)kBlockBytes;
 #pragma unroll
@@ -157,14 +225,15 @@ __global__ void __launch_bounds__(256) pack_cols_kernel(const uint16_t* __restri
 struct FwdTileArgs {
   const uint16_t* weight;  // [H,V]
   const uint16_t* xb;      // blocked hidden: strips of 256 tokens, K = H
-  const int32_t* lab;      // [N], -1 = no label
+  const int32_t* lab;      // [N] compacted label codes (label logit captured when >= 0)
+  const int32_t* nvalid;   // device: number n of compacted tokens
   int64_t N, H, V;
   int hkb;                 // K blocks per strip, ceil(H / 32)
   int VT, TB;              // vocabulary tiles, token blocks
   int group;               // token blocks per XCD patch (see group_map)
   float cap, cap_k;        // softcap c and 2*log2(e)/c
-  float4* part;            // [VT][N] {m, s, u, sum z'} per vocabulary tile
-  float* zlab;             // [N] capped logit of the label
+  float4* part;            // [VT][N] {m, s, u, sum z'} per vocabulary tile (compacted tokens)
+  float* zlab;             // [N] capped logit of the label (compacted tokens)
 };
 
 // Merge state (m2, s2, u2) into (m, s, u); u in base-2 units (times log2 e).
@@ -254,6 +323,7 @@ fwd_tile_kernel(FwdTileArgs a) {
   const int lane = threadIdx.x & 63, lh = lane >> 5;
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t n0 = (int64_t)tb * kTile;
+  if (n0 >= *a.nvalid) return;  // token tile past the compacted tokens
 
   Acc acc;
   {
@@ -347,24 +417,39 @@ struct CombineArgs {
   int S;                   // vocabulary tiles (or slices)
   const float* zlab;       // [nz][N] label logits, summed (one of them holds each label)
   int nz;
-  const int32_t* lab32;    // -1: ignored token
+  // Compacted (idx set): entry r < *nvalid belongs to token idx[r]. Direct
+  // (idx null): entry t is token t, valid when labels[t] is.
+  const int32_t* idx;
+  const int32_t* nvalid;
+  const int64_t* labels;   // direct mode
+  int64_t ignore_index;
   int64_t N, V;            // V: the whole vocabulary
   float zl_scale;          // lam
   float *lse, *logprob, *entropy;
   float *uniform_ce, *z_loss;  // optional
   double4* bsum;               // optional: {logprob, entropy, uniform_ce, z_loss} per block
   float4* state_out;           // if set: write the merged state {m, s, u, sum z'} instead
+  float* label_logit;          // with state_out: the label logit per token
 };
 
 __global__ void __launch_bounds__(1024) fwd_combine_kernel(CombineArgs a) {
   __shared__ float4 st[kCombineWaves][kCombineTokens];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t t = (int64_t)blockIdx.x * kCombineTokens + lane;
-  const bool valid = t < a.N && a.lab32[t] != -1;
+  const int64_t r = (int64_t)blockIdx.x * kCombineTokens + lane;  // entry
+  bool valid;
+  int64_t t;  // token
+  if (a.idx != nullptr) {
+    valid = r < *a.nvalid;
+    t = valid ? a.idx[r] : -1;
+  } else {
+    bool bad;
+    valid = r < a.N && label_code(a.labels[r], a.ignore_index, a.V, 0, a.V, bad) != -1;
+    t = r;
+  }
   float m = kNegBig, s = 0.f, u = 0.f, zs = 0.f;
   if (valid)
     for (int k = w; k < a.S; k += kCombineWaves) {
-      const float4 q = a.part[(int64_t)k * a.N + t];
+      const float4 q = a.part[(int64_t)k * a.N + r];
       merge_state(m, s, u, q.x, q.y, q.z);
       zs += q.w;
     }
@@ -378,7 +463,11 @@ __global__ void __launch_bounds__(1024) fwd_combine_kernel(CombineArgs a) {
     zs += q.w;
   }
   if (a.state_out != nullptr) {
-    if (t < a.N) a.state_out[t] = valid ? make_float4(m, s, u, zs) : make_float4(kNegBig, 0.f, 0.f, 0.f);
+    // Ignored tokens got the empty state from the prep kernel.
+    if (valid) {
+      a.state_out[t] = make_float4(m, s, u, zs);
+      a.label_logit[t] = a.zlab[r];
+    }
     return;
   }
   double r0 = 0.0, r1 = 0.0, r2 = 0.0, r3 = 0.0;
@@ -387,7 +476,7 @@ __global__ void __launch_bounds__(1024) fwd_combine_kernel(CombineArgs a) {
     const float l = m + ls;
     const float e = ls - u / s;
     float zy = 0.f;
-    for (int k = 0; k < a.nz; ++k) zy += a.zlab[(int64_t)k * a.N + t];
+    for (int k = 0; k < a.nz; ++k) zy += a.zlab[(int64_t)k * a.N + r];
     const float lp = zy - l;
     const float uc = l - zs / (float)a.V;
     const float zl = a.zl_scale * l * l;
@@ -400,12 +489,12 @@ __global__ void __launch_bounds__(1024) fwd_combine_kernel(CombineArgs a) {
     r1 = e;
     r2 = uc;
     r3 = zl;
-  } else if (t < a.N) {
-    a.lse[t] = 0.f;
-    a.entropy[t] = 0.f;
-    a.logprob[t] = 0.f;
-    if (a.uniform_ce) a.uniform_ce[t] = 0.f;
-    if (a.z_loss) a.z_loss[t] = 0.f;
+  } else if (a.idx == nullptr && r < a.N) {
+    a.lse[r] = 0.f;
+    a.entropy[r] = 0.f;
+    a.logprob[r] = 0.f;
+    if (a.uniform_ce) a.uniform_ce[r] = 0.f;
+    if (a.z_loss) a.z_loss[r] = 0.f;
   }
   if (a.bsum != nullptr) {
 #pragma unroll
@@ -467,6 +556,7 @@ struct PrepArgs {
   const int64_t* labels;
   int64_t N, V, ignore_index;  // V: the whole vocabulary
   int64_t v_begin, Vs;         // vocabulary slice of this call
+  int32_t* idx;                // [N] compacted: original index of the r-th valid token
   int reduction;               // 0 none, 1 mean, 2 sum
   float zl_scale;              // lam
   const float *lse, *entropy;
@@ -476,18 +566,18 @@ struct PrepArgs {
   int32_t* header;
 };
 
-// One block of 1024: counts, per-token coefficients and int32 labels
-// (relative to the slice; -1 when the label is ignored or outside the slice,
-// which drops the label term but keeps the token's other terms).
+// One block of 1024: compacts the valid tokens (in token order) and writes
+// their coefficients and label offsets in compacted order; entries past the
+// valid tokens get the ignored-token values. Label offsets are relative to
+// the slice; -1 when the label lies outside it, which drops the label term
+// but keeps the token's other terms.
 __global__ void __launch_bounds__(1024) bwd_prep_kernel(PrepArgs a) {
   __shared__ int sh[1024];
   int inv = 0, nv = 0;
   for (int64_t t = threadIdx.x; t < a.N; t += 1024) {
-    const int64_t y = a.labels[t];
-    if (y != a.ignore_index) {
-      if (y >= 0 && y < a.V) ++nv;
-      else ++inv;
-    }
+    bool bad;
+    if (label_code(a.labels[t], a.ignore_index, a.V, a.v_begin, a.Vs, bad) != -1) ++nv;
+    inv += bad ? 1 : 0;
   }
   inv = block_sum<int, 1024>(inv, sh);
   nv = block_sum<int, 1024>(nv, sh);
@@ -498,29 +588,57 @@ __global__ void __launch_bounds__(1024) bwd_prep_kernel(PrepArgs a) {
   auto scal = [&](const float* g) { return (scalar && g != nullptr) ? g[0] * div : 0.f; };
   const float g0 = scal(a.glp), e0 = scal(a.gent), u0 = scal(a.guce), z0 = scal(a.gzl);
   const float invV = 1.f / (float)a.V;
-  for (int64_t t = threadIdx.x; t < a.N; t += 1024) {
-    const int64_t y = a.labels[t];
-    DzToken c{1e30f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int32_t lab = -1;
-    if (y != a.ignore_index && y >= 0 && y < a.V) {
+  int base = 0;
+  for (int64_t c0 = 0; c0 < a.N; c0 += 1024) {
+    const int64_t t = c0 + threadIdx.x;
+    bool bad;
+    const int32_t code =
+        t < a.N ? label_code(a.labels[t], a.ignore_index, a.V, a.v_begin, a.Vs, bad) : -1;
+    const bool valid = code != -1;
+    int total;
+    const int r = base + chunk_rank(valid, sh, total);
+    if (valid) {
       auto per = [&](const float* g, float s0) { return scalar ? s0 : (g != nullptr ? g[t] : 0.f); };
-      const bool here = y >= a.v_begin && y < a.v_begin + a.Vs;
       const float g = per(a.glp, g0), e = per(a.gent, e0), u = per(a.guce, u0), z = per(a.gzl, z0);
       const float l = a.lse[t];
       const float S = l - a.entropy[t];
+      DzToken c;
       c.lse = l;
       c.ebar = e;
       c.cs = g - e * S - u - 2.f * a.zl_scale * z * l;
-      c.gbar = here ? g : 0.f;
+      c.gbar = code >= 0 ? g : 0.f;
       c.k0 = -u * invV;
-      lab = here ? (int32_t)(y - a.v_begin) : -1;
+      c.pad0 = c.pad1 = c.pad2 = 0.f;
+      a.coef[r] = c;
+      a.lab32[r] = code >= 0 ? code : -1;
+      a.idx[r] = (int32_t)t;
     }
-    a.coef[t] = c;
-    a.lab32[t] = lab;
+    base += total;
+  }
+  for (int64_t r = base + threadIdx.x; r < a.N; r += 1024) {
+    a.coef[r] = DzToken{1e30f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    a.lab32[r] = -1;
   }
   if (threadIdx.x == 0) {
     a.header[0] = inv;
     a.header[1] = nv;
+  }
+}
+
+// Zeroes the rows of `out` ([N, row_bytes]) whose token is ignored or has an
+// invalid label: the compacted contractions never write them. One block per
+// token (grid-stride), 16-byte stores; row_bytes is a multiple of 16.
+__global__ void __launch_bounds__(256) zero_ignored_rows_kernel(const int64_t* __restrict__ labels,
+                                                                int64_t N, int64_t V,
+                                                                int64_t ignore_index,
+                                                                char* __restrict__ out,
+                                                                int64_t row_bytes) {
+  for (int64_t t = blockIdx.x; t < N; t += gridDim.x) {
+    bool bad;
+    if (label_code(labels[t], ignore_index, V, 0, V, bad) != -1) continue;
+    char* row = out + t * row_bytes;
+    for (int64_t o = (int64_t)threadIdx.x * 16; o < row_bytes; o += 256 * 16)
+      *reinterpret_cast<u32x4_t*>(row + o) = u32x4_t{0u, 0u, 0u, 0u};
   }
 }
 
@@ -529,8 +647,9 @@ __global__ void __launch_bounds__(1024) bwd_prep_kernel(PrepArgs a) {
 struct DlogitsArgs {
   const uint16_t* weight;  // [H,V]
   const uint16_t* xb;      // blocked hidden
-  const DzToken* coef;     // [N]
-  const int32_t* lab;      // [N]
+  const DzToken* coef;     // [N] compacted tokens
+  const int32_t* lab;      // [N] compacted label offsets in the slice (-1: none)
+  const int32_t* nvalid;   // device: number of compacted tokens
   int64_t N, H, V;
   int hkb;                 // K blocks of the hidden strips
   int64_t v0;              // first vocabulary column of this chunk (multiple of 256)
@@ -617,6 +736,7 @@ bwd_dlogits_kernel(DlogitsArgs a) {
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t n0 = (int64_t)tb * kTile;
   const int64_t vg0 = a.v0 + (int64_t)vt * kTile;  // first vocabulary column of the tile
+  if (n0 >= *a.nvalid) return;  // token tile past the compacted tokens
 
   Acc acc;
   {
@@ -696,8 +816,10 @@ struct DxArgs {
   int nk;                  // K blocks of the chunk
   int TB, HT;              // token blocks, hidden tiles
   int group;
-  float* acc;              // [N,H] fp32 accumulator over chunks
-  void* gh;                // [N,H] output, bf16 or fp32 (F32OUT)
+  float* acc;              // [N,H] fp32 accumulator over chunks (compacted rows)
+  void* gh;                // [N,H] output, bf16 or fp32 (F32OUT); row idx[r] of compacted row r
+  const int32_t* idx;      // [N] compacted -> original token
+  const int32_t* nvalid;   // device: number of compacted tokens
 };
 
 // C[t][h] = sum_v D[t][v] W[h][v0 + v] over the chunk. MODE: DX_ONLY (single chunk: write
@@ -714,6 +836,8 @@ bwd_dx_kernel(DxArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t m0 = (int64_t)tb * kTile, h0 = (int64_t)ht * kTile;
+  const int nval = *a.nvalid;
+  if (m0 >= nval) return;  // token tile past the compacted tokens
   Acc acc;
   {
     Mainloop ml;
@@ -722,14 +846,14 @@ bwd_dx_kernel(DxArgs a) {
   }
   const int64_t base = m0 * a.H + h0;
   const int64_t span = (a.N - m0) * a.H - h0;  // elements from the tile origin to the end
-  constexpr int kOut = F32OUT ? 4 : 2;  // bytes per output element
-  const __amdgpu_buffer_rsrc_t rg =
-      make_rsrc(static_cast<char*>(a.gh) + base * kOut, span * kOut);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.acc + base, span * 4);
+  constexpr int kOut = F32OUT ? 4 : 2;  // bytes per output element
+  char* const gh = static_cast<char*>(a.gh);
   // Per 4 accumulator rows of a 32 x 32 block, a quad transpose hands lane
   // 4q+a row (first + a) at the quad's four columns: 16-byte fp32 and 8-byte
   // bf16 accesses. H is a multiple of 4, so a quad's columns are all inside or
-  // all outside.
+  // all outside. Output rows go to their original token (idx); compacted rows
+  // past the valid tokens are not written.
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int hq = acc_col(wn, j, lane) & ~3;
@@ -740,24 +864,28 @@ bwd_dx_kernel(DxArgs a) {
       for (int rq = 0; rq < 4; ++rq) {
         const int row = acc_row(wm, i, rq * 4, lane) + (lane & 3);
         const uint32_t e = (uint32_t)(row * a.H + hq);
+        const bool out_ok = hok && m0 + row < nval;
+        char* dst = out_ok ? gh + ((int64_t)a.idx[m0 + row] * a.H + h0 + hq) * kOut : nullptr;
         const float x[4] = {acc[i][j][rq * 4], acc[i][j][rq * 4 + 1], acc[i][j][rq * 4 + 2],
                             acc[i][j][rq * 4 + 3]};
         if constexpr (MODE == DX_ONLY && !F32OUT) {
           const u32x2_t v = quad_transpose_bf16(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
-          buf_store_u32x2(v, rg, hok ? e * 2 : kOOB);
+          if (out_ok) *reinterpret_cast<u32x2_t*>(dst) = v;
         } else if constexpr (MODE == DX_ONLY) {
-          buf_store_f32x4(quad_transpose_f32(x[0], x[1], x[2], x[3]), rg, hok ? e * 4 : kOOB);
+          const f32x4_t v = quad_transpose_f32(x[0], x[1], x[2], x[3]);
+          if (out_ok) *reinterpret_cast<f32x4_t*>(dst) = v;
         } else {
           f32x4_t v = quad_transpose_f32(x[0], x[1], x[2], x[3]);
           const uint32_t o = hok ? e * 4 : kOOB;
           if constexpr (MODE != DX_FIRST) v += buf_load_f32x4(ra, o);
-          if constexpr (MODE == DX_LAST && F32OUT)
-            buf_store_f32x4(v, rg, o);
-          else if constexpr (MODE == DX_LAST)
-            buf_store_u32x2(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rg,
-                            hok ? e * 2 : kOOB);
-          else
+          if constexpr (MODE == DX_LAST && F32OUT) {
+            if (out_ok) *reinterpret_cast<f32x4_t*>(dst) = v;
+          } else if constexpr (MODE == DX_LAST) {
+            const u32x2_t b = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            if (out_ok) *reinterpret_cast<u32x2_t*>(dst) = b;
+          } else {
             buf_store_f32x4(v, ra, o);
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);  // one 32 x 32 block at a time
@@ -772,6 +900,7 @@ struct DwArgs {
   const uint16_t* dvt;     // blocked D^T of the chunk (strips of 256 vocabulary rows, K = tokens)
   int64_t N, H, V, v0, vc;
   int kbn;                 // K blocks per strip of both (token blocks * 8)
+  const int32_t* nvalid;   // device: number of compacted tokens (the K extent)
   int HT, VTc, splits;
   int group;
   int kper;                // K blocks per split
@@ -795,7 +924,9 @@ bwd_dw_kernel(DwArgs a) {
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t h0 = (int64_t)ht * kTile, vl0 = (int64_t)vt * kTile;
   const int kbeg = sp * a.kper;
-  const int kend = kbeg + a.kper < a.kbn ? kbeg + a.kper : a.kbn;
+  const int kval = (*a.nvalid + kBK - 1) / kBK;  // K blocks holding compacted tokens
+  const int klim = kval < a.kbn ? kval : a.kbn;
+  const int kend = kbeg + a.kper < klim ? kbeg + a.kper : klim;
   Acc acc;
   {
     Mainloop ml;
