@@ -46,6 +46,7 @@ struct Plan {
   int kbv;             // Vc / 32
   int nchunks;
   int VTc;             // vocabulary tiles per chunk
+  int dx_splits;       // K splits of the dH contraction within a chunk
   int dw_splits;       // split over tokens of the dW contraction
   int dw_kper;         // K blocks per dW split
   int group;           // tile rows per XCD patch of the block -> tile map
@@ -94,6 +95,21 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   p.kbv = (int)(vc / kBK);
   p.nchunks = (int)ceil_div(V, vc);
   p.VTc = (int)(vc / kTile);
+  // dH: split each chunk's K range when the N x H tiles alone fill the GPU
+  // poorly; S minimises ceil(tiles * S / CUs) / S (rounds per unit of work).
+  {
+    const int64_t t = (int64_t)p.TB * p.HT;
+    int best = 1;
+    double bcost = 1e30;
+    for (int sk = 1; sk <= 4; ++sk) {
+      const double cost = (double)ceil_div(t * sk, kNumCUs) / sk;
+      if (cost < bcost - 1e-9) {
+        bcost = cost;
+        best = sk;
+      }
+    }
+    p.dx_splits = best;
+  }
   // dW: split the token reduction when there are too few output tiles.
   const int64_t tiles = (int64_t)p.HT * p.VTc;
   int sp = 1;
@@ -141,7 +157,8 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   p.b_dvt = off;
   off = align_up(off + blk * (size_t)p.VTc * (size_t)p.nkb);
   p.b_acc = off;
-  off = align_up(off + (p.nchunks > 1 ? 4 * (size_t)N * (size_t)H : 0));
+  off = align_up(off + (p.nchunks > 1 || p.dx_splits > 1
+                            ? 4 * (size_t)p.dx_splits * (size_t)N * (size_t)H : 0));
   p.b_part = off;
   off = align_up(off + (p.dw_splits > 1 ? 4 * (size_t)p.dw_splits * (size_t)H * (size_t)p.Vc : 0));
   p.b_total = off;
@@ -178,11 +195,11 @@ constexpr int64_t kMaxVF32 = (int64_t)1 << 21;
 // ---- kernel timing hooks --------------------------------------------------------
 enum Kind {
   K_FWD_PREP, K_FWD_TILE, K_FWD_COMBINE, K_FWD_REDUCE, K_BWD_PREP, K_BWD_DLOGITS, K_BWD_DX,
-  K_BWD_DW, K_DW_REDUCE, K_FILL, K_PACK_WEIGHT, K_PACK_HIDDEN, K_NUM
+  K_BWD_DW, K_DW_REDUCE, K_FILL, K_PACK_WEIGHT, K_PACK_HIDDEN, K_DX_FINALIZE, K_NUM
 };
 const char* kKindNames[K_NUM] = {"fwd_prep", "fwd_tile", "fwd_combine", "fwd_reduce", "bwd_prep",
                                  "bwd_dlogits", "bwd_dx", "bwd_dw", "dw_reduce", "fill_zero",
-                                 "pack_weight", "pack_hidden"};
+                                 "pack_weight", "pack_hidden", "dx_finalize"};
 
 struct Pending {
   int kind;
@@ -553,9 +570,15 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
     x.gh = grad_hidden;
     x.idx = idx;
     x.nvalid = nvalid;
-    const int mode =
-        p.nchunks == 1 ? DX_ONLY : (c == 0 ? DX_FIRST : (c == p.nchunks - 1 ? DX_LAST : DX_MID));
-    const int gx = p.TB * p.HT;
+    x.splits = p.dx_splits;
+    // With K splits every split accumulates (first chunk stores, later ones
+    // add) and dx_finalize writes the output after the last chunk.
+    const bool split = p.dx_splits > 1;
+    const int mode = split ? (c == 0 ? DX_FIRST : DX_MID)
+                           : (p.nchunks == 1 ? DX_ONLY
+                                             : (c == 0 ? DX_FIRST
+                                                       : (c == p.nchunks - 1 ? DX_LAST : DX_MID)));
+    const int gx = p.TB * p.HT * p.dx_splits;
     FLCE_TRY(launch(K_BWD_DX, st, [&] {
       if (f32) {
         switch (mode) {
@@ -573,6 +596,19 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
         }
       }
     }));
+
+    if (split && c == p.nchunks - 1) {
+      const int64_t work = N * (H / 4);
+      const int fb = (int)(ceil_div(work, 256) < 16384 ? ceil_div(work, 256) : 16384);
+      FLCE_TRY(launch(K_DX_FINALIZE, st, [&] {
+        if (f32)
+          dx_finalize_kernel<true><<<fb, 256, 0, st>>>(acc, p.dx_splits, N, H, idx, nvalid,
+                                                       grad_hidden);
+        else
+          dx_finalize_kernel<false><<<fb, 256, 0, st>>>(acc, p.dx_splits, N, H, idx, nvalid,
+                                                        grad_hidden);
+      }));
+    }
 
     DwArgs w{};
     w.xtb = xtb;

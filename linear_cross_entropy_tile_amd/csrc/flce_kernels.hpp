@@ -816,7 +816,8 @@ struct DxArgs {
   int nk;                  // K blocks of the chunk
   int TB, HT;              // token blocks, hidden tiles
   int group;
-  float* acc;              // [N,H] fp32 accumulator over chunks (compacted rows)
+  int splits;              // K splits of the chunk; split s accumulates into acc + s*N*H
+  float* acc;              // [splits][N,H] fp32 accumulators over chunks (compacted rows)
   void* gh;                // [N,H] output, bf16 or fp32 (F32OUT); row idx[r] of compacted row r
   const int32_t* idx;      // [N] compacted -> original token
   const int32_t* nvalid;   // device: number of compacted tokens
@@ -831,21 +832,28 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(2, 2)))
 bwd_dx_kernel(DxArgs a) {
   FLCE_DECLARE_STAGES(sa, sb);
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_split = a.TB * a.HT;
+  const int sp = L / per_split;
   int tb, ht;
-  group_map(xcd_remap(blockIdx.x, gridDim.x), a.TB, a.HT, a.group, tb, ht);
+  group_map(L - sp * per_split, a.TB, a.HT, a.group, tb, ht);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t m0 = (int64_t)tb * kTile, h0 = (int64_t)ht * kTile;
   const int nval = *a.nvalid;
   if (m0 >= nval) return;  // token tile past the compacted tokens
+  // K blocks [kb0, kb1) of the chunk belong to split sp.
+  const int kper = (a.nk + a.splits - 1) / a.splits;
+  const int kb0 = sp * kper;
+  const int kb1 = kb0 + kper < a.nk ? kb0 + kper : a.nk;
   Acc acc;
   {
     Mainloop ml;
-    ml.run(sa, sb, blocked_a(Strip{a.dtv + (int64_t)tb * a.kbv * kBlockElems, a.kbv}, 0),
-           Strip{a.wb + (int64_t)ht * a.kbv * kBlockElems, a.kbv}, 0, a.nk, acc);
+    ml.run(sa, sb, blocked_a(Strip{a.dtv + (int64_t)tb * a.kbv * kBlockElems, a.kbv}, kb0),
+           Strip{a.wb + (int64_t)ht * a.kbv * kBlockElems, a.kbv}, kb0, kb1 - kb0, acc);
   }
-  const int64_t base = m0 * a.H + h0;
-  const int64_t span = (a.N - m0) * a.H - h0;  // elements from the tile origin to the end
+  const int64_t base = (int64_t)sp * a.N * a.H + m0 * a.H + h0;
+  const int64_t span = (a.N - m0) * a.H - h0;  // elements from the tile origin to the split's end
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.acc + base, span * 4);
   constexpr int kOut = F32OUT ? 4 : 2;  // bytes per output element
   char* const gh = static_cast<char*>(a.gh);
@@ -890,6 +898,30 @@ bwd_dx_kernel(DxArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);  // one 32 x 32 block at a time
     }
+  }
+}
+
+// With K-split dH: grad_hidden row idx[r] = sum over splits of acc[s][r],
+// for the compacted rows r < n, in split order; bf16 (RNE) or fp32.
+template <bool F32OUT>
+__global__ void __launch_bounds__(256) dx_finalize_kernel(const float* __restrict__ acc, int splits,
+                                                          int64_t N, int64_t H,
+                                                          const int32_t* __restrict__ idx,
+                                                          const int32_t* __restrict__ nvalid,
+                                                          void* __restrict__ gh) {
+  const int64_t n = *nvalid;
+  const int64_t q = H / 4;  // 4-element groups per row
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n * q; e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / q, c = (e % q) * 4;
+    f32x4_t v = *reinterpret_cast<const f32x4_t*>(acc + r * H + c);
+    for (int s = 1; s < splits; ++s)
+      v += *reinterpret_cast<const f32x4_t*>(acc + (int64_t)s * N * H + r * H + c);
+    const int64_t o = (int64_t)idx[r] * H + c;
+    if constexpr (F32OUT)
+      *reinterpret_cast<f32x4_t*>(static_cast<float*>(gh) + o) = v;
+    else
+      *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(gh) + o) =
+          u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
   }
 }
 
