@@ -318,12 +318,15 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(2, 2)))
 fwd_tile_kernel(FwdTileArgs a) {
   FLCE_DECLARE_STAGES(sa, sb);
+  // Only the token tiles that hold compacted tokens take part; the tile
+  // numbering runs over them alone, so every XCD gets its share.
+  const int tbv = (*a.nvalid + kTile - 1) / kTile;
+  if ((int)blockIdx.x >= tbv * a.VT) return;
   int tb, vt;
-  group_map(xcd_remap(blockIdx.x, gridDim.x), a.TB, a.VT, a.group, tb, vt);
+  group_map(xcd_remap(blockIdx.x, tbv * a.VT), tbv, a.VT, a.group, tb, vt);
   const int lane = threadIdx.x & 63, lh = lane >> 5;
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t n0 = (int64_t)tb * kTile;
-  if (n0 >= *a.nvalid) return;  // token tile past the compacted tokens
 
   Acc acc;
   {
@@ -730,13 +733,15 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(2, 2)))
 bwd_dlogits_kernel(DlogitsArgs a) {
   FLCE_DECLARE_STAGES(sa, sb);
+  // Tiles numbered over the token tiles that hold compacted tokens only.
+  const int tbv = (*a.nvalid + kTile - 1) / kTile;
+  if ((int)blockIdx.x >= tbv * a.VTc) return;
   int tb, vt;
-  group_map(xcd_remap(blockIdx.x, gridDim.x), a.TB, a.VTc, a.group, tb, vt);
+  group_map(xcd_remap(blockIdx.x, tbv * a.VTc), tbv, a.VTc, a.group, tb, vt);
   const int lane = threadIdx.x & 63, lh = lane >> 5;
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t n0 = (int64_t)tb * kTile;
   const int64_t vg0 = a.v0 + (int64_t)vt * kTile;  // first vocabulary column of the tile
-  if (n0 >= *a.nvalid) return;  // token tile past the compacted tokens
 
   Acc acc;
   {
@@ -832,16 +837,18 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(2, 2)))
 bwd_dx_kernel(DxArgs a) {
   FLCE_DECLARE_STAGES(sa, sb);
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int per_split = a.TB * a.HT;
+  // Tiles numbered over the token tiles that hold compacted tokens only.
+  const int nval = *a.nvalid;
+  const int tbv = (nval + kTile - 1) / kTile;
+  const int per_split = tbv * a.HT;
+  if ((int)blockIdx.x >= per_split * a.splits) return;
+  const int L = xcd_remap(blockIdx.x, per_split * a.splits);
   const int sp = L / per_split;
   int tb, ht;
-  group_map(L - sp * per_split, a.TB, a.HT, a.group, tb, ht);
+  group_map(L - sp * per_split, tbv, a.HT, a.group, tb, ht);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t m0 = (int64_t)tb * kTile, h0 = (int64_t)ht * kTile;
-  const int nval = *a.nvalid;
-  if (m0 >= nval) return;  // token tile past the compacted tokens
   // K blocks [kb0, kb1) of the chunk belong to split sp.
   const int kper = (a.nk + a.splits - 1) / a.splits;
   const int kb0 = sp * kper;
