@@ -1,9 +1,14 @@
 // Kernels of the fused linear cross-entropy + entropy head (gfx950).
 //
-// Forward:  fwd_prep, pack (hidden) -> fwd_tile -> fwd_combine (-> fwd_reduce)
-// Backward: bwd_prep, pack (hidden, hidden^T) -> per vocabulary chunk
-//           { pack (weight chunk) -> bwd_dlogits -> bwd_dx -> bwd_dw
+// Forward:  fwd_prep (label checks, compaction of the valid tokens),
+//           pack (hidden) -> fwd_tile -> fwd_combine (-> fwd_reduce)
+// Backward: bwd_prep (compaction, per-token gradient constants),
+//           zero_ignored_rows, pack (hidden, hidden^T) -> per vocabulary chunk
+//           { pack (weight chunk) -> bwd_dlogits -> bwd_dx (-> dx_finalize
+//             after the last chunk when dH is K-split) -> bwd_dw
 //             (-> dw_reduce) }
+// Only the valid tokens, compacted in token order, enter the contractions;
+// results are scattered back to the original token rows.
 //
 // GEMM operands are read in the blocked layout of flce_gemm.hpp (the pack
 // kernels below build it from the caller's row-major tensors, and the
