@@ -253,6 +253,49 @@ flce_status_t flce_backward_shard(const void* hidden, const void* weight_shard,
                                   void* grad_hidden_partial, void* grad_weight_shard,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Fused forward + backward (gradient in the forward) ----------------------
+ * When the upstream gradients are known before the forward runs (a terminal
+ * loss such as the mean cross-entropy, or per-token weights fixed in
+ * advance), the logit gradient can be formed from logits kept during the
+ * forward instead of recomputing them in the backward: this is how the fused
+ * linear cross-entropy of Liger-Kernel pull request #551 (item 1 of its
+ * description) produces the loss and its input gradient in one pass. Here the
+ * tokens are taken in chunks; per chunk the capped logits of the whole
+ * vocabulary are kept as z' - m in bf16 (m: the maximum over 128 vocabulary
+ * rows, so the rounding error is relative to the distance from the maximum),
+ * and the gradient is formed from them once the chunk's logsumexp is known.
+ * Compared with flce_forward_ex + flce_backward_ex this saves the backward's
+ * logit GEMM (2*N*H*V flops) and costs workspace and HBM traffic:
+ *   chunk images  4 * 256*ceil(Nc/256) * 256*ceil(V/256) bytes,
+ *   the weight re-laid out, 2 * H * 256*ceil(V/256) bytes,
+ *   with more than one chunk and bf16 gradients, an fp32 dW accumulator of
+ *   4 * H * V bytes (fp32 gradients accumulate in grad_weight itself).
+ * The results agree with flce_forward_ex followed by flce_backward_ex to the
+ * rounding of the kept logits (bf16 of z' - m), not bit for bit.
+ *
+ * chunk_tokens: tokens per chunk Nc (rounded up to 256); 0 picks 4096, or all
+ * tokens when N <= 4096 + H (then chunking would not save memory). V <= 2^21.
+ * Workspace bytes for this shape, options and chunk_tokens (host only): */
+flce_status_t flce_fused_workspace_size(int64_t N, int64_t H, int64_t V, const flce_options_t* opt,
+                                        int64_t chunk_tokens, size_t* bytes);
+
+/* The outputs of flce_forward_ex (lse, logprob, entropy required when N > 0;
+ * uniform_ce, z_loss optional; reduced [4] required unless reduction is NONE)
+ * and the gradients of flce_backward_ex (grad_hidden [N,H], grad_weight [H,V],
+ * bf16 or fp32 as opt->grad_dtype says) for the upstream gradients given here
+ * as for flce_backward_ex ([N] under NONE, [1] under MEAN and SUM, NULL =
+ * zero). Under MEAN the scalar gradients are divided by the number of valid
+ * tokens counted by this call. Errors as flce_backward_ex; FLCE_ERR_BAD_SHAPE
+ * also for V > 2^21 or chunk_tokens < 0. */
+flce_status_t flce_forward_backward(const void* hidden, const void* weight, const int64_t* labels,
+                                    int64_t N, int64_t H, int64_t V, const flce_options_t* opt,
+                                    int64_t chunk_tokens, const float* grad_logprob,
+                                    const float* grad_entropy, const float* grad_uniform_ce,
+                                    const float* grad_z_loss, float* lse, float* logprob,
+                                    float* entropy, float* uniform_ce, float* z_loss,
+                                    float* reduced, void* grad_hidden, void* grad_weight,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Reads the status word that the last flce_forward / flce_backward on this
  * workspace left, after synchronising `stream`. *invalid_labels (may be NULL)
  * receives the number of labels that were neither ignore_index nor in [0, V);

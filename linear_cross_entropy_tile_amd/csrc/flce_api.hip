@@ -175,6 +175,82 @@ size_t merge_bytes(int64_t N) {
   return align_up(merge_bsum_off(N) + 32 * (size_t)ceil_div(N > 0 ? N : 1, kCombineTokens));
 }
 
+// ---- the fused path's plan --------------------------------------------------
+// The tokens are processed in chunks of TBc token blocks. Per chunk the
+// forward keeps the capped logits of all V columns (bf16, two bytes each) and
+// the logit gradient is formed from them in both blocked layouts, so the
+// chunk images take 4 * 256 TBc * 256 VT bytes; with several chunks dW is
+// accumulated over them in fp32 (H * V * 4 bytes, or in grad_weight itself
+// when it is fp32). By default a chunk holds 4096 tokens, or all of them when
+// that costs no more memory than chunking (N <= 4096 + H, counted in blocks).
+constexpr int kFusedChunkBlocks = 16;
+
+struct FusedPlan {
+  Plan b;              // TB, VT, HT, hkb, nkb, group of the shape
+  int TBc;             // token blocks per chunk
+  int nchunks;
+  int dx_splits;       // K splits of dH per chunk
+  int kbv;             // VT * 8: K blocks of a vocabulary-long strip
+  bool dw_acc;         // a separate fp32 dW accumulator
+  size_t idx, labc, zlab, part, bsum, coef, xb, xtb, wb, dtv, dvt, mref, dxacc, dwacc, total;
+};
+
+FusedPlan make_fused_plan(int64_t N, int64_t H, int64_t V, const flce_options_t& o,
+                          int64_t chunk_tokens) {
+  FusedPlan f{};
+  f.b = make_plan(N, H, V, o.reduction);
+  const Plan& p = f.b;
+  const int TB = p.TB;
+  int tbc;
+  if (chunk_tokens > 0)
+    tbc = (int)ceil_div(chunk_tokens, kTile);
+  else
+    tbc = TB <= kFusedChunkBlocks + p.HT ? TB : kFusedChunkBlocks;
+  if (tbc > TB) tbc = TB;
+  if (tbc < 1) tbc = 1;
+  f.TBc = tbc;
+  f.nchunks = TB > 0 ? (int)ceil_div(TB, tbc) : 0;
+  f.kbv = p.VT * (kTile / kBK);
+  {
+    const int64_t t = (int64_t)tbc * p.HT;
+    int best = 1;
+    double bcost = 1e30;
+    for (int sk = 1; sk <= 4; ++sk) {
+      const double cost = (double)ceil_div(t * sk, kNumCUs) / sk;
+      if (cost < bcost - 1e-9) {
+        bcost = cost;
+        best = sk;
+      }
+    }
+    f.dx_splits = best;
+  }
+  f.dw_acc = f.nchunks > 1 && o.grad_dtype != FLCE_GRAD_F32;
+  const size_t blk = (size_t)kBlockBytes;
+  const size_t rows = (size_t)TB * kTile;    // compacted rows, padded
+  const size_t crow = (size_t)tbc * kTile;   // rows of one chunk
+  size_t off = kHeaderBytes;
+  auto take = [&](size_t& field, size_t bytes) {
+    field = off;
+    off = align_up(off + bytes);
+  };
+  take(f.idx, 4 * (size_t)N);
+  take(f.labc, 4 * (size_t)N);
+  take(f.zlab, 4 * (size_t)N);
+  take(f.part, 16 * (size_t)p.VT * (size_t)N);
+  take(f.bsum, o.reduction != FLCE_REDUCTION_NONE ? 32 * rows / kCombineTokens : 0);
+  take(f.coef, sizeof(DzToken) * rows);
+  take(f.xb, blk * (size_t)TB * (size_t)p.hkb);
+  take(f.xtb, blk * (size_t)p.HT * (size_t)p.nkb);
+  take(f.wb, blk * (size_t)p.HT * (size_t)f.kbv);
+  take(f.dtv, blk * (size_t)tbc * (size_t)f.kbv);
+  take(f.dvt, blk * (size_t)p.VT * (size_t)tbc * (kTile / kBK));
+  take(f.mref, 4 * 2 * (size_t)p.VT * crow);
+  take(f.dxacc, f.dx_splits > 1 ? 4 * (size_t)f.dx_splits * crow * (size_t)H : 0);
+  take(f.dwacc, f.dw_acc ? 4 * (size_t)H * (size_t)V : 0);
+  f.total = off;
+  return f;
+}
+
 flce_status_t check_shape(int64_t N, int64_t H, int64_t V) {
   if (N < 0 || H < 1 || V < 1) return FLCE_ERR_BAD_SHAPE;
   if (N > kMaxN || H > kMaxH || V > kMaxV) return FLCE_ERR_BAD_SHAPE;
@@ -195,11 +271,13 @@ constexpr int64_t kMaxVF32 = (int64_t)1 << 21;
 // ---- kernel timing hooks --------------------------------------------------------
 enum Kind {
   K_FWD_PREP, K_FWD_TILE, K_FWD_COMBINE, K_FWD_REDUCE, K_BWD_PREP, K_BWD_DLOGITS, K_BWD_DX,
-  K_BWD_DW, K_DW_REDUCE, K_FILL, K_PACK_WEIGHT, K_PACK_HIDDEN, K_DX_FINALIZE, K_NUM
+  K_BWD_DW, K_DW_REDUCE, K_FILL, K_PACK_WEIGHT, K_PACK_HIDDEN, K_DX_FINALIZE, K_FUSED_TILE,
+  K_FUSED_DLOGITS, K_NUM
 };
 const char* kKindNames[K_NUM] = {"fwd_prep", "fwd_tile", "fwd_combine", "fwd_reduce", "bwd_prep",
                                  "bwd_dlogits", "bwd_dx", "bwd_dw", "dw_reduce", "fill_zero",
-                                 "pack_weight", "pack_hidden", "dx_finalize"};
+                                 "pack_weight", "pack_hidden", "dx_finalize", "fused_tile",
+                                 "fused_dlogits"};
 
 struct Pending {
   int kind;
@@ -401,6 +479,7 @@ flce_status_t forward_impl(const void* hidden, const void* weight, const int64_t
     a.hkb = p.hkb;
     a.VT = p.VT;
     a.TB = p.TB;
+    a.tb0 = 0;
     a.group = p.group;
     a.cap = softcap > 0.f ? softcap : 0.f;
     a.cap_k = softcap > 0.f ? 2.f * kLog2e / softcap : 0.f;
@@ -409,9 +488,9 @@ flce_status_t forward_impl(const void* hidden, const void* weight, const int64_t
     const int grid = p.TB * p.VT;
     FLCE_TRY(launch(K_FWD_TILE, st, [&] {
       if (softcap > 0.f)
-        fwd_tile_kernel<true><<<grid, kThreads, 0, st>>>(a);
+        fwd_tile_kernel<true, false><<<grid, kThreads, 0, st>>>(a);
       else
-        fwd_tile_kernel<false><<<grid, kThreads, 0, st>>>(a);
+        fwd_tile_kernel<false, false><<<grid, kThreads, 0, st>>>(a);
     }));
     CombineArgs c{};
     c.part = part;
@@ -571,6 +650,7 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
     x.idx = idx;
     x.nvalid = nvalid;
     x.splits = p.dx_splits;
+    x.r0 = 0;
     // With K splits every split accumulates (first chunk stores, later ones
     // add) and dx_finalize writes the output after the last chunk.
     const bool split = p.dx_splits > 1;
@@ -602,10 +682,10 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
       const int fb = (int)(ceil_div(work, 256) < 16384 ? ceil_div(work, 256) : 16384);
       FLCE_TRY(launch(K_DX_FINALIZE, st, [&] {
         if (f32)
-          dx_finalize_kernel<true><<<fb, 256, 0, st>>>(acc, p.dx_splits, N, H, idx, nvalid,
+          dx_finalize_kernel<true><<<fb, 256, 0, st>>>(acc, p.dx_splits, N, H, idx, nvalid, 0,
                                                        grad_hidden);
         else
-          dx_finalize_kernel<false><<<fb, 256, 0, st>>>(acc, p.dx_splits, N, H, idx, nvalid,
+          dx_finalize_kernel<false><<<fb, 256, 0, st>>>(acc, p.dx_splits, N, H, idx, nvalid, 0,
                                                         grad_hidden);
       }));
     }
@@ -619,6 +699,9 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
     w.v0 = v0;
     w.vc = vc;
     w.kbn = p.nkb;
+    w.kbn_a = p.nkb;
+    w.ka0 = 0;
+    w.r0 = 0;
     w.nvalid = nvalid;
     w.ldp = p.Vc;
     w.HT = p.HT;
@@ -631,11 +714,11 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
     const int gw = p.HT * vtc * p.dw_splits;
     FLCE_TRY(launch(K_BWD_DW, st, [&] {
       if (p.dw_splits > 1)
-        bwd_dw_kernel<true, false><<<gw, kThreads, 0, st>>>(w);
+        bwd_dw_kernel<DW_SPLIT, false><<<gw, kThreads, 0, st>>>(w);
       else if (f32)
-        bwd_dw_kernel<false, true><<<gw, kThreads, 0, st>>>(w);
+        bwd_dw_kernel<DW_DIRECT, true><<<gw, kThreads, 0, st>>>(w);
       else
-        bwd_dw_kernel<false, false><<<gw, kThreads, 0, st>>>(w);
+        bwd_dw_kernel<DW_DIRECT, false><<<gw, kThreads, 0, st>>>(w);
     }));
     if (p.dw_splits > 1) {
       const int64_t n = H * vc;
@@ -649,6 +732,278 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
                                                           grad_weight);
       }));
     }
+  }
+  return FLCE_OK;
+}
+
+// The fused forward + backward (gradient in the forward): the outputs of
+// forward_impl and the gradients of backward_impl in one pass over the
+// logits per chunk of tokens, without the backward's recompute.
+flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* labels, int64_t N,
+                         int64_t H, int64_t V, const flce_options_t& o, int64_t chunk_tokens,
+                         const float* grad_logprob, const float* grad_entropy,
+                         const float* grad_uniform_ce, const float* grad_z_loss, float* lse,
+                         float* logprob, float* entropy, float* uniform_ce, float* z_loss,
+                         float* reduced, void* grad_hidden, void* grad_weight, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const int reduction = o.reduction;
+  const bool reduce = reduction != FLCE_REDUCTION_NONE;
+  const bool f32 = o.grad_dtype == FLCE_GRAD_F32;
+  if (V > kMaxVF32) return FLCE_ERR_BAD_SHAPE;
+  if (chunk_tokens < 0) return FLCE_ERR_BAD_SHAPE;
+  if (workspace == nullptr || weight == nullptr || grad_weight == nullptr)
+    return FLCE_ERR_NULL_POINTER;
+  if (reduce && reduced == nullptr) return FLCE_ERR_NULL_POINTER;
+  if (N > 0 && (hidden == nullptr || labels == nullptr || lse == nullptr || logprob == nullptr ||
+                entropy == nullptr || grad_hidden == nullptr))
+    return FLCE_ERR_NULL_POINTER;
+  if (!aligned16(hidden) || !aligned16(weight) || !aligned16(grad_hidden) ||
+      !aligned16(grad_weight) || !aligned16(workspace))
+    return FLCE_ERR_MISALIGNED;
+  const FusedPlan f = make_fused_plan(N, H, V, o, chunk_tokens);
+  const Plan& p = f.b;
+  if (workspace_bytes < f.total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t out_elem = f32 ? 4 : 2;
+  const float softcap = o.softcap;
+  const bool capped = softcap > 0.f;
+
+  int32_t* header = reinterpret_cast<int32_t*>(workspace);
+  const int32_t* nvalid = header + 1;
+  int32_t* idx = reinterpret_cast<int32_t*>(wsp(workspace, f.idx));
+  int32_t* labc = reinterpret_cast<int32_t*>(wsp(workspace, f.labc));
+  float* zlab = reinterpret_cast<float*>(wsp(workspace, f.zlab));
+  float4* part = reinterpret_cast<float4*>(wsp(workspace, f.part));
+  double4* bsum = reduce ? reinterpret_cast<double4*>(wsp(workspace, f.bsum)) : nullptr;
+  DzToken* coef = reinterpret_cast<DzToken*>(wsp(workspace, f.coef));
+  uint16_t* xb = reinterpret_cast<uint16_t*>(wsp(workspace, f.xb));
+  uint16_t* xtb = reinterpret_cast<uint16_t*>(wsp(workspace, f.xtb));
+  uint16_t* wb = reinterpret_cast<uint16_t*>(wsp(workspace, f.wb));
+  uint16_t* dtv = reinterpret_cast<uint16_t*>(wsp(workspace, f.dtv));
+  uint16_t* dvt = reinterpret_cast<uint16_t*>(wsp(workspace, f.dvt));
+  float* mref = reinterpret_cast<float*>(wsp(workspace, f.mref));
+  float* dxacc = reinterpret_cast<float*>(wsp(workspace, f.dxacc));
+  float* dwacc = f32 ? static_cast<float*>(grad_weight)
+                     : reinterpret_cast<float*>(wsp(workspace, f.dwacc));
+
+  FwdPrepArgs pr{};
+  pr.labels = labels;
+  pr.N = N;
+  pr.V_total = V;
+  pr.v_begin = 0;
+  pr.Vs = V;
+  pr.ignore_index = o.ignore_index;
+  pr.idx = idx;
+  pr.labc = labc;
+  pr.zlab = zlab;
+  pr.lse = lse;
+  pr.logprob = logprob;
+  pr.entropy = entropy;
+  pr.uniform_ce = uniform_ce;
+  pr.z_loss = z_loss;
+  pr.header = header;
+  FLCE_TRY(launch(K_FWD_PREP, st, [&] { fwd_prep_kernel<<<1, 1024, 0, st>>>(pr); }));
+  const int nb = p.TB * (kTile / kCombineTokens);
+  if (N == 0) {
+    FLCE_TRY(zero_fill(grad_weight, out_elem * (size_t)H * (size_t)V, st));
+  } else {
+    const int zb = (int)(N < 16384 ? N : 16384);
+    FLCE_TRY(launch(K_FILL, st, [&] {
+      zero_ignored_rows_kernel<<<zb, 256, 0, st>>>(labels, N, V, o.ignore_index,
+                                                   static_cast<char*>(grad_hidden),
+                                                   (int64_t)out_elem * H);
+    }));
+    // Blocked operands over the valid tokens compacted in token order: hidden
+    // (K = H) for the logit tiles, hidden^T (K = tokens) for dW, and the
+    // weight (H rows, K = vocabulary) for dH.
+    FLCE_TRY(pack_rows(K_PACK_HIDDEN, hidden, N, H, H, p.hkb, idx, nvalid, xb, st));
+    FLCE_TRY(pack_cols(K_PACK_HIDDEN, hidden, H, N, H, p.nkb, idx, nvalid, xtb, st));
+    FLCE_TRY(pack_rows(K_PACK_WEIGHT, weight, H, V, V, f.kbv, nullptr, nullptr, wb, st));
+    const int64_t mld = (int64_t)f.TBc * kTile;
+    for (int c = 0; c < f.nchunks; ++c) {
+      const int tb0 = c * f.TBc;
+      const int tbc = p.TB - tb0 < f.TBc ? p.TB - tb0 : f.TBc;
+      const int r0 = tb0 * kTile;
+      const int64_t rows = (int64_t)tbc * kTile;
+
+      FwdTileArgs a{};
+      a.weight = static_cast<const uint16_t*>(weight);
+      a.xb = xb;
+      a.lab = labc;
+      a.nvalid = nvalid;
+      a.N = N;
+      a.H = H;
+      a.V = V;
+      a.hkb = p.hkb;
+      a.VT = p.VT;
+      a.TB = tbc;
+      a.tb0 = tb0;
+      a.group = p.group;
+      a.cap = capped ? softcap : 0.f;
+      a.cap_k = capped ? 2.f * kLog2e / softcap : 0.f;
+      a.part = part;
+      a.zlab = zlab;
+      a.dz = dtv;
+      a.kbv = f.kbv;
+      a.mref = mref;
+      a.mld = mld;
+      FLCE_TRY(launch(K_FUSED_TILE, st, [&] {
+        if (capped)
+          fwd_tile_kernel<true, true><<<tbc * p.VT, kThreads, 0, st>>>(a);
+        else
+          fwd_tile_kernel<false, true><<<tbc * p.VT, kThreads, 0, st>>>(a);
+      }));
+
+      CombineArgs cb{};
+      cb.part = part;
+      cb.S = p.VT;
+      cb.zlab = zlab;
+      cb.nz = 1;
+      cb.idx = idx;
+      cb.nvalid = nvalid;
+      cb.N = N;
+      cb.V = V;
+      cb.zl_scale = o.z_loss_scale;
+      cb.lse = lse;
+      cb.logprob = logprob;
+      cb.entropy = entropy;
+      cb.uniform_ce = uniform_ce;
+      cb.z_loss = z_loss;
+      cb.bsum = bsum;
+      cb.r0 = r0;
+      cb.coef = coef;
+      cb.glp = grad_logprob;
+      cb.gent = grad_entropy;
+      cb.guce = grad_uniform_ce;
+      cb.gzl = grad_z_loss;
+      cb.reduction = reduction;
+      cb.header = header;
+      FLCE_TRY(launch(K_FWD_COMBINE, st, [&] {
+        fwd_combine_kernel<<<(int)(rows / kCombineTokens), 64 * kCombineWaves, 0, st>>>(cb);
+      }));
+
+      FusedDzArgs d{};
+      d.dtv = dtv;
+      d.dvt = dvt;
+      d.mref = mref;
+      d.mld = mld;
+      d.coef = coef + r0;
+      d.lab = labc + r0;
+      d.nvalid = nvalid;
+      d.r0 = r0;
+      d.rows = N - r0 < rows ? N - r0 : rows;  // rows with coefficients and label codes
+      d.V = V;
+      d.VT = p.VT;
+      d.TB = tbc;
+      d.group = p.group;
+      d.kbv = f.kbv;
+      d.kbn = tbc * (kTile / kBK);
+      d.cap = capped ? softcap : 0.f;
+      d.inv_cap = capped ? 1.f / softcap : 0.f;
+      FLCE_TRY(launch(K_FUSED_DLOGITS, st, [&] {
+        if (capped)
+          fused_dlogits_kernel<true><<<tbc * p.VT, kThreads, 0, st>>>(d);
+        else
+          fused_dlogits_kernel<false><<<tbc * p.VT, kThreads, 0, st>>>(d);
+      }));
+
+      DxArgs x{};
+      x.dtv = dtv;
+      x.wb = wb;
+      x.N = rows;
+      x.H = H;
+      x.V = V;
+      x.kbv = f.kbv;
+      x.nk = f.kbv;
+      x.TB = tbc;
+      x.HT = p.HT;
+      x.group = p.group;
+      x.acc = dxacc;
+      x.gh = grad_hidden;
+      x.idx = idx + r0;
+      x.nvalid = nvalid;
+      x.splits = f.dx_splits;
+      x.r0 = r0;
+      const bool split = f.dx_splits > 1;
+      const int gx = tbc * p.HT * f.dx_splits;
+      FLCE_TRY(launch(K_BWD_DX, st, [&] {
+        if (split) {
+          if (f32)
+            bwd_dx_kernel<DX_FIRST, true><<<gx, kThreads, 0, st>>>(x);
+          else
+            bwd_dx_kernel<DX_FIRST, false><<<gx, kThreads, 0, st>>>(x);
+        } else {
+          if (f32)
+            bwd_dx_kernel<DX_ONLY, true><<<gx, kThreads, 0, st>>>(x);
+          else
+            bwd_dx_kernel<DX_ONLY, false><<<gx, kThreads, 0, st>>>(x);
+        }
+      }));
+      if (split) {
+        const int64_t work = rows * (H / 4);
+        const int fb = (int)(ceil_div(work, 256) < 16384 ? ceil_div(work, 256) : 16384);
+        FLCE_TRY(launch(K_DX_FINALIZE, st, [&] {
+          if (f32)
+            dx_finalize_kernel<true><<<fb, 256, 0, st>>>(dxacc, f.dx_splits, rows, H, idx + r0,
+                                                         nvalid, r0, grad_hidden);
+          else
+            dx_finalize_kernel<false><<<fb, 256, 0, st>>>(dxacc, f.dx_splits, rows, H, idx + r0,
+                                                          nvalid, r0, grad_hidden);
+        }));
+      }
+
+      DwArgs w{};
+      w.xtb = xtb;
+      w.dvt = dvt;
+      w.N = N;
+      w.H = H;
+      w.V = V;
+      w.v0 = 0;
+      w.vc = V;
+      w.kbn = tbc * (kTile / kBK);
+      w.kbn_a = p.nkb;
+      w.ka0 = tb0 * (kTile / kBK);
+      w.nvalid = nvalid;
+      w.r0 = r0;
+      w.HT = p.HT;
+      w.VTc = p.VT;
+      w.splits = 1;
+      w.group = p.group;
+      w.kper = w.kbn;
+      w.ldp = 0;
+      w.gw = grad_weight;
+      w.part = nullptr;
+      w.accw = dwacc;
+      // One chunk writes dW; several accumulate it in fp32 (in grad_weight
+      // itself when that is fp32) and the last one writes it.
+      const int mode = f.nchunks == 1 ? DW_DIRECT
+                                      : (c == 0 ? DW_FIRST : (c == f.nchunks - 1 ? DW_LAST : DW_MID));
+      const int gw = p.HT * p.VT;
+      FLCE_TRY(launch(K_BWD_DW, st, [&] {
+        if (f32) {
+          switch (mode) {
+            case DW_DIRECT: bwd_dw_kernel<DW_DIRECT, true><<<gw, kThreads, 0, st>>>(w); break;
+            case DW_FIRST: bwd_dw_kernel<DW_FIRST, true><<<gw, kThreads, 0, st>>>(w); break;
+            case DW_MID: bwd_dw_kernel<DW_MID, true><<<gw, kThreads, 0, st>>>(w); break;
+            default: bwd_dw_kernel<DW_LAST, true><<<gw, kThreads, 0, st>>>(w); break;
+          }
+        } else {
+          switch (mode) {
+            case DW_DIRECT: bwd_dw_kernel<DW_DIRECT, false><<<gw, kThreads, 0, st>>>(w); break;
+            case DW_FIRST: bwd_dw_kernel<DW_FIRST, false><<<gw, kThreads, 0, st>>>(w); break;
+            case DW_MID: bwd_dw_kernel<DW_MID, false><<<gw, kThreads, 0, st>>>(w); break;
+            default: bwd_dw_kernel<DW_LAST, false><<<gw, kThreads, 0, st>>>(w); break;
+          }
+        }
+      }));
+    }
+  }
+  if (reduce) {
+    const int mean = reduction == FLCE_REDUCTION_MEAN;
+    FLCE_TRY(launch(K_FWD_REDUCE, st, [&] {
+      fwd_reduce_kernel<<<1, 256, 0, st>>>(bsum, N > 0 ? nb : 0, header, mean, reduced,
+                                           reduced + 1, reduced + 2, reduced + 3);
+    }));
   }
   return FLCE_OK;
 }
@@ -713,6 +1068,32 @@ flce_status_t flce_backward_ex(const void* hidden, const void* weight, const int
   return backward_impl(hidden, weight, labels, N, H, V, 0, V, *opt, lse, entropy, grad_logprob,
                        grad_entropy, grad_uniform_ce, grad_z_loss, grad_hidden, grad_weight,
                        workspace, workspace_bytes, stream);
+}
+
+// ---- fused forward + backward ------------------------------------------------------
+
+flce_status_t flce_fused_workspace_size(int64_t N, int64_t H, int64_t V, const flce_options_t* opt,
+                                        int64_t chunk_tokens, size_t* bytes) {
+  FLCE_TRY(check_shape(N, H, V));
+  FLCE_TRY(check_options(opt));
+  if (V > kMaxVF32 || chunk_tokens < 0) return FLCE_ERR_BAD_SHAPE;
+  if (bytes) *bytes = make_fused_plan(N, H, V, *opt, chunk_tokens).total;
+  return FLCE_OK;
+}
+
+flce_status_t flce_forward_backward(const void* hidden, const void* weight, const int64_t* labels,
+                                    int64_t N, int64_t H, int64_t V, const flce_options_t* opt,
+                                    int64_t chunk_tokens, const float* grad_logprob,
+                                    const float* grad_entropy, const float* grad_uniform_ce,
+                                    const float* grad_z_loss, float* lse, float* logprob,
+                                    float* entropy, float* uniform_ce, float* z_loss,
+                                    float* reduced, void* grad_hidden, void* grad_weight,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  FLCE_TRY(check_shape(N, H, V));
+  FLCE_TRY(check_options(opt));
+  return fused_impl(hidden, weight, labels, N, H, V, *opt, chunk_tokens, grad_logprob,
+                    grad_entropy, grad_uniform_ce, grad_z_loss, lse, logprob, entropy, uniform_ce,
+                    z_loss, reduced, grad_hidden, grad_weight, workspace, workspace_bytes, stream);
 }
 
 // ---- vocabulary-sharded head ---------------------------------------------------
@@ -861,7 +1242,7 @@ const char* flce_status_string(flce_status_t s) {
   return "unknown status";
 }
 
-int flce_version(void) { return 200; }
+int flce_version(void) { return 210; }
 
 flce_status_t flce_profile_enable(int enable) {
   Profiler& P = prof();

@@ -113,6 +113,9 @@ __device__ __forceinline__ void buf_store_u16(uint32_t v, __amdgpu_buffer_rsrc_t
 __device__ __forceinline__ void buf_store_u32x2(u32x2_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);
 }
+__device__ __forceinline__ u32x2_t buf_load_u32x2(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+}
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4_t buf_load_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));

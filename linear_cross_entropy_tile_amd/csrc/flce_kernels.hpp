@@ -7,6 +7,12 @@
 //           { pack (weight chunk) -> bwd_dlogits -> bwd_dx (-> dx_finalize
 //             after the last chunk when dH is K-split) -> bwd_dw
 //             (-> dw_reduce) }
+// Fused (gradient in the forward, when the upstream gradients are known
+// before the forward runs): fwd_prep, pack (hidden, hidden^T, weight) ->
+//           per chunk of tokens { fwd_tile storing z' - m (bf16) ->
+//             fwd_combine (+ gradient constants) -> fused_dlogits ->
+//             bwd_dx (-> dx_finalize) -> bwd_dw (accumulating over chunks) }
+//           (-> fwd_reduce)
 // Only the valid tokens, compacted in token order, enter the contractions;
 // results are scattered back to the original token rows.
 //
@@ -234,12 +240,38 @@ struct FwdTileArgs {
   const int32_t* nvalid;   // device: number n of compacted tokens
   int64_t N, H, V;
   int hkb;                 // K blocks per strip, ceil(H / 32)
-  int VT, TB;              // vocabulary tiles, token blocks
+  int VT, TB;              // vocabulary tiles, token blocks of this launch
+  int tb0;                 // first token block of this launch
   int group;               // token blocks per XCD patch (see group_map)
   float cap, cap_k;        // softcap c and 2*log2(e)/c
   float4* part;            // [VT][N] {m, s, u, sum z'} per vocabulary tile (compacted tokens)
   float* zlab;             // [N] capped logit of the label (compacted tokens)
+  // STORE only: z' - mref as bf16 in a blocked image of the launch's tokens
+  // (strips of 256 tokens, K = vocabulary, kbv blocks per strip), and mref,
+  // the maximum of z' over each wave's 128 vocabulary rows, at
+  // mref[(2 vt + half) * mld + local token].
+  uint16_t* dz;
+  int kbv;
+  float* mref;
+  int64_t mld;
 };
+
+// Copies a tile's eight 16 KiB blocks from the stage arrays (block b in sa[b]
+// for b < 4, sb[b - 4] otherwise) to 128 KiB of contiguous memory: each wave
+// instruction stores 1 KiB. Iteration it covers half of block it / 2. The
+// caller synchronises the block before.
+__device__ __forceinline__ void copy_out_tile(char* const (&sa)[kStages],
+                                              char* const (&sb)[kStages],
+                                              __amdgpu_buffer_rsrc_t dst) {
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int b = it >> 1;
+    const int off = ((it & 1) * kThreads + (int)threadIdx.x) * 16;
+    const char* src = (b < 4 ? sa[b & 3] : sb[b & 3]) + off;
+    __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t*>(src), dst,
+                                           (uint32_t)(b * kBlockBytes + off), 0, 0);
+  }
+}
 
 // Merge state (m2, s2, u2) into (m, s, u); u in base-2 units (times log2 e).
 __device__ __forceinline__ void merge_state2(float& m, float& s, float& u, float m2, float s2,
@@ -317,18 +349,23 @@ __device__ __forceinline__ void column_stats(const Acc& acc, int j, float cap, f
 // accumulators of one 32-column block
 // belong to one token and the row statistics need no cross-lane work until the
 // end. The block reduces its tile to (m, s, u) per token and stores it as the
-// tile's partial state.
-template <bool CAP>
+// tile's partial state. STORE also keeps the capped logits for the fused
+// path, as z' - mref in bf16 (mref: the maximum over the wave's 128
+// vocabulary rows), so that the logit gradient can be formed later without
+// recomputing the tile.
+template <bool CAP, bool STORE>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(2, 2)))
 fwd_tile_kernel(FwdTileArgs a) {
   FLCE_DECLARE_STAGES(sa, sb);
-  // Only the token tiles that hold compacted tokens take part; the tile
-  // numbering runs over them alone, so every XCD gets its share.
-  const int tbv = (*a.nvalid + kTile - 1) / kTile;
+  // Only the token tiles of this launch that hold compacted tokens take part;
+  // the tile numbering runs over them alone, so every XCD gets its share.
+  const int left = (*a.nvalid + kTile - 1) / kTile - a.tb0;
+  const int tbv = left < a.TB ? (left > 0 ? left : 0) : a.TB;
   if ((int)blockIdx.x >= tbv * a.VT) return;
-  int tb, vt;
-  group_map(xcd_remap(blockIdx.x, tbv * a.VT), tbv, a.VT, a.group, tb, vt);
+  int tbl, vt;
+  group_map(xcd_remap(blockIdx.x, tbv * a.VT), tbv, a.VT, a.group, tbl, vt);
+  const int tb = a.tb0 + tbl;
   const int lane = threadIdx.x & 63, lh = lane >> 5;
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t n0 = (int64_t)tb * kTile;
@@ -345,6 +382,13 @@ fwd_tile_kernel(FwdTileArgs a) {
   const bool full = (int64_t)vb + 128 <= a.V;
   // Rows at offset o (0..127, without the lane-half term) are valid iff o < lim.
   const int lim = (int)(a.V - vb) - 4 * lh;
+  // STORE: the tile's eight dz blocks are assembled in the stage arrays,
+  // block 4 wm + i (vocabulary rows [32 (4 wm + i), +32)) in lds[i].
+  char* lds[4];
+  if constexpr (STORE) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds[i] = wm ? sb[i] : sa[i];
+  }
   float m[2], s[2], u[2], zs[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -353,6 +397,24 @@ fwd_tile_kernel(FwdTileArgs a) {
       column_stats<CAP, false>(acc, j, a.cap, a.cap_k, lim, z, m[j], s[j], u[j], zs[j]);
     else
       column_stats<CAP, true>(acc, j, a.cap, a.cap_k, lim, z, m[j], s[j], u[j], zs[j]);
+
+    if constexpr (STORE) {
+      // Rows m0 .. m0+3 (vocabulary) of token column n: one 8-byte piece.
+      // Masked rows hold kNegBig - mw (or 0 when the wave has no valid row);
+      // the gradient pass zeroes them.
+      const float mw = fmaxf(m[j], __shfl_xor(m[j], 32));
+      const int n = acc_col(wn, j, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int q = i * 16 + rq * 4;
+          const int m0 = acc_row(wm, i, rq * 4, lane);
+          *reinterpret_cast<u32x2_t*>(lds[i] + blk_byte(n, m0 & 31)) =
+              u32x2_t{pack_bf16x2(z[q] - mw, z[q + 1] - mw), pack_bf16x2(z[q + 2] - mw, z[q + 3] - mw)};
+        }
+      if (lh == 0) a.mref[(int64_t)(2 * vt + wm) * a.mld + tbl * kTile + n] = mw;
+    }
 
     // The label's logit: exactly one lane of one block in the grid owns it,
     // and most waves own none (skipped by a wave-uniform test).
@@ -378,7 +440,9 @@ fwd_tile_kernel(FwdTileArgs a) {
     merge_state2(m[j], s[j], u[j], m2, s2, u2);
     zs[j] += __shfl_xor(zs[j], 32);
   }
-  float4* red = reinterpret_cast<float4*>(sa[0]);
+  // (The stage arrays hold the dz blocks under STORE.)
+  __shared__ float4 red_store[STORE ? kTile : 1];
+  float4* red = STORE ? red_store : reinterpret_cast<float4*>(sa[0]);
   if (wm == 1 && lane < 32) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) red[acc_col(wn, j, lane)] = make_float4(m[j], s[j], u[j], zs[j]);
@@ -394,6 +458,9 @@ fwd_tile_kernel(FwdTileArgs a) {
       if (t < a.N) a.part[(int64_t)vt * a.N + t] = make_float4(m[j], s[j], u[j] * kLn2, zs[j] + q.w);
     }
   }
+  if constexpr (STORE)
+    copy_out_tile(sa, sb, make_rsrc(a.dz + ((int64_t)tbl * a.kbv + 8 * vt) * kBlockElems,
+                                    8 * (int64_t)kBlockBytes));
 }
 
 // ---- forward: merge the vocabulary splits -------------------------------------
@@ -408,6 +475,17 @@ __device__ __forceinline__ void merge_state(float& m, float& s, float& u, float 
   s = a1 * s + a2 * s2;
   m = mn;
 }
+
+// Per-token constants of the logit gradient (see bwd_dlogits_kernel):
+//   dz'_v = gbar [v == y] + k0 - p_v (ebar z'_v + cs),
+//   cs = gbar - ebar S - gu - 2 lam gz lse,  k0 = -gu / V,
+// from the upstream gradients gbar (logprob), ebar (entropy), gu
+// (uniform_ce) and gz (z_loss). Ignored tokens: lse = 1e30 (every p
+// underflows to 0) and zeros.
+struct DzToken {
+  float lse, ebar, cs, gbar;
+  float k0, pad0, pad1, pad2;
+};
 
 constexpr int kCombineTokens = 64;   // tokens per combine block (one per lane)
 constexpr int kCombineWaves = 16;    // vocabulary-tile groups per combine block
@@ -438,12 +516,42 @@ struct CombineArgs {
   double4* bsum;               // optional: {logprob, entropy, uniform_ce, z_loss} per block
   float4* state_out;           // if set: write the merged state {m, s, u, sum z'} instead
   float* label_logit;          // with state_out: the label logit per token
+  int64_t r0;                  // first entry of this launch (a multiple of 64)
+  // If coef is set (fused path, compacted mode): also the logit-gradient
+  // constants of each entry (see DzToken), from the upstream gradients
+  // glp, gent, guce, gzl ([N] under reduction none, [1] otherwise, null =
+  // zero); under mean the scalars are divided by the valid count header[1].
+  DzToken* coef;
+  const float *glp, *gent, *guce, *gzl;
+  int reduction;
+  const int32_t* header;
 };
+
+// Gradient constants of valid token t with lse l and entropy e (fused path;
+// the same arithmetic as bwd_prep_kernel, every label inside the vocabulary).
+__device__ __forceinline__ DzToken token_coef(const CombineArgs& a, int64_t t, float l, float e) {
+  const bool scalar = a.reduction != 0;
+  const int nv = a.header[1];
+  const float div = a.reduction == 1 ? (nv > 0 ? 1.f / (float)nv : 0.f) : 1.f;
+  auto grad = [&](const float* g) {
+    return g == nullptr ? 0.f : (scalar ? g[0] * div : g[t]);
+  };
+  const float g = grad(a.glp), ge = grad(a.gent), gu = grad(a.guce), gz = grad(a.gzl);
+  const float S = l - e;
+  DzToken c;
+  c.lse = l;
+  c.ebar = ge;
+  c.cs = g - ge * S - gu - 2.f * a.zl_scale * gz * l;
+  c.gbar = g;
+  c.k0 = -gu * (1.f / (float)a.V);
+  c.pad0 = c.pad1 = c.pad2 = 0.f;
+  return c;
+}
 
 __global__ void __launch_bounds__(1024) fwd_combine_kernel(CombineArgs a) {
   __shared__ float4 st[kCombineWaves][kCombineTokens];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t r = (int64_t)blockIdx.x * kCombineTokens + lane;  // entry
+  const int64_t r = a.r0 + (int64_t)blockIdx.x * kCombineTokens + lane;  // entry
   bool valid;
   int64_t t;  // token
   if (a.idx != nullptr) {
@@ -497,6 +605,9 @@ __global__ void __launch_bounds__(1024) fwd_combine_kernel(CombineArgs a) {
     r1 = e;
     r2 = uc;
     r3 = zl;
+    if (a.coef != nullptr) a.coef[r] = token_coef(a, t, l, e);
+  } else if (a.coef != nullptr) {
+    a.coef[r] = DzToken{1e30f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   } else if (a.idx == nullptr && r < a.N) {
     a.lse[r] = 0.f;
     a.entropy[r] = 0.f;
@@ -512,7 +623,7 @@ __global__ void __launch_bounds__(1024) fwd_combine_kernel(CombineArgs a) {
       r2 += __shfl_xor(r2, o);
       r3 += __shfl_xor(r3, o);
     }
-    if (lane == 0) a.bsum[blockIdx.x] = make_double4(r0, r1, r2, r3);
+    if (lane == 0) a.bsum[a.r0 / kCombineTokens + blockIdx.x] = make_double4(r0, r1, r2, r3);
   }
 }
 
@@ -549,16 +660,6 @@ __global__ void __launch_bounds__(256) fwd_reduce_kernel(const double4* __restri
 
 // ---- backward: per-token coefficients ------------------------------------------
 
-// Per-token constants of the logit gradient (see bwd_dlogits_kernel):
-//   dz'_v = gbar [v == y] + k0 - p_v (ebar z'_v + cs),
-//   cs = gbar - ebar S - gu - 2 lam gz lse,  k0 = -gu / V,
-// from the upstream gradients gbar (logprob), ebar (entropy), gu
-// (uniform_ce) and gz (z_loss). Ignored tokens: lse = 1e30 (every p
-// underflows to 0) and zeros.
-struct DzToken {
-  float lse, ebar, cs, gbar;
-  float k0, pad0, pad1, pad2;
-};
 
 struct PrepArgs {
   const int64_t* labels;
@@ -681,14 +782,15 @@ struct DzCoef {
 };
 
 // The logit gradient of token column j of a wave's 128 x 32 block, rounded to
-// bf16, for both blocked images (see bwd_dlogits_kernel). LABEL adds gbar at
-// the label's row offset yl; MASK zeroes rows at offset >= lim.
-// The token-major image goes to LDS (`lds[i]` holds block 4 wm + i of the
-// tile's 8 dtv blocks) and is copied out by the caller; the vocabulary-major
-// image is stored directly.
-template <bool CAP, bool MASK, bool LABEL>
+// bf16, for both blocked images (see bwd_dlogits_kernel). The accumulators
+// hold raw logits (RAW: the cap is applied here) or capped ones. LABEL adds
+// gbar at the label's row offset yl; MASK zeroes rows at offset >= lim.
+// The token-major piece of rows m0 .. m0+3 goes to out(i, n, m0, piece)
+// (block 4 wm + i of the tile's 8 dtv blocks); the vocabulary-major image is
+// stored directly.
+template <bool CAP, bool RAW, bool MASK, bool LABEL, class Out>
 __device__ __forceinline__ void dz_column(const Acc& acc, int j, const DzCoef& k, int yl, int lim,
-                                          int n, int wm, int wn, int lane, char* const (&lds)[kStages],
+                                          int n, int wm, int wn, int lane, const Out& out,
                                           __amdgpu_buffer_rsrc_t rvt) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -699,7 +801,7 @@ __device__ __forceinline__ void dz_column(const Acc& acc, int j, const DzCoef& k
       for (int r3 = 0; r3 < 4; ++r3) {
         const int o = i * 32 + 8 * rq + r3;
         float z = acc[i][j][rq * 4 + r3];
-        if constexpr (CAP) z = softcap_apply(z, k.cap, k.cap_k);
+        if constexpr (CAP && RAW) z = softcap_apply(z, k.cap, k.cap_k);
         const float p = fast_exp2(fmaf(z, kLog2e, k.nl));
         float v;
         if constexpr (LABEL)
@@ -717,13 +819,62 @@ __device__ __forceinline__ void dz_column(const Acc& acc, int j, const DzCoef& k
       const int m0 = acc_row(wm, i, rq * 4, lane);
       const uint32_t p0 = pack_bf16x2(d[0], d[1]), p1 = pack_bf16x2(d[2], d[3]);
       // dtv: row n (token), K = vocabulary m0 .. m0+3: one 8-byte piece.
-      *reinterpret_cast<u32x2_t*>(lds[i] + blk_byte(n, m0 & 31)) = u32x2_t{p0, p1};
+      out(i, n, m0, u32x2_t{p0, p1});
       // dvt: after the quad transpose, lane 4q+a holds row m0 + a for the
       // four token columns of its quad: one 8-byte piece at K = n & ~3.
       const u32x2_t tv = quad_transpose_bf16(p0, p1);
       buf_store_u32x2(tv, rvt, (uint32_t)((wn * 2 + j) * kBlockBytes +
                                           blk_byte(m0 + (lane & 3), (lane & 31) & ~3)));
     }
+  }
+}
+
+// The logit gradient of a tile held in the accumulators (raw logits when RAW,
+// capped ones otherwise), for both images: token-major pieces to out(), see
+// dz_column, and the vocabulary-major image through rvt. coef and lab are
+// indexed by compacted row; rows at or past `rows` get zero gradient. vg0 is
+// the tile's first vocabulary column within [0, V); kc carries the cap
+// constants.
+template <bool CAP, bool RAW, class Out>
+__device__ __forceinline__ void dlogits_epilogue(const Acc& acc, const DzToken* coef,
+                                                 const int32_t* lab, int64_t rows, int64_t n0,
+                                                 int64_t vg0, int64_t V, const DzCoef& kc, int wm,
+                                                 int wn, int lane, const Out& out,
+                                                 __amdgpu_buffer_rsrc_t rvt) {
+  const int lh = lane >> 5;
+  // Rows at offset o (i*32 + 8*(r/4) + r%4) of this lane are inside the
+  // vocabulary iff o < lim.
+  const int lim = (int)(V - vg0) - wm * 128 - 4 * lh;
+  const bool full = vg0 + kTile <= V;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = acc_col(wn, j, lane);
+    const int64_t t = n0 + n;
+    DzToken c{1e30f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int y = -1;
+    if (t < rows) {
+      c = coef[t];
+      y = lab[t];
+    }
+    // The label's row offset within this lane's rows, or -1.
+    const int64_t yo = (int64_t)y - vg0 - wm * 128 - 4 * lh;
+    const int yl = (y >= 0 && yo >= 0 && yo < 128) ? (int)yo : -1;
+    const DzCoef k{-c.lse * kLog2e, c.ebar, c.cs, c.gbar, c.k0, kc.cap, kc.cap_k, kc.inv_cap};
+    // Wave-uniform choice of the variant: the label term is needed by few
+    // waves, the row mask only in the last vocabulary tile.
+    const bool any_label = __builtin_amdgcn_ballot_w64(yl >= 0) != 0;
+    if (full) {
+      if (any_label)
+        dz_column<CAP, RAW, false, true>(acc, j, k, yl, lim, n, wm, wn, lane, out, rvt);
+      else
+        dz_column<CAP, RAW, false, false>(acc, j, k, yl, lim, n, wm, wn, lane, out, rvt);
+    } else {
+      if (any_label)
+        dz_column<CAP, RAW, true, true>(acc, j, k, yl, lim, n, wm, wn, lane, out, rvt);
+      else
+        dz_column<CAP, RAW, true, false>(acc, j, k, yl, lim, n, wm, wn, lane, out, rvt);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one token column at a time
   }
 }
 
@@ -743,7 +894,7 @@ bwd_dlogits_kernel(DlogitsArgs a) {
   if ((int)blockIdx.x >= tbv * a.VTc) return;
   int tb, vt;
   group_map(xcd_remap(blockIdx.x, tbv * a.VTc), tbv, a.VTc, a.group, tb, vt);
-  const int lane = threadIdx.x & 63, lh = lane >> 5;
+  const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t n0 = (int64_t)tb * kTile;
   const int64_t vg0 = a.v0 + (int64_t)vt * kTile;  // first vocabulary column of the tile
@@ -762,56 +913,88 @@ bwd_dlogits_kernel(DlogitsArgs a) {
       a.dtv + ((int64_t)tb * a.kbv + 8 * vt) * kBlockElems, 8 * (int64_t)kBlockBytes);
   const __amdgpu_buffer_rsrc_t rvt = make_rsrc(
       a.dvt + ((int64_t)vt * a.kbn + 8 * tb) * kBlockElems, 8 * (int64_t)kBlockBytes);
-  // Rows at offset o (i*32 + 8*(r/4) + r%4) of this lane are inside the
-  // vocabulary iff o < lim.
-  const int lim = (int)(a.V - vg0) - wm * 128 - 4 * lh;
-  const bool full = vg0 + kTile <= a.V;
   // The stage arrays are free after the main loop: the tile's 8 dtv blocks
   // (128 KiB) are assembled there, block b in sa[b] (b < 4) or sb[b - 4].
-  char* lds[kStages];
+  char* lds[4];
 #pragma unroll
-  for (int i = 0; i < kStages; ++i) lds[i] = wm ? sb[i] : sa[i];
+  for (int i = 0; i < 4; ++i) lds[i] = wm ? sb[i] : sa[i];
+  dlogits_epilogue<CAP, true>(
+      acc, a.coef, a.lab, a.N, n0, vg0, a.V, DzCoef{0.f, 0.f, 0.f, 0.f, 0.f, a.cap, a.cap_k, a.inv_cap},
+      wm, wn, lane,
+      [&](int i, int n, int m0, u32x2_t v) {
+        *reinterpret_cast<u32x2_t*>(lds[i] + blk_byte(n, m0 & 31)) = v;
+      },
+      rvt);
+  __syncthreads();
+  copy_out_tile(sa, sb, rtv);
+}
+
+// ---- fused path: the logit gradient from the stored logits ----------------------
+
+struct FusedDzArgs {
+  uint16_t* dtv;           // chunk image (strips of 256 tokens, K = vocabulary): z' - mref in
+                           // bf16 on entry (fwd_tile STORE), the logit gradient on exit
+  uint16_t* dvt;           // chunk image of its transpose (strips of 256 vocabulary rows,
+                           // K = the chunk's tokens)
+  const float* mref;       // [2 VT][mld] reference maxima (fwd_tile STORE)
+  int64_t mld;
+  const DzToken* coef;     // the chunk's rows (compacted)
+  const int32_t* lab;      // the chunk's label codes
+  const int32_t* nvalid;   // device: number of compacted tokens
+  int r0;                  // first compacted row of the chunk
+  int64_t rows;            // chunk rows that have coefficients and label codes (rows past
+                           // them get zero gradient)
+  int64_t V;
+  int VT, TB;              // vocabulary tiles, token blocks of the chunk
+  int group;
+  int kbv, kbn;            // K blocks per strip of dtv (VT * 8) and dvt (TB * 8)
+  float cap, inv_cap;
+};
+
+// Block (tb, vt) of a token chunk: reads the tile's stored z' - mref (the
+// lane layout of the MFMA accumulators, 8-byte pieces), adds mref back and
+// forms the logit gradient exactly as bwd_dlogits_kernel does from its
+// recomputed tile, writing dtv in place and dvt. Memory-bound: 2 bytes read
+// and 4 written per logit.
+template <bool CAP>
+__global__ void __launch_bounds__(kThreads) fused_dlogits_kernel(FusedDzArgs a) {
+  const int left = (*a.nvalid - a.r0 + kTile - 1) / kTile;
+  const int tbv = left < a.TB ? (left > 0 ? left : 0) : a.TB;
+  if ((int)blockIdx.x >= tbv * a.VT) return;
+  int tb, vt;
+  group_map(xcd_remap(blockIdx.x, tbv * a.VT), tbv, a.VT, a.group, tb, vt);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
+  const int64_t n0 = (int64_t)tb * kTile;
+  const int64_t vg0 = (int64_t)vt * kTile;
+  const __amdgpu_buffer_rsrc_t rtv = make_rsrc(
+      a.dtv + ((int64_t)tb * a.kbv + 8 * vt) * kBlockElems, 8 * (int64_t)kBlockBytes);
+  const __amdgpu_buffer_rsrc_t rvt = make_rsrc(
+      a.dvt + ((int64_t)vt * a.kbn + 8 * tb) * kBlockElems, 8 * (int64_t)kBlockBytes);
+  // Byte offset in the tile's dtv blocks of rows m0 .. m0+3 of token column n.
+  auto piece = [&](int i, int n, int m0) {
+    return (uint32_t)((4 * wm + i) * kBlockBytes + blk_byte(n, m0 & 31));
+  };
+  Acc acc;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int n = acc_col(wn, j, lane);
-    const int64_t t = n0 + n;
-    DzToken c{1e30f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int y = -1;
-    if (t < a.N) {
-      c = a.coef[t];
-      y = a.lab[t];
-    }
-    // The label's row offset within this lane's rows, or -1.
-    const int64_t yo = (int64_t)y - vg0 - wm * 128 - 4 * lh;
-    const int yl = (y >= 0 && yo >= 0 && yo < 128) ? (int)yo : -1;
-    const DzCoef k{-c.lse * kLog2e, c.ebar, c.cs, c.gbar, c.k0, a.cap, a.cap_k, a.inv_cap};
-    // Wave-uniform choice of the variant: the label term is needed by few
-    // waves, the row mask only in the last vocabulary tile.
-    const bool any_label = __builtin_amdgcn_ballot_w64(yl >= 0) != 0;
-    if (full) {
-      if (any_label)
-        dz_column<CAP, false, true>(acc, j, k, yl, lim, n, wm, wn, lane, lds, rvt);
-      else
-        dz_column<CAP, false, false>(acc, j, k, yl, lim, n, wm, wn, lane, lds, rvt);
-    } else {
-      if (any_label)
-        dz_column<CAP, true, true>(acc, j, k, yl, lim, n, wm, wn, lane, lds, rvt);
-      else
-        dz_column<CAP, true, false>(acc, j, k, yl, lim, n, wm, wn, lane, lds, rvt);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // one token column at a time
-  }
-  // Copy the dtv blocks out: each wave instruction stores 1 KiB of contiguous
-  // memory. Iteration it covers half of block it / 2.
-  __syncthreads();
+    const float mw = a.mref[(int64_t)(2 * vt + wm) * a.mld + n0 + n];
 #pragma unroll
-  for (int it = 0; it < 2 * 2 * kStages; ++it) {
-    const int b = it >> 1;
-    const int off = ((it & 1) * kThreads + (int)threadIdx.x) * 16;
-    const char* src = (b < kStages ? sa[b % kStages] : sb[b % kStages]) + off;
-    __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t*>(src), rtv,
-                                           (uint32_t)(b * kBlockBytes + off), 0, 0);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const u32x2_t v = buf_load_u32x2(rtv, piece(i, n, acc_row(wm, i, rq * 4, lane)));
+        acc[i][j][rq * 4 + 0] = __uint_as_float(v[0] << 16) + mw;
+        acc[i][j][rq * 4 + 1] = __uint_as_float(v[0] & 0xFFFF0000u) + mw;
+        acc[i][j][rq * 4 + 2] = __uint_as_float(v[1] << 16) + mw;
+        acc[i][j][rq * 4 + 3] = __uint_as_float(v[1] & 0xFFFF0000u) + mw;
+      }
   }
+  dlogits_epilogue<CAP, false>(
+      acc, a.coef, a.lab, a.rows, n0, vg0, a.V, DzCoef{0.f, 0.f, 0.f, 0.f, 0.f, a.cap, 0.f, a.inv_cap},
+      wm, wn, lane,
+      [&](int i, int n, int m0, u32x2_t v) { buf_store_u32x2(v, rtv, piece(i, n, m0)); }, rvt);
 }
 
 // ---- backward: dH (+)= D W_chunk^T ---------------------------------------------
@@ -829,8 +1012,10 @@ struct DxArgs {
   int splits;              // K splits of the chunk; split s accumulates into acc + s*N*H
   float* acc;              // [splits][N,H] fp32 accumulators over chunks (compacted rows)
   void* gh;                // [N,H] output, bf16 or fp32 (F32OUT); row idx[r] of compacted row r
-  const int32_t* idx;      // [N] compacted -> original token
+  const int32_t* idx;      // [N] compacted -> original token (of this launch's rows)
   const int32_t* nvalid;   // device: number of compacted tokens
+  int r0;                  // compacted row of this launch's row 0 (a token chunk; else 0);
+                           // N, TB, acc, idx and dtv cover the launch's rows
 };
 
 // C[t][h] = sum_v D[t][v] W[h][v0 + v] over the chunk. MODE: DX_ONLY (single chunk: write
@@ -843,8 +1028,9 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 bwd_dx_kernel(DxArgs a) {
   FLCE_DECLARE_STAGES(sa, sb);
   // Tiles numbered over the token tiles that hold compacted tokens only.
-  const int nval = *a.nvalid;
-  const int tbv = (nval + kTile - 1) / kTile;
+  const int nval = *a.nvalid - a.r0;  // valid rows from this launch's row 0
+  const int left = (nval + kTile - 1) / kTile;
+  const int tbv = left < a.TB ? (left > 0 ? left : 0) : a.TB;
   const int per_split = tbv * a.HT;
   if ((int)blockIdx.x >= per_split * a.splits) return;
   const int L = xcd_remap(blockIdx.x, per_split * a.splits);
@@ -914,14 +1100,16 @@ bwd_dx_kernel(DxArgs a) {
 }
 
 // With K-split dH: grad_hidden row idx[r] = sum over splits of acc[s][r],
-// for the compacted rows r < n, in split order; bf16 (RNE) or fp32.
+// for the rows r < min(n - r0, N) (n valid tokens, r0 the compacted row of
+// row 0), in split order; bf16 (RNE) or fp32.
 template <bool F32OUT>
 __global__ void __launch_bounds__(256) dx_finalize_kernel(const float* __restrict__ acc, int splits,
                                                           int64_t N, int64_t H,
                                                           const int32_t* __restrict__ idx,
                                                           const int32_t* __restrict__ nvalid,
-                                                          void* __restrict__ gh) {
-  const int64_t n = *nvalid;
+                                                          int64_t r0, void* __restrict__ gh) {
+  const int64_t nl = (int64_t)*nvalid - r0;
+  const int64_t n = nl < N ? (nl > 0 ? nl : 0) : N;
   const int64_t q = H / 4;  // 4-element groups per row
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n * q; e += (int64_t)gridDim.x * 256) {
     const int64_t r = e / q, c = (e % q) * 4;
@@ -939,22 +1127,32 @@ __global__ void __launch_bounds__(256) dx_finalize_kernel(const float* __restric
 
 // ---- backward: dW_chunk = hidden^T D ------------------------------------------
 
+// How bwd_dw_kernel stores its tile: DW_DIRECT writes dW (bf16 or fp32);
+// DW_SPLIT writes an fp32 partial of its token split; over the token chunks
+// of the fused path, DW_FIRST stores the fp32 accumulator, DW_MID adds into
+// it and DW_LAST adds and writes dW.
+enum { DW_DIRECT = 0, DW_SPLIT = 1, DW_FIRST = 2, DW_MID = 3, DW_LAST = 4 };
+
 struct DwArgs {
   const uint16_t* xtb;     // blocked hidden^T (strips of 256 hidden rows, K = tokens)
   const uint16_t* dvt;     // blocked D^T of the chunk (strips of 256 vocabulary rows, K = tokens)
   int64_t N, H, V, v0, vc;
-  int kbn;                 // K blocks per strip of both (token blocks * 8)
+  int kbn;                 // K blocks per strip of dvt (token blocks * 8)
+  int kbn_a;               // K blocks per strip of xtb
+  int ka0;                 // xtb's K block at dvt's K block 0 (a token chunk's first block)
   const int32_t* nvalid;   // device: number of compacted tokens (the K extent)
+  int r0;                  // compacted row at dvt's K index 0
   int HT, VTc, splits;
   int group;
   int kper;                // K blocks per split
   int64_t ldp;             // row stride of the split partials
   void* gw;                // [H,V] output, bf16 or fp32 (F32OUT)
-  float* part;             // [splits][H][ldp] fp32 (SPLIT only)
+  float* part;             // [splits][H][ldp] fp32 (DW_SPLIT)
+  float* accw;             // [H,V] fp32 accumulator (DW_FIRST, DW_MID, DW_LAST)
 };
 
 // C[h][v] = sum_t hidden[t][h] D[t][v] over the split's tokens.
-template <bool SPLIT, bool F32OUT>
+template <int MODE, bool F32OUT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(2, 2)))
 bwd_dw_kernel(DwArgs a) {
@@ -968,17 +1166,21 @@ bwd_dw_kernel(DwArgs a) {
   const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int64_t h0 = (int64_t)ht * kTile, vl0 = (int64_t)vt * kTile;
   const int kbeg = sp * a.kper;
-  const int kval = (*a.nvalid + kBK - 1) / kBK;  // K blocks holding compacted tokens
-  const int klim = kval < a.kbn ? kval : a.kbn;
+  // K blocks holding compacted tokens, from the launch's first row.
+  const int kval = (*a.nvalid - a.r0 + kBK - 1) / kBK;
+  const int klim = kval < a.kbn ? (kval > 0 ? kval : 0) : a.kbn;
   const int kend = kbeg + a.kper < klim ? kbeg + a.kper : klim;
   Acc acc;
   {
     Mainloop ml;
-    ml.run(sa, sb, blocked_a(Strip{a.xtb + (int64_t)ht * a.kbn * kBlockElems, a.kbn}, kbeg),
+    ml.run(sa, sb,
+           blocked_a(Strip{a.xtb + (int64_t)ht * a.kbn_a * kBlockElems, a.kbn_a}, a.ka0 + kbeg),
            Strip{a.dvt + (int64_t)vt * a.kbn * kBlockElems, a.kbn}, kbeg, kend - kbeg, acc);
   }
+  constexpr bool kSplit = MODE == DW_SPLIT;
+  constexpr bool kAccum = MODE == DW_FIRST || MODE == DW_MID || MODE == DW_LAST;
   int64_t ld, base, span;
-  if constexpr (SPLIT) {
+  if constexpr (kSplit) {
     ld = a.ldp;
     base = ((int64_t)sp * a.H + h0) * ld + vl0;
     span = (a.H - h0) * ld - vl0;
@@ -987,10 +1189,14 @@ bwd_dw_kernel(DwArgs a) {
     base = h0 * ld + a.v0 + vl0;
     span = (a.H - h0) * ld - (a.v0 + vl0);
   }
-  constexpr int kOut = (SPLIT || F32OUT) ? 4 : 2;  // bytes per stored element
+  // Bytes per stored element: fp32 for partials, the accumulator and fp32 dW.
+  constexpr int kOut = (MODE == DW_DIRECT || MODE == DW_LAST) && !F32OUT ? 2 : 4;
+  float* const fdst = kSplit ? a.part : (kAccum && MODE != DW_LAST ? a.accw : nullptr);
   const __amdgpu_buffer_rsrc_t rs =
-      SPLIT ? make_rsrc(a.part + base, span * 4)
-            : make_rsrc(static_cast<char*>(a.gw) + base * kOut, span * kOut);
+      fdst != nullptr ? make_rsrc(fdst + base, span * 4)
+                      : make_rsrc(static_cast<char*>(a.gw) + base * kOut, span * kOut);
+  const __amdgpu_buffer_rsrc_t racc =
+      (MODE == DW_MID || MODE == DW_LAST) ? make_rsrc(a.accw + base, span * 4) : rs;
   // Quad transposes as in bwd_dx_kernel; vc is a multiple of 8.
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -1004,11 +1210,19 @@ bwd_dw_kernel(DwArgs a) {
         const uint32_t e = (uint32_t)(row * ld + vq);
         const float x[4] = {acc[i][j][rq * 4], acc[i][j][rq * 4 + 1], acc[i][j][rq * 4 + 2],
                             acc[i][j][rq * 4 + 3]};
-        if constexpr (SPLIT || F32OUT)
-          buf_store_f32x4(quad_transpose_f32(x[0], x[1], x[2], x[3]), rs, vok ? e * 4 : kOOB);
-        else
+        if constexpr (kOut == 4) {
+          f32x4_t v = quad_transpose_f32(x[0], x[1], x[2], x[3]);
+          if constexpr (MODE == DW_MID || MODE == DW_LAST) v += buf_load_f32x4(racc, vok ? e * 4 : kOOB);
+          buf_store_f32x4(v, rs, vok ? e * 4 : kOOB);
+        } else if constexpr (MODE == DW_LAST) {
+          const f32x4_t v = quad_transpose_f32(x[0], x[1], x[2], x[3]) +
+                            buf_load_f32x4(racc, vok ? e * 4 : kOOB);
+          buf_store_u32x2(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rs,
+                          vok ? e * 2 : kOOB);
+        } else {
           buf_store_u32x2(quad_transpose_bf16(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])), rs,
                           vok ? e * 2 : kOOB);
+        }
       }
     }
   }

@@ -25,10 +25,10 @@ __all__ = [
     "FLCE_REDUCTION_NONE", "FLCE_REDUCTION_MEAN", "FLCE_REDUCTION_SUM",
     "FLCE_GRAD_BF16", "FLCE_GRAD_F32", "FlceOptions",
     "flce_workspace_size", "flce_forward", "flce_backward", "flce_forward_ex",
-    "flce_backward_ex", "flce_get_status",
+    "flce_backward_ex", "flce_fused_workspace_size", "flce_forward_backward", "flce_get_status",
     "flce_status_string", "flce_version", "flce_profile_enable", "flce_profile_reset",
     "flce_profile_kinds", "flce_profile_read", "profile_table",
-    "forward", "backward", "workspace_bytes",
+    "forward", "backward", "forward_backward", "workspace_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflce.so")
@@ -72,6 +72,12 @@ _SIG = {
                                        _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "flce_backward_ex": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, ctypes.POINTER(FlceOptions),
                                         _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "flce_fused_workspace_size": (ctypes.c_int, [_I64, _I64, _I64, ctypes.POINTER(FlceOptions),
+                                                 _I64, ctypes.POINTER(ctypes.c_size_t)]),
+    "flce_forward_backward": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64,
+                                             ctypes.POINTER(FlceOptions), _I64, _P, _P, _P, _P,
+                                             _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                             _P]),
     "flce_forward_shard": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64,
                                           ctypes.POINTER(FlceOptions), _P, _P, _P,
                                           ctypes.c_size_t, _P]),
@@ -168,6 +174,24 @@ def flce_backward_ex(hidden, weight, labels, N, H, V, opt, lse, entropy, grad_lo
                                   entropy, grad_logprob, grad_entropy, grad_uniform_ce,
                                   grad_z_loss, grad_hidden, grad_weight, workspace,
                                   workspace_bytes, stream), "flce_backward_ex")
+
+
+def flce_fused_workspace_size(N: int, H: int, V: int, opt, chunk_tokens: int = 0) -> int:
+    b = ctypes.c_size_t(0)
+    _check(lib().flce_fused_workspace_size(N, H, V, ctypes.byref(opt), chunk_tokens,
+                                           ctypes.byref(b)), "flce_fused_workspace_size")
+    return b.value
+
+
+def flce_forward_backward(hidden, weight, labels, N, H, V, opt, chunk_tokens, grad_logprob,
+                          grad_entropy, grad_uniform_ce, grad_z_loss, lse, logprob, entropy,
+                          uniform_ce, z_loss, reduced, grad_hidden, grad_weight, workspace,
+                          workspace_bytes, stream):
+    _check(lib().flce_forward_backward(hidden, weight, labels, N, H, V, ctypes.byref(opt),
+                                       chunk_tokens, grad_logprob, grad_entropy, grad_uniform_ce,
+                                       grad_z_loss, lse, logprob, entropy, uniform_ce, z_loss,
+                                       reduced, grad_hidden, grad_weight, workspace,
+                                       workspace_bytes, stream), "flce_forward_backward")
 
 
 def flce_forward_shard(hidden, weight_shard, labels, N, H, Vs, v_begin, V_total, opt, state,
@@ -386,3 +410,61 @@ def backward(hidden, weight, labels, lse, entropy, grad_logprob=None, grad_entro
                      _ptr(grad_uniform_ce), _ptr(grad_z_loss), gh.data_ptr(), gw.data_ptr(),
                      workspace.data_ptr(), workspace.numel(), _stream())
     return gh, gw
+
+
+def forward_backward(hidden, weight, labels, grad_logprob=None, grad_entropy=None,
+                     ignore_index: int = -100, softcap: float = 0.0, reduction: str = "none",
+                     grad_uniform_ce=None, grad_z_loss=None, z_loss_scale: float = 0.0,
+                     grad_dtype: str = "bf16", aux: bool = False, chunk_tokens: int = 0,
+                     workspace=None) -> dict:
+    """The fused forward + backward (flce_forward_backward): the outputs of
+    ``forward`` and, under "grad_hidden" / "grad_weight", the gradients of
+    ``backward`` for upstream gradients known before the call (fp32 [N] under
+    "none", [1] under "mean" and "sum", None for zero).
+    """
+    torch = _torch()
+    _require(hidden, torch.bfloat16, 2, "hidden")
+    _require(weight, torch.bfloat16, 2, "weight")
+    _require(labels, torch.int64, 1, "labels")
+    N, H = hidden.shape
+    V = weight.shape[1]
+    if weight.shape[0] != H or labels.shape[0] != N:
+        raise ValueError("shape mismatch among hidden [N,H], weight [H,V], labels [N]")
+    red = _REDUCTIONS[reduction]
+    gdt = _GRAD_DTYPES[grad_dtype]
+    want = N if red == FLCE_REDUCTION_NONE else 1
+    grads = ((grad_logprob, "grad_logprob"), (grad_entropy, "grad_entropy"),
+             (grad_uniform_ce, "grad_uniform_ce"), (grad_z_loss, "grad_z_loss"))
+    for g, name in grads:
+        if g is not None:
+            _require(g, torch.float32, 1, name)
+            if g.shape[0] != want:
+                raise ValueError(f"{name} must have {want} element(s) under '{reduction}'")
+    opt = FlceOptions(int(ignore_index), float(softcap), red, float(z_loss_scale), gdt)
+    nbytes = flce_fused_workspace_size(N, H, V, opt, int(chunk_tokens))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=hidden.device)
+    dev = hidden.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    odt = torch.float32 if gdt == FLCE_GRAD_F32 else torch.bfloat16
+    out = {"lse": torch.empty(N, **f32), "logprob": torch.empty(N, **f32),
+           "entropy": torch.empty(N, **f32), "workspace": workspace,
+           "grad_hidden": torch.empty((N, H), dtype=odt, device=dev),
+           "grad_weight": torch.empty((H, V), dtype=odt, device=dev)}
+    uce = torch.empty(N, **f32) if aux else None
+    zl = torch.empty(N, **f32) if aux else None
+    reduced = torch.empty(4, **f32) if red != FLCE_REDUCTION_NONE else None
+    flce_forward_backward(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), N, H, V, opt,
+                          int(chunk_tokens), _ptr(grad_logprob), _ptr(grad_entropy),
+                          _ptr(grad_uniform_ce), _ptr(grad_z_loss), out["lse"].data_ptr(),
+                          out["logprob"].data_ptr(), out["entropy"].data_ptr(), _ptr(uce),
+                          _ptr(zl), _ptr(reduced), out["grad_hidden"].data_ptr(),
+                          out["grad_weight"].data_ptr(), workspace.data_ptr(), workspace.numel(),
+                          _stream())
+    if aux:
+        out["uniform_ce"] = uce
+        out["z_loss"] = zl
+    if reduced is not None:
+        for k, name in enumerate(_OUT_NAMES):
+            out[f"{name}_{reduction}"] = reduced[k:k + 1]
+    return out

@@ -216,3 +216,49 @@ def test_merge_rejects_and_size():
     assert L.flce_merge_shards(A, A, 2, A, 4, 16, ctypes.byref(o), A, A, A, None, None, A, A, 8,
                                None) == 5
     assert flce.flce_merge_workspace_size(8192) >= 8192 * 8
+
+
+def _fused(opt=None, **kw):
+    args = dict(hidden=A, weight=A, labels=A, N=4, H=8, V=8, chunk=0, g=A, e=A, gu=None, gz=None,
+                lse=A, lp=A, ent=A, uce=None, zl=None, red=None, gh=A, gw=A, ws=A, wsb=BIG,
+                st=None)
+    args.update(kw)
+    o = ctypes.byref(opt) if opt is not None else None
+    return flce.lib().flce_forward_backward(
+        args["hidden"], args["weight"], args["labels"], args["N"], args["H"], args["V"], o,
+        args["chunk"], args["g"], args["e"], args["gu"], args["gz"], args["lse"], args["lp"],
+        args["ent"], args["uce"], args["zl"], args["red"], args["gh"], args["gw"], args["ws"],
+        args["wsb"], args["st"])
+
+
+@pytest.mark.parametrize("okw,kw,code", [
+    (None, {}, 1),                                           # no options
+    (dict(reduction=1), {}, 1), (dict(reduction=2), {}, 1),  # reduced outputs required
+    (dict(reduction=4), {}, 3), (dict(softcap=float("inf")), {}, 6),
+    (dict(z_loss_scale=-1.0), {}, 9), (dict(grad_dtype=2), {}, 9),
+    (dict(), dict(N=-1), 2), (dict(), dict(V=(1 << 21) + 8), 2),  # V <= 2^21
+    (dict(), dict(chunk=-256), 2), (dict(), dict(H=12), 4),
+    (dict(), dict(lse=None), 1), (dict(), dict(gw=None), 1), (dict(), dict(ws=None), 1),
+    (dict(), dict(gh=A + 8), 4), (dict(), dict(wsb=8), 5),
+])
+def test_forward_backward_rejects(okw, kw, code):
+    assert _fused(_opt(**okw) if okw is not None else None, **kw) == code
+
+
+def test_fused_workspace_size():
+    o = _opt()
+    one = flce.flce_fused_workspace_size(8192, 4096, 128256, o, 0)
+    four = flce.flce_fused_workspace_size(8192, 4096, 128256, o, 2048)
+    vt = -(-128256 // 256) * 256
+    # One chunk: both bf16 images of all 8192 x vt logits, the re-laid-out
+    # weight, and the forward's partial states.
+    assert one >= 4 * 8192 * vt + 2 * 4096 * vt + 16 * 8192 * (vt // 256)
+    # Four chunks: images of 2048 tokens plus the fp32 dW accumulator.
+    assert four >= 4 * 2048 * vt + 4 * 4096 * 128256
+    assert four < one
+    # fp32 gradients accumulate dW in grad_weight itself.
+    assert flce.flce_fused_workspace_size(8192, 4096, 128256, _opt(grad_dtype=1), 2048) < four
+    # The default keeps all tokens in one chunk when N <= 4096 + H.
+    assert flce.flce_fused_workspace_size(8192, 4096, 128256, o, 8192) == one
+    with pytest.raises(flce.FlceError):
+        flce.flce_fused_workspace_size(8, 8, (1 << 21) + 8, o, 0)
