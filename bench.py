@@ -7,6 +7,11 @@ seeded synthetic data resident in HBM before the timed region. The default
 workload is the Llama-3-shaped head (N=8192 tokens, H=4096, V=128256, Zipf
 labels, reduction none, per-token upstream gradients).
 
+--path fused times flce_forward_backward instead (the gradient formed from
+logits kept during the forward, for upstream gradients known in advance; no
+recompute GEMM). With the default path the fused one is also timed on the
+same inputs and reported under alt_paths.fused (--alt-fused 0 skips it).
+
 Prints one JSON line. Besides the throughput it reports:
   roofline      the dominant kernel's algorithmic TFLOP/s (flops per launch /
                 mean launch time from HIP events recorded by the library on its
@@ -14,7 +19,7 @@ Prints one JSON line. Besides the throughput it reports:
                 MFMA peak;
   kernels       the same figures for every kernel kind;
   cpu_baseline  the float64 CPU oracle timed on a bounded token sample;
-  memory        peak device memory of the fused step vs the fp32 logits that a
+  memory        peak device memory of one step vs the fp32 logits that a
                 materialising implementation needs;
   torch_ref     (optional) a materialising torch implementation of the same
                 forward + backward on the same GPU, for context.
@@ -48,7 +53,12 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 flop/clk x 2.4 GHz, dense
 METRIC = "fwd+bwd tokens/s and % bf16 MFMA peak, N=8192 H=4096 V=128256, 1 GPU"
 
 # Algorithmic flops per valid token of each kernel kind, in units of H*V.
-FLOPS_PER_TOKEN_HV = {"fwd_tile": 2, "bwd_dlogits": 2, "bwd_dx": 2, "bwd_dw": 2}
+FLOPS_PER_TOKEN_HV = {"fwd_tile": 2, "bwd_dlogits": 2, "bwd_dx": 2, "bwd_dw": 2, "fused_tile": 2}
+# Algorithmic HBM bytes per valid token of the memory-bound kernels, in units
+# of V: the fused path's gradient pass reads each kept bf16 logit and writes
+# the two bf16 gradient images.
+BYTES_PER_TOKEN_V = {"fused_dlogits": 6}
+PEAK_HBM_GBPS = 8000.0
 
 
 def parse():
@@ -61,6 +71,10 @@ def parse():
                     help="tokens of the CPU oracle sample (0 skips the CPU baseline)")
     ap.add_argument("--torch-ref", type=int, default=1,
                     help="also time a materialising torch fwd+bwd (0/1)")
+    ap.add_argument("--path", choices=("recompute", "fused"), default="recompute",
+                    help="recompute: flce_forward + flce_backward; fused: flce_forward_backward")
+    ap.add_argument("--alt-fused", type=int, default=1,
+                    help="with --path recompute, also time the fused path (0/1)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warmup "
                          "(the reference point of the HBM byte counters)")
@@ -171,6 +185,56 @@ def torch_reference(t, wl, iters=2):
             "what": "torch eager, fp32 logits materialised, autograd backward"}
 
 
+def kernel_rows(table, steps, n_valid, H, V):
+    """Per kernel kind: launches and ms per step, and the algorithmic rate."""
+    kernels = {}
+    for name, (n, tot) in table.items():
+        per = tot / n
+        row = {"launches_per_step": n / steps, "ms_per_launch": per, "ms_per_step": tot / steps}
+        if name in FLOPS_PER_TOKEN_HV:
+            flops = FLOPS_PER_TOKEN_HV[name] * n_valid * H * V * steps / n
+            row["tflops"] = flops / (per * 1e-3) / 1e12
+            row["mfma_frac"] = row["tflops"] / PEAK_BF16_TFLOPS
+        if name in BYTES_PER_TOKEN_V:
+            nbytes = BYTES_PER_TOKEN_V[name] * n_valid * V * steps / n
+            row["gbps"] = nbytes / (per * 1e-3) / 1e9
+            row["hbm_frac"] = row["gbps"] / PEAK_HBM_GBPS
+        kernels[name] = row
+    return kernels
+
+
+def timed(step, steps, warmup):
+    """Mean ms per step over `steps` after `warmup` steps, and the library's
+    per-kernel event timings of the timed steps."""
+    import torch
+    from linear_cross_entropy_tile_amd import flce
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    flce.flce_profile_reset()
+    flce.flce_profile_enable(True)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    flce.flce_profile_enable(False)
+    return a.elapsed_time(b) / steps, flce.profile_table()
+
+
+def peak_of(step):
+    """Peak device memory (torch allocator) of one step."""
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    step()
+    torch.cuda.synchronize()
+    return int(torch.cuda.max_memory_allocated())
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -208,7 +272,7 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     P = {k: v.data_ptr() for k, v in t.items()}
 
-    def step():
+    def step_recompute():
         flce.flce_forward(P["hidden"], P["weight"], P["labels"], N, H, V, wl.ignore_index,
                           wl.softcap, red, lse.data_ptr(), lp.data_ptr(), ent.data_ptr(),
                           lpm.data_ptr(), entm.data_ptr(), wsf.data_ptr(), fbytes, stream)
@@ -216,6 +280,22 @@ def main():
                            wl.softcap, red, lse.data_ptr(), ent.data_ptr(), P["grad_logprob"],
                            P["grad_entropy"], gh.data_ptr(), gw.data_ptr(), wsb.data_ptr(),
                            bbytes, stream)
+
+    opt = flce.FlceOptions(wl.ignore_index, wl.softcap, red, 0.0, flce.FLCE_GRAD_BF16)
+    reduced = torch.empty(4, **f32)
+    fused_ws = {}
+
+    def step_fused():
+        if "buf" not in fused_ws:
+            fused_ws["bytes"] = flce.flce_fused_workspace_size(N, H, V, opt, 0)
+            fused_ws["buf"] = torch.empty(fused_ws["bytes"], dtype=torch.uint8, device=dev)
+        flce.flce_forward_backward(P["hidden"], P["weight"], P["labels"], N, H, V, opt, 0,
+                                   P["grad_logprob"], P["grad_entropy"], None, None,
+                                   lse.data_ptr(), lp.data_ptr(), ent.data_ptr(), None, None,
+                                   reduced.data_ptr(), gh.data_ptr(), gw.data_ptr(),
+                                   fused_ws["buf"].data_ptr(), fused_ws["bytes"], stream)
+
+    step = step_fused if args.path == "fused" else step_recompute
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 19   # bf16 elements
@@ -227,46 +307,20 @@ def main():
         del src, dst
         print(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done", flush=True)
 
-    # Peak memory of one fused step, everything allocated by torch.
-    torch.cuda.synchronize()
-    torch.cuda.reset_peak_memory_stats()
-    step()
-    torch.cuda.synchronize()
-    fused_peak = torch.cuda.max_memory_allocated()
-    print(f"[bench] {wl.name} N={N} H={H} V={V}: warmup {args.warmup}", flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    print(f"[bench] timing {args.steps} steps", flush=True)
-    flce.flce_profile_reset()
-    flce.flce_profile_enable(True)
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(args.steps):
-        step()
-    b.record()
-    torch.cuda.synchronize()
-    flce.flce_profile_enable(False)
-    ms = a.elapsed_time(b) / args.steps
-    table = flce.profile_table()
-
-    kernels = {}
-    for name, (n, tot) in table.items():
-        per = tot / n
-        row = {"launches_per_step": n / args.steps, "ms_per_launch": per,
-               "ms_per_step": tot / args.steps}
-        if name in FLOPS_PER_TOKEN_HV:
-            flops = FLOPS_PER_TOKEN_HV[name] * n_valid * H * V * args.steps / n
-            row["tflops"] = flops / (per * 1e-3) / 1e12
-            row["mfma_frac"] = row["tflops"] / PEAK_BF16_TFLOPS
-        kernels[name] = row
-    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    # Peak memory of one step, everything allocated by torch.
+    step_peak = peak_of(step)
+    print(f"[bench] {wl.name} N={N} H={H} V={V} path={args.path}: warmup {args.warmup}, "
+          f"timing {args.steps} steps", flush=True)
+    ms, table = timed(step, args.steps, args.warmup)
+    kernels = kernel_rows(table, args.steps, n_valid, H, V)
+    dom = max((k for k in kernels if "tflops" in kernels[k]),
+              key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dom]
-    traffic = counted_traffic(wl.name)
-    step_tflops = 8.0 * n_valid * H * V / (ms * 1e-3) / 1e12
+    traffic = counted_traffic(wl.name) if args.path == "recompute" else None
+    # Algorithmic flops of the step: 8 N H V with the recompute (forward,
+    # recompute, dH, dW), 6 N H V on the fused path, which skips the recompute.
+    step_flops_hv = 8.0 if args.path == "recompute" else 6.0
+    step_tflops = step_flops_hv * n_valid * H * V / (ms * 1e-3) / 1e12
 
     out = {
         "metric": METRIC,
@@ -283,7 +337,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "N": N, "H": H, "V": V, "n_valid": n_valid,
                    "labels": wl.labels, "softcap": wl.softcap, "reduction": wl.reduction,
-                   "parallelism": "single GPU"},
+                   "path": args.path, "parallelism": "single GPU"},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": dk.get("tflops"),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": dk.get("mfma_frac"),
@@ -291,10 +345,21 @@ def main():
         "step_tflops": step_tflops,
         "step_mfma_frac": step_tflops / PEAK_BF16_TFLOPS,
         "kernels": kernels,
-        "memory": {"fused_step_peak_bytes": int(fused_peak),
+        "memory": {"step_peak_bytes": int(step_peak),
                    "fp32_logits_bytes": 4 * N * V,
-                   "workspace_bytes": {"forward": fbytes, "backward": bbytes}},
+                   "workspace_bytes": ({"forward": fbytes, "backward": bbytes}
+                                       if args.path == "recompute"
+                                       else {"fused": fused_ws.get("bytes")})},
     }
+    if args.path == "recompute" and args.alt_fused:
+        print("[bench] fused path (gradient in the forward)", flush=True)
+        fpeak = peak_of(step_fused)
+        fms, ftable = timed(step_fused, args.steps, args.warmup)
+        out["alt_paths"] = {"fused": {
+            "value": N / (fms * 1e-3), "unit": "tokens/s", "ms_per_step": fms,
+            "executed_tflops": 6.0 * n_valid * H * V / (fms * 1e-3) / 1e12,
+            "peak_bytes": fpeak, "workspace_bytes": fused_ws["bytes"],
+            "kernels": kernel_rows(ftable, args.steps, n_valid, H, V)}}
     if args.torch_ref:
         try:
             print("[bench] torch materialising reference", flush=True)

@@ -21,7 +21,10 @@
  *                                                is the label-smoothed cross-entropy)
  *   z_loss_i     = lam * lse_i^2                (z-loss with scale lam)
  *
- * a "sum" reduction, and fp32 gradient outputs.
+ * a "sum" reduction, and fp32 gradient outputs. flce_forward_backward
+ * returns the outputs and the gradients of one batch in a single call when
+ * the upstream gradients are known in advance (the logit gradient formed from
+ * logits kept during the forward, no recompute).
  *
  * Sources: verl pull request #462 (memory-efficient linear_cross_entropy),
  * sections "Equivalent compute logic" (the definition above, and that logprobs
@@ -273,8 +276,8 @@ flce_status_t flce_backward_shard(const void* hidden, const void* weight_shard,
  * The results agree with flce_forward_ex followed by flce_backward_ex to the
  * rounding of the kept logits (bf16 of z' - m), not bit for bit.
  *
- * chunk_tokens: tokens per chunk Nc (rounded up to 256); 0 picks 4096, or all
- * tokens when N <= 4096 + H (then chunking would not save memory). V <= 2^21.
+ * chunk_tokens: tokens per chunk Nc (rounded up to 256); 0 picks 8192, or all
+ * tokens when N <= 8192 + H (then chunking would not save memory). V <= 2^21.
  * Workspace bytes for this shape, options and chunk_tokens (host only): */
 flce_status_t flce_fused_workspace_size(int64_t N, int64_t H, int64_t V, const flce_options_t* opt,
                                         int64_t chunk_tokens, size_t* bytes);

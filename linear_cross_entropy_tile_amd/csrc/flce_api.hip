@@ -181,9 +181,9 @@ size_t merge_bytes(int64_t N) {
 // the logit gradient is formed from them in both blocked layouts, so the
 // chunk images take 4 * 256 TBc * 256 VT bytes; with several chunks dW is
 // accumulated over them in fp32 (H * V * 4 bytes, or in grad_weight itself
-// when it is fp32). By default a chunk holds 4096 tokens, or all of them when
-// that costs no more memory than chunking (N <= 4096 + H, counted in blocks).
-constexpr int kFusedChunkBlocks = 16;
+// when it is fp32). By default a chunk holds 8192 tokens, or all of them when
+// that costs no more memory than chunking (N <= 8192 + H, counted in blocks).
+constexpr int kFusedChunkBlocks = 32;
 
 struct FusedPlan {
   Plan b;              // TB, VT, HT, hkb, nkb, group of the shape

@@ -258,7 +258,10 @@ def test_fused_workspace_size():
     assert four < one
     # fp32 gradients accumulate dW in grad_weight itself.
     assert flce.flce_fused_workspace_size(8192, 4096, 128256, _opt(grad_dtype=1), 2048) < four
-    # The default keeps all tokens in one chunk when N <= 4096 + H.
+    # The default keeps all tokens in one chunk when N <= 8192 + H, else
+    # takes chunks of 8192.
     assert flce.flce_fused_workspace_size(8192, 4096, 128256, o, 8192) == one
+    assert (flce.flce_fused_workspace_size(32768, 4096, 128256, o, 0)
+            == flce.flce_fused_workspace_size(32768, 4096, 128256, o, 8192))
     with pytest.raises(flce.FlceError):
         flce.flce_fused_workspace_size(8, 8, (1 << 21) + 8, o, 0)
