@@ -93,16 +93,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def counted_traffic(workload: str):
-    """Per-kernel HBM bytes per launch from profiles/traffic_<workload>.txt, or
-    None when absent or taken on other sources. Lines of that file:
+def counted_traffic(workload: str, path: str = "recompute"):
+    """Per-kernel HBM bytes per launch from profiles/traffic_<workload>.txt
+    (traffic_<workload>_fused.txt for the fused path), or None when absent or
+    taken on other sources. Lines of that file:
       source_sha256 <hex>
       kernel <kind> fetch_bytes <B> write_bytes <B>"""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
-    if not os.path.exists(path):
+    suffix = "" if path == "recompute" else "_" + path
+    fname = os.path.join(ROOT, "profiles", f"traffic_{workload}{suffix}.txt")
+    if not os.path.exists(fname):
         return None
     sha, per = None, {}
-    with open(path) as fh:
+    with open(fname) as fh:
         for line in fh:
             f = line.split()
             if len(f) >= 2 and f[0] == "source_sha256":
@@ -316,7 +318,7 @@ def main():
     dom = max((k for k in kernels if "tflops" in kernels[k]),
               key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dom]
-    traffic = counted_traffic(wl.name) if args.path == "recompute" else None
+    traffic = counted_traffic(wl.name, args.path)
     # Algorithmic flops of the step: 8 N H V with the recompute (forward,
     # recompute, dH, dW), 6 N H V on the fused path, which skips the recompute.
     step_flops_hv = 8.0 if args.path == "recompute" else 6.0
@@ -355,11 +357,17 @@ def main():
         print("[bench] fused path (gradient in the forward)", flush=True)
         fpeak = peak_of(step_fused)
         fms, ftable = timed(step_fused, args.steps, args.warmup)
+        fk = kernel_rows(ftable, args.steps, n_valid, H, V)
+        fdom = max((k for k in fk if "tflops" in fk[k]), key=lambda k: fk[k]["ms_per_step"])
         out["alt_paths"] = {"fused": {
             "value": N / (fms * 1e-3), "unit": "tokens/s", "ms_per_step": fms,
             "executed_tflops": 6.0 * n_valid * H * V / (fms * 1e-3) / 1e12,
             "peak_bytes": fpeak, "workspace_bytes": fused_ws["bytes"],
-            "kernels": kernel_rows(ftable, args.steps, n_valid, H, V)}}
+            "roofline": {"kernel": fdom, "bound": "mfma", "achieved": fk[fdom]["tflops"],
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": fk[fdom]["mfma_frac"],
+                         "traffic": (counted_traffic(wl.name, "fused") or {}).get(fdom)},
+            "kernels": fk}}
     if args.torch_ref:
         try:
             print("[bench] torch materialising reference", flush=True)

@@ -488,9 +488,9 @@ flce_status_t forward_impl(const void* hidden, const void* weight, const int64_t
     const int grid = p.TB * p.VT;
     FLCE_TRY(launch(K_FWD_TILE, st, [&] {
       if (softcap > 0.f)
-        fwd_tile_kernel<true, false><<<grid, kThreads, 0, st>>>(a);
+        fwd_tile_kernel<true><<<grid, kThreads, 0, st>>>(a);
       else
-        fwd_tile_kernel<false, false><<<grid, kThreads, 0, st>>>(a);
+        fwd_tile_kernel<false><<<grid, kThreads, 0, st>>>(a);
     }));
     CombineArgs c{};
     c.part = part;
@@ -849,9 +849,9 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
       a.mld = mld;
       FLCE_TRY(launch(K_FUSED_TILE, st, [&] {
         if (capped)
-          fwd_tile_kernel<true, true><<<tbc * p.VT, kThreads, 0, st>>>(a);
+          fused_tile_kernel<true><<<tbc * p.VT, kThreads, 0, st>>>(a);
         else
-          fwd_tile_kernel<false, true><<<tbc * p.VT, kThreads, 0, st>>>(a);
+          fused_tile_kernel<false><<<tbc * p.VT, kThreads, 0, st>>>(a);
       }));
 
       CombineArgs cb{};

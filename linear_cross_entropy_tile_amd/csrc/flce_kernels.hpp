@@ -354,9 +354,7 @@ __device__ __forceinline__ void column_stats(const Acc& acc, int j, float cap, f
 // vocabulary rows), so that the logit gradient can be formed later without
 // recomputing the tile.
 template <bool CAP, bool STORE>
-__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                               amdgpu_waves_per_eu(2, 2)))
-fwd_tile_kernel(FwdTileArgs a) {
+__device__ __forceinline__ void fwd_tile_body(const FwdTileArgs& a) {
   FLCE_DECLARE_STAGES(sa, sb);
   // Only the token tiles of this launch that hold compacted tokens take part;
   // the tile numbering runs over them alone, so every XCD gets its share.
@@ -461,6 +459,21 @@ fwd_tile_kernel(FwdTileArgs a) {
   if constexpr (STORE)
     copy_out_tile(sa, sb, make_rsrc(a.dz + ((int64_t)tbl * a.kbv + 8 * vt) * kBlockElems,
                                     8 * (int64_t)kBlockBytes));
+}
+
+template <bool CAP>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                               amdgpu_waves_per_eu(2, 2)))
+fwd_tile_kernel(FwdTileArgs a) {
+  fwd_tile_body<CAP, false>(a);
+}
+
+// The fused path's logit tiles: fwd_tile_kernel plus the kept logits.
+template <bool CAP>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                               amdgpu_waves_per_eu(2, 2)))
+fused_tile_kernel(FwdTileArgs a) {
+  fwd_tile_body<CAP, true>(a);
 }
 
 // ---- forward: merge the vocabulary splits -------------------------------------
