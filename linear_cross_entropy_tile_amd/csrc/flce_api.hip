@@ -974,27 +974,17 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
       w.gw = grad_weight;
       w.part = nullptr;
       w.accw = dwacc;
-      // One chunk writes dW; several accumulate it in fp32 (in grad_weight
-      // itself when that is fp32) and the last one writes it.
-      const int mode = f.nchunks == 1 ? DW_DIRECT
-                                      : (c == 0 ? DW_FIRST : (c == f.nchunks - 1 ? DW_LAST : DW_MID));
+      w.rows = rows;
+      w.first = c == 0;
+      // The chunk holding the last valid token writes dW; earlier chunks
+      // accumulate it in fp32 (in grad_weight itself when that is fp32);
+      // later, empty chunks exit. Decided on the device from the valid count.
       const int gw = p.HT * p.VT;
       FLCE_TRY(launch(K_BWD_DW, st, [&] {
-        if (f32) {
-          switch (mode) {
-            case DW_DIRECT: bwd_dw_kernel<DW_DIRECT, true><<<gw, kThreads, 0, st>>>(w); break;
-            case DW_FIRST: bwd_dw_kernel<DW_FIRST, true><<<gw, kThreads, 0, st>>>(w); break;
-            case DW_MID: bwd_dw_kernel<DW_MID, true><<<gw, kThreads, 0, st>>>(w); break;
-            default: bwd_dw_kernel<DW_LAST, true><<<gw, kThreads, 0, st>>>(w); break;
-          }
-        } else {
-          switch (mode) {
-            case DW_DIRECT: bwd_dw_kernel<DW_DIRECT, false><<<gw, kThreads, 0, st>>>(w); break;
-            case DW_FIRST: bwd_dw_kernel<DW_FIRST, false><<<gw, kThreads, 0, st>>>(w); break;
-            case DW_MID: bwd_dw_kernel<DW_MID, false><<<gw, kThreads, 0, st>>>(w); break;
-            default: bwd_dw_kernel<DW_LAST, false><<<gw, kThreads, 0, st>>>(w); break;
-          }
-        }
+        if (f32)
+          bwd_dw_kernel<DW_CHUNK, true><<<gw, kThreads, 0, st>>>(w);
+        else
+          bwd_dw_kernel<DW_CHUNK, false><<<gw, kThreads, 0, st>>>(w);
       }));
     }
   }

@@ -1141,10 +1141,15 @@ __global__ void __launch_bounds__(256) dx_finalize_kernel(const float* __restric
 // ---- backward: dW_chunk = hidden^T D ------------------------------------------
 
 // How bwd_dw_kernel stores its tile: DW_DIRECT writes dW (bf16 or fp32);
-// DW_SPLIT writes an fp32 partial of its token split; over the token chunks
-// of the fused path, DW_FIRST stores the fp32 accumulator, DW_MID adds into
-// it and DW_LAST adds and writes dW.
-enum { DW_DIRECT = 0, DW_SPLIT = 1, DW_FIRST = 2, DW_MID = 3, DW_LAST = 4 };
+// DW_SPLIT writes an fp32 partial of its token split. DW_CHUNK is the fused
+// path's token chunk, whose store is chosen on the device from the number n
+// of valid tokens: a chunk holding none exits (chunk 0 excepted, which writes
+// zeros when n = 0); chunk 0 stores the fp32 accumulator, or writes dW when
+// it also holds the last valid token; later chunks add into the accumulator,
+// and the one holding the last valid token adds and writes dW. Empty chunks
+// thus cost no pass over the accumulator.
+enum { DW_DIRECT = 0, DW_SPLIT = 1, DW_CHUNK = 2 };
+enum { DWS_DIRECT = 0, DWS_SPLIT = 1, DWS_FIRST = 2, DWS_MID = 3, DWS_LAST = 4 };
 
 struct DwArgs {
   const uint16_t* xtb;     // blocked hidden^T (strips of 256 hidden rows, K = tokens)
@@ -1155,43 +1160,24 @@ struct DwArgs {
   int ka0;                 // xtb's K block at dvt's K block 0 (a token chunk's first block)
   const int32_t* nvalid;   // device: number of compacted tokens (the K extent)
   int r0;                  // compacted row at dvt's K index 0
+  int64_t rows;            // DW_CHUNK: rows of this chunk
+  int first;               // DW_CHUNK: 1 for the first chunk
   int HT, VTc, splits;
   int group;
   int kper;                // K blocks per split
   int64_t ldp;             // row stride of the split partials
   void* gw;                // [H,V] output, bf16 or fp32 (F32OUT)
   float* part;             // [splits][H][ldp] fp32 (DW_SPLIT)
-  float* accw;             // [H,V] fp32 accumulator (DW_FIRST, DW_MID, DW_LAST)
+  float* accw;             // [H,V] fp32 accumulator over chunks (DW_CHUNK; grad_weight
+                           // itself when F32OUT)
 };
 
-// C[h][v] = sum_t hidden[t][h] D[t][v] over the split's tokens.
-template <int MODE, bool F32OUT>
-__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                               amdgpu_waves_per_eu(2, 2)))
-bwd_dw_kernel(DwArgs a) {
-  FLCE_DECLARE_STAGES(sa, sb);
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int per = a.HT * a.VTc;
-  const int sp = L / per;
-  int ht, vt;
-  group_map(L - sp * per, a.HT, a.VTc, a.group, ht, vt);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
-  const int64_t h0 = (int64_t)ht * kTile, vl0 = (int64_t)vt * kTile;
-  const int kbeg = sp * a.kper;
-  // K blocks holding compacted tokens, from the launch's first row.
-  const int kval = (*a.nvalid - a.r0 + kBK - 1) / kBK;
-  const int klim = kval < a.kbn ? (kval > 0 ? kval : 0) : a.kbn;
-  const int kend = kbeg + a.kper < klim ? kbeg + a.kper : klim;
-  Acc acc;
-  {
-    Mainloop ml;
-    ml.run(sa, sb,
-           blocked_a(Strip{a.xtb + (int64_t)ht * a.kbn_a * kBlockElems, a.kbn_a}, a.ka0 + kbeg),
-           Strip{a.dvt + (int64_t)vt * a.kbn * kBlockElems, a.kbn}, kbeg, kend - kbeg, acc);
-  }
-  constexpr bool kSplit = MODE == DW_SPLIT;
-  constexpr bool kAccum = MODE == DW_FIRST || MODE == DW_MID || MODE == DW_LAST;
+// Stores tile (h0, vl0) of split sp as STORE (a DWS_ value) says.
+template <int STORE, bool F32OUT>
+__device__ __forceinline__ void dw_store_tile(const Acc& acc, const DwArgs& a, int64_t h0,
+                                              int64_t vl0, int sp, int wm, int wn, int lane) {
+  constexpr bool kSplit = STORE == DWS_SPLIT;
+  constexpr bool kRead = STORE == DWS_MID || STORE == DWS_LAST;
   int64_t ld, base, span;
   if constexpr (kSplit) {
     ld = a.ldp;
@@ -1203,13 +1189,13 @@ bwd_dw_kernel(DwArgs a) {
     span = (a.H - h0) * ld - (a.v0 + vl0);
   }
   // Bytes per stored element: fp32 for partials, the accumulator and fp32 dW.
-  constexpr int kOut = (MODE == DW_DIRECT || MODE == DW_LAST) && !F32OUT ? 2 : 4;
-  float* const fdst = kSplit ? a.part : (kAccum && MODE != DW_LAST ? a.accw : nullptr);
+  constexpr int kOut = (STORE == DWS_DIRECT || STORE == DWS_LAST) && !F32OUT ? 2 : 4;
+  float* const fdst =
+      kSplit ? a.part : ((STORE == DWS_FIRST || STORE == DWS_MID) ? a.accw : nullptr);
   const __amdgpu_buffer_rsrc_t rs =
       fdst != nullptr ? make_rsrc(fdst + base, span * 4)
                       : make_rsrc(static_cast<char*>(a.gw) + base * kOut, span * kOut);
-  const __amdgpu_buffer_rsrc_t racc =
-      (MODE == DW_MID || MODE == DW_LAST) ? make_rsrc(a.accw + base, span * 4) : rs;
+  const __amdgpu_buffer_rsrc_t racc = kRead ? make_rsrc(a.accw + base, span * 4) : rs;
   // Quad transposes as in bwd_dx_kernel; vc is a multiple of 8.
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -1225,9 +1211,9 @@ bwd_dw_kernel(DwArgs a) {
                             acc[i][j][rq * 4 + 3]};
         if constexpr (kOut == 4) {
           f32x4_t v = quad_transpose_f32(x[0], x[1], x[2], x[3]);
-          if constexpr (MODE == DW_MID || MODE == DW_LAST) v += buf_load_f32x4(racc, vok ? e * 4 : kOOB);
+          if constexpr (kRead) v += buf_load_f32x4(racc, vok ? e * 4 : kOOB);
           buf_store_f32x4(v, rs, vok ? e * 4 : kOOB);
-        } else if constexpr (MODE == DW_LAST) {
+        } else if constexpr (kRead) {
           const f32x4_t v = quad_transpose_f32(x[0], x[1], x[2], x[3]) +
                             buf_load_f32x4(racc, vok ? e * 4 : kOOB);
           buf_store_u32x2(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rs,
@@ -1238,6 +1224,54 @@ bwd_dw_kernel(DwArgs a) {
         }
       }
     }
+  }
+}
+
+// C[h][v] = sum_t hidden[t][h] D[t][v] over the split's (or chunk's) tokens.
+template <int MODE, bool F32OUT>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                               amdgpu_waves_per_eu(2, 2)))
+bwd_dw_kernel(DwArgs a) {
+  FLCE_DECLARE_STAGES(sa, sb);
+  const int n = *a.nvalid;
+  bool last = true;
+  if constexpr (MODE == DW_CHUNK) {
+    if (!a.first && n <= a.r0) return;  // no valid token in this chunk
+    last = n <= a.r0 + a.rows;          // the chunk holds the last valid token
+  }
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int per = a.HT * a.VTc;
+  const int sp = L / per;
+  int ht, vt;
+  group_map(L - sp * per, a.HT, a.VTc, a.group, ht, vt);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
+  const int64_t h0 = (int64_t)ht * kTile, vl0 = (int64_t)vt * kTile;
+  const int kbeg = sp * a.kper;
+  // K blocks holding compacted tokens, from the launch's first row.
+  const int kval = (n - a.r0 + kBK - 1) / kBK;
+  const int klim = kval < a.kbn ? (kval > 0 ? kval : 0) : a.kbn;
+  const int kend = kbeg + a.kper < klim ? kbeg + a.kper : klim;
+  Acc acc;
+  {
+    Mainloop ml;
+    ml.run(sa, sb,
+           blocked_a(Strip{a.xtb + (int64_t)ht * a.kbn_a * kBlockElems, a.kbn_a}, a.ka0 + kbeg),
+           Strip{a.dvt + (int64_t)vt * a.kbn * kBlockElems, a.kbn}, kbeg, kend - kbeg, acc);
+  }
+  if constexpr (MODE == DW_SPLIT) {
+    dw_store_tile<DWS_SPLIT, F32OUT>(acc, a, h0, vl0, sp, wm, wn, lane);
+  } else if constexpr (MODE == DW_DIRECT) {
+    dw_store_tile<DWS_DIRECT, F32OUT>(acc, a, h0, vl0, sp, wm, wn, lane);
+  } else {
+    if (a.first && last)
+      dw_store_tile<DWS_DIRECT, F32OUT>(acc, a, h0, vl0, sp, wm, wn, lane);
+    else if (a.first)
+      dw_store_tile<DWS_FIRST, F32OUT>(acc, a, h0, vl0, sp, wm, wn, lane);
+    else if (last)
+      dw_store_tile<DWS_LAST, F32OUT>(acc, a, h0, vl0, sp, wm, wn, lane);
+    else
+      dw_store_tile<DWS_MID, F32OUT>(acc, a, h0, vl0, sp, wm, wn, lane);
   }
 }
 

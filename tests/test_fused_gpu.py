@@ -195,3 +195,29 @@ def test_fused_full_size(name):
     ign = torch.from_numpy(x["labels"] == wl.ignore_index).to(G.dev())
     if bool(ign.any()):
         assert torch.count_nonzero(out["grad_hidden"][ign]).item() == 0
+
+
+def test_fused_mostly_ignored_chunks():
+    """Most tokens ignored, one token block per chunk: only the first chunks
+    hold valid tokens, the chunk holding the last one writes dW and the empty
+    chunks exit. Against the oracle and the one-chunk run."""
+    wl = W.WORKLOADS["dw_split"]
+    x = W.make_inputs(wl)
+    rng = np.random.default_rng(7)
+    keep = np.sort(rng.choice(wl.N, size=300, replace=False))
+    labels = np.full(wl.N, wl.ignore_index, dtype=np.int64)
+    labels[keep] = x["labels"][keep]
+    x = dict(x, labels=labels)
+    t = G.upload(x)
+    grads = _grads(wl.N, "sum", 11)
+    outs = [_fused(t, wl, "sum", 0.0, grads, "bf16", c) for c in (256, 0)]
+    hf = W.bf16_bits_to_f32(x["hidden"])
+    wf = W.bf16_bits_to_f32(x["weight"])
+    dh, dw = oracle.backward(hf, wf, labels, ignore_index=wl.ignore_index, softcap_c=wl.softcap,
+                             reduction="sum", grad_logprob=grads[0], grad_entropy=grads[1],
+                             grad_uniform_ce=grads[2], grad_z_loss=grads[3], z_loss_scale=0.0)
+    for out in outs:
+        for what, ref in (("grad_hidden", dh), ("grad_weight", dw)):
+            e = G.rel_l2(out[what].float().cpu().numpy(), ref)
+            assert e <= G.GRAD_REL_L2, f"{what} rel L2 {e:.2e}"
+    assert torch.equal(outs[0]["lse"], outs[1]["lse"])
