@@ -902,9 +902,9 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
       d.inv_cap = capped ? 1.f / softcap : 0.f;
       FLCE_TRY(launch(K_FUSED_DLOGITS, st, [&] {
         if (capped)
-          fused_dlogits_kernel<true><<<tbc * p.VT, kThreads, 0, st>>>(d);
+          fused_dlogits_kernel<true><<<2 * tbc * p.VT, kDzThreads, 0, st>>>(d);
         else
-          fused_dlogits_kernel<false><<<tbc * p.VT, kThreads, 0, st>>>(d);
+          fused_dlogits_kernel<false><<<2 * tbc * p.VT, kDzThreads, 0, st>>>(d);
       }));
 
       DxArgs x{};

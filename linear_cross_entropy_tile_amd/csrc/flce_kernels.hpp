@@ -964,30 +964,47 @@ struct FusedDzArgs {
   float cap, inv_cap;
 };
 
-// Block (tb, vt) of a token chunk: reads the tile's stored z' - mref (the
-// lane layout of the MFMA accumulators, 8-byte pieces), adds mref back and
-// forms the logit gradient exactly as bwd_dlogits_kernel does from its
-// recomputed tile, writing dtv in place and dvt. Memory-bound: 2 bytes read
-// and 4 written per logit.
+// Half wm of tile (tb, vt) of a token chunk: vocabulary rows [128 wm, +128)
+// of the tile, all 256 tokens, by four waves wn = 0..3 laid out as in the
+// GEMM tile. The half tile's four dtv blocks (64 KiB, contiguous) come into
+// LDS by direct DMA (1 KiB per wave instruction); each lane reads its pieces
+// of the stored z' - mref in the lane layout of the MFMA accumulators, adds
+// mref back and forms the logit gradient exactly as bwd_dlogits_kernel does
+// from its recomputed tile, writing the dtv pieces back in place in LDS and
+// the dvt pieces directly; the four blocks then go back to dtv with 16-byte
+// stores (1 KiB per wave instruction). Memory-bound: 2 bytes read and 4
+// written per logit. 64 KiB of LDS per block leaves room for two blocks per
+// CU, so one block's transfers overlap the other's arithmetic.
+constexpr int kDzThreads = 256;
+
 template <bool CAP>
-__global__ void __launch_bounds__(kThreads) fused_dlogits_kernel(FusedDzArgs a) {
+__global__ void __launch_bounds__(kDzThreads) fused_dlogits_kernel(FusedDzArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[4 * kBlockBytes];
   const int left = (*a.nvalid - a.r0 + kTile - 1) / kTile;
   const int tbv = left < a.TB ? (left > 0 ? left : 0) : a.TB;
-  if ((int)blockIdx.x >= tbv * a.VT) return;
+  const int tile = (int)(blockIdx.x >> 1);
+  if (tile >= tbv * a.VT) return;
   int tb, vt;
-  group_map(xcd_remap(blockIdx.x, tbv * a.VT), tbv, a.VT, a.group, tb, vt);
+  group_map(xcd_remap(tile, tbv * a.VT), tbv, a.VT, a.group, tb, vt);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
+  const int wm = (int)(blockIdx.x & 1), wn = threadIdx.x >> 6;
   const int64_t n0 = (int64_t)tb * kTile;
   const int64_t vg0 = (int64_t)vt * kTile;
+  constexpr int kHalf = 4 * kBlockBytes;
   const __amdgpu_buffer_rsrc_t rtv = make_rsrc(
-      a.dtv + ((int64_t)tb * a.kbv + 8 * vt) * kBlockElems, 8 * (int64_t)kBlockBytes);
+      a.dtv + ((int64_t)tb * a.kbv + 8 * vt + 4 * wm) * kBlockElems, kHalf);
   const __amdgpu_buffer_rsrc_t rvt = make_rsrc(
       a.dvt + ((int64_t)vt * a.kbn + 8 * tb) * kBlockElems, 8 * (int64_t)kBlockBytes);
-  // Byte offset in the tile's dtv blocks of rows m0 .. m0+3 of token column n.
-  auto piece = [&](int i, int n, int m0) {
-    return (uint32_t)((4 * wm + i) * kBlockBytes + blk_byte(n, m0 & 31));
-  };
+#pragma unroll
+  for (int q = 0; q < kHalf / 1024 / 4; ++q) {
+    const int c = wn * (kHalf / 1024 / 4) + q;  // 1 KiB piece of this wave instruction
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rtv, (lds_void_t*)(lds + c * 1024), 16,
+                                             (uint32_t)(c * 1024 + lane * 16), 0, 0, 0);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  // Byte offset in LDS of rows m0 .. m0+3 (block i of the half) of token column n.
+  auto piece = [&](int i, int n, int m0) { return i * kBlockBytes + blk_byte(n, m0 & 31); };
   Acc acc;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -997,17 +1014,27 @@ __global__ void __launch_bounds__(kThreads) fused_dlogits_kernel(FusedDzArgs a) 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const u32x2_t v = buf_load_u32x2(rtv, piece(i, n, acc_row(wm, i, rq * 4, lane)));
+        const u32x2_t v =
+            *reinterpret_cast<const u32x2_t*>(lds + piece(i, n, acc_row(wm, i, rq * 4, lane)));
         acc[i][j][rq * 4 + 0] = __uint_as_float(v[0] << 16) + mw;
         acc[i][j][rq * 4 + 1] = __uint_as_float(v[0] & 0xFFFF0000u) + mw;
         acc[i][j][rq * 4 + 2] = __uint_as_float(v[1] << 16) + mw;
         acc[i][j][rq * 4 + 3] = __uint_as_float(v[1] & 0xFFFF0000u) + mw;
       }
   }
+  // Each lane rewrites only the pieces it read: no barrier between.
   dlogits_epilogue<CAP, false>(
       acc, a.coef, a.lab, a.rows, n0, vg0, a.V, DzCoef{0.f, 0.f, 0.f, 0.f, 0.f, a.cap, 0.f, a.inv_cap},
       wm, wn, lane,
-      [&](int i, int n, int m0, u32x2_t v) { buf_store_u32x2(v, rtv, piece(i, n, m0)); }, rvt);
+      [&](int i, int n, int m0, u32x2_t v) { *reinterpret_cast<u32x2_t*>(lds + piece(i, n, m0)) = v; },
+      rvt);
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kHalf / (kDzThreads * 16); ++q) {
+    const int off = (q * kDzThreads + (int)threadIdx.x) * 16;
+    __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t*>(lds + off), rtv,
+                                           (uint32_t)off, 0, 0);
+  }
 }
 
 // ---- backward: dH (+)= D W_chunk^T ---------------------------------------------
