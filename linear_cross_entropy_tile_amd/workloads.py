@@ -96,6 +96,16 @@ WORKLOADS = {
     "dw_split": Workload("dw_split", 4096, 256, 2048, seed=205, weight_std=0.1,
                          ignore="fraction", ignore_fraction=0.05,
                          grad_logprob=("normal",), grad_entropy=("normal",)),
+    # The library's size limits, one extreme at a time (weight std 1/sqrt(H)
+    # keeps the logits of order 1).
+    "max_vocab": Workload("max_vocab", 64, 64, (1 << 22) - 256, seed=206, weight_std=0.125,
+                          ignore="fraction", ignore_fraction=0.1,
+                          grad_logprob=("normal",), grad_entropy=("normal",)),
+    "max_tokens": Workload("max_tokens", 1 << 21, 64, 512, seed=207, weight_std=0.125,
+                           ignore="fraction", ignore_fraction=0.1,
+                           grad_logprob=("normal",), grad_entropy=("normal",)),
+    "max_hidden": Workload("max_hidden", 256, 1 << 20, 256, seed=208, weight_std=1.0 / 1024,
+                           grad_logprob=("normal",), grad_entropy=("normal",)),
 }
 
 
