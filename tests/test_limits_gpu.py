@@ -1,6 +1,8 @@
 """GPU parity at the library's size limits, one at a time: the largest
-vocabulary (V = 2^22 - 256), the most tokens (N = 2^21) and the widest hidden
-size (H = 2^20), through the recompute entry points the benchmark times.
+vocabulary (V = 2^22 - 256; 2^21 for the fused call), the most tokens
+(N = 2^21: 256 token chunks on the fused path) and the widest hidden size
+(H = 2^20), through the recompute entry points the benchmark times and
+through the fused forward + backward.
 
 The upstream gradients are kept on a sample of 48 tokens (first and last
 included) and set to zero elsewhere, so both gradients depend on the sampled
@@ -20,10 +22,13 @@ from linear_cross_entropy_tile_amd import flce, workloads as W
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("path", ["recompute", "fused"])
 @pytest.mark.parametrize("name", ["max_vocab", "max_tokens", "max_hidden"])
-def test_size_limits(name):
+def test_size_limits(name, path):
     wl = W.WORKLOADS[name]
-    print(f"[limits] {name} N={wl.N} H={wl.H} V={wl.V}", flush=True)
+    if path == "fused" and wl.V > 1 << 21:
+        wl = wl.with_(V=1 << 21)  # the fused call's vocabulary limit
+    print(f"[limits] {name} {path} N={wl.N} H={wl.H} V={wl.V}", flush=True)
     x = W.make_inputs(wl)
     rows = W.sample_indices(wl.N, 48, wl.seed + 1)
     keep = np.zeros(wl.N, dtype=bool)
@@ -31,7 +36,17 @@ def test_size_limits(name):
     for k in ("grad_logprob", "grad_entropy"):
         x[k] = np.where(keep, x[k], 0.0).astype(np.float32)
     t = G.upload(x)
-    got = G.run(wl, t, keep_grads_on_gpu=True)
+    if path == "recompute":
+        got = G.run(wl, t, keep_grads_on_gpu=True)
+    else:
+        out = flce.forward_backward(t["hidden"], t["weight"], t["labels"], t["grad_logprob"],
+                                    t["grad_entropy"], ignore_index=wl.ignore_index,
+                                    softcap=wl.softcap, reduction=wl.reduction)
+        torch.cuda.synchronize()
+        got = {k: out[k].cpu().numpy() for k in ("lse", "logprob", "entropy")}
+        got["grad_hidden"], got["grad_weight"] = out["grad_hidden"], out["grad_weight"]
+        got["invalid_labels"] = flce.flce_get_status(out["workspace"].data_ptr(),
+                                                     torch.cuda.current_stream().cuda_stream)
 
     hs = W.bf16_bits_to_f32(x["hidden"][rows])
     wf = W.bf16_bits_to_f32(x["weight"])
