@@ -299,8 +299,8 @@ flce_status_t flce_forward_backward(const void* hidden, const void* weight, cons
                                     float* reduced, void* grad_hidden, void* grad_weight,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* Reads the status word that the last flce_forward / flce_backward on this
- * workspace left, after synchronising `stream`. *invalid_labels (may be NULL)
+/* Reads the status word that the last flce_forward / flce_backward /
+ * flce_forward_backward on this workspace left, after synchronising `stream`. *invalid_labels (may be NULL)
  * receives the number of labels that were neither ignore_index nor in [0, V);
  * returns FLCE_ERR_INVALID_LABEL if that number is not 0, else FLCE_OK. */
 flce_status_t flce_get_status(const void* workspace, int64_t* invalid_labels, void* stream);

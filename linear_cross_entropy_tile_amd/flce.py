@@ -7,10 +7,11 @@ Two layers, both argument marshalling only:
   Python function per C entry point, same name, same arguments (device
   pointers and streams as integers, the options as ``FlceOptions``). A non-OK
   status raises ``FlceError``.
-* ``forward`` / ``backward``: take torch CUDA tensors, check dtypes and
-  layouts, allocate outputs and the workspace with torch (so torch's caching
-  allocator owns all memory), and call the C entry points on torch's current
-  stream. No arithmetic of the head happens here.
+* ``forward`` / ``backward`` / ``forward_backward`` (the fused call, for
+  upstream gradients known before the forward): take torch CUDA tensors,
+  check dtypes and layouts, allocate outputs and the workspace with torch (so
+  torch's caching allocator owns all memory), and call the C entry points on
+  torch's current stream. No arithmetic of the head happens here.
 
 The library is loaded on first use. There is no fallback: if libflce.so is
 missing or the device is not a GPU, calls raise.
