@@ -105,11 +105,13 @@ enum { FLCE_GRAD_BF16 = 0, FLCE_GRAD_F32 = 1 };
  * out-pointer may be NULL. The forward size is about 16 * N * ceil(V/256) +
  * 2 * N * H bytes (one partial softmax state per token and 256-wide
  * vocabulary tile, and a re-laid-out copy of hidden). The backward size holds
- * a bounded slice of the logit gradient in two bf16 layouts
- * (4 * 256*ceil(N/256) * Vc <= 1 GiB unless Vc is at its floor of 2048
- * columns; independent of V), re-laid-out copies of hidden and of a weight
- * slice, and, when the slice does not cover the whole vocabulary, an fp32
- * accumulator of N*H*4 bytes. */
+ * a slice of Vc vocabulary columns of the logit gradient in two bf16 layouts
+ * (4 * Np * Vc bytes, Np = 256*ceil(N/256); independent of V): Vc fills
+ * 1 GiB while that gives at least 16384 columns, is 16384 up to 4 GiB, and
+ * beyond that whatever fits in 4 GiB, down to a floor of 2048 columns. Then
+ * re-laid-out copies of hidden and of the weight slice, and, when the slice
+ * does not cover the whole vocabulary or dH is K-split, fp32 accumulators of
+ * N*H*4 bytes each. */
 flce_status_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int reduction,
                                   size_t* fwd_bytes, size_t* bwd_bytes);
 
