@@ -40,6 +40,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -81,15 +82,24 @@ def parse():
     return ap.parse_args()
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments and with whitespace collapsed: editing a
+    comment does not change a kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    """SHA-256 over the library's kernel and boundary sources, in a fixed order."""
+    """SHA-256 over the code (comments and blank space dropped) of the
+    library's kernel and boundary sources, in a fixed order."""
     files = sorted(glob.glob(os.path.join(ROOT, "linear_cross_entropy_tile_amd", "csrc", "*")))
     files.append(os.path.join(ROOT, "include", "flce.h"))
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 
