@@ -19,6 +19,10 @@ Prints one JSON line. Besides the throughput it reports:
                 MFMA peak;
   kernels       the same figures for every kernel kind;
   cpu_baseline  the float64 CPU oracle timed on a bounded token sample;
+  mfma_sustained  the bf16 MFMA rate the device sustains in the kernels' wave
+                tile with no memory traffic, on pseudo-random and on zero
+                operands (flce_probe_mfma_rate); roofline.frac_of_sustained is
+                the roofline kernel's rate against the random-operand figure;
   memory        peak device memory of one step vs the fp32 logits that a
                 materialising implementation needs;
   torch_ref     (optional) a materialising torch implementation of the same
@@ -363,6 +367,21 @@ def main():
                                        if args.path == "recompute"
                                        else {"fused": fused_ws.get("bytes")})},
     }
+    # The rate the matrix cores sustain here on varying data (context for
+    # the roofline fraction against the published peak).
+    probe_ws = torch.empty(256 * 512 * 4, dtype=torch.uint8, device=dev)
+    probe = lambda zero, steps: flce.flce_probe_mfma_rate(zero, steps, probe_ws.data_ptr(),
+                                                          probe_ws.numel(), stream)
+    probe(False, 20000)  # warm-up: let the clock settle under this load
+    sustained = {
+        "random_tflops": probe(False, 120000),
+        "zero_tflops": probe(True, 120000),
+        "what": "register-only 4 x 2 v_mfma_f32_32x32x16_bf16 wave tile, 2 waves per SIMD, "
+                "one block per CU, operands uniform in [-2, 2) or zero",
+    }
+    out["mfma_sustained"] = sustained
+    if out["roofline"]["achieved"]:
+        out["roofline"]["frac_of_sustained"] = out["roofline"]["achieved"] / sustained["random_tflops"]
     if args.path == "recompute" and args.alt_fused:
         print("[bench] fused path (gradient in the forward)", flush=True)
         fpeak = peak_of(step_fused)

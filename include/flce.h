@@ -325,6 +325,19 @@ int flce_profile_kinds(void);
  * launches and the summed duration (ms) of kernel kind `kind`. */
 flce_status_t flce_profile_read(int kind, const char** name, int64_t* launches, double* total_ms);
 
+/* Measurement hook, for context in benchmarks: the bf16 MFMA rate (TFLOP/s,
+ * in *tflops) that this device sustains in the GEMM kernels' wave tile with no
+ * memory traffic at all: one 512-thread block per CU (two waves per SIMD), each
+ * wave running `steps` (4 <= steps <= 2^24, rounded down to a multiple of 4)
+ * 16-wide K steps of 4 x 2 v_mfma_f32_32x32x16_bf16 on operands held in
+ * registers, pseudo-random bf16 in [-2, 2) (zero_operands = 0) or zeros (1).
+ * The published dense peak assumes a clock that the matrix cores hold on
+ * zero operands but not under the power they draw on varying data.
+ * workspace: device, at least 256 * 512 * 4 bytes (scratch for the results).
+ * Synchronises `stream`. */
+flce_status_t flce_probe_mfma_rate(int zero_operands, int64_t steps, double* tflops,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

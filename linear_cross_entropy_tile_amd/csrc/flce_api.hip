@@ -1234,6 +1234,37 @@ const char* flce_status_string(flce_status_t s) {
 
 int flce_version(void) { return 210; }
 
+flce_status_t flce_probe_mfma_rate(int zero_operands, int64_t steps, double* tflops,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (tflops == nullptr || workspace == nullptr) return FLCE_ERR_NULL_POINTER;
+  if (steps < 4 || steps > ((int64_t)1 << 24)) return FLCE_ERR_BAD_SHAPE;
+  const int blocks = kNumCUs;
+  if (workspace_bytes < (size_t)blocks * kThreads * 4) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int n = (int)(steps / 4 * 4);
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipEventCreate(&a) != hipSuccess) return FLCE_ERR_HIP;
+  if (hipEventCreate(&b) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    return FLCE_ERR_HIP;
+  }
+  float ms = 0.f;
+  bool ok = hipEventRecord(a, st) == hipSuccess;
+  if (ok) {
+    mfma_probe_kernel<<<blocks, kThreads, 0, st>>>(n, zero_operands != 0,
+                                                   static_cast<float*>(workspace));
+    ok = hipGetLastError() == hipSuccess && hipEventRecord(b, st) == hipSuccess &&
+         hipEventSynchronize(b) == hipSuccess && hipEventElapsedTime(&ms, a, b) == hipSuccess;
+  }
+  (void)hipEventDestroy(a);
+  (void)hipEventDestroy(b);
+  if (!ok || ms <= 0.f) return FLCE_ERR_HIP;
+  // Per wave and step: 4 x 2 MFMAs of 32 x 32 x 16 multiply-adds.
+  const double flops = (double)blocks * kWaves * (double)n * 8.0 * 2.0 * 32 * 32 * 16;
+  *tflops = flops / ((double)ms * 1e-3) / 1e12;
+  return FLCE_OK;
+}
+
 flce_status_t flce_profile_enable(int enable) {
   Profiler& P = prof();
   std::lock_guard<std::mutex> g(P.mu);

@@ -1320,6 +1320,78 @@ __global__ void __launch_bounds__(256) dw_reduce_kernel(const float* __restrict_
   }
 }
 
+// ---- measurement: the sustained MFMA rate ------------------------------------------
+
+// lowbias32, an integer mixer published with C. Wellons' hash-prospector:
+// a counter-based source of operand bits for the probe below.
+__device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// Eight bf16 values uniform in [-2, 2) from counter c (or zeros).
+__device__ __forceinline__ bf16x8_t probe_frag(uint32_t c, bool zero) {
+  u32x4_t w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t x = probe_hash(c * 8u + (uint32_t)(2 * e + h));
+      v[h] = zero ? 0.f : (float)(x >> 8) * (4.f / 16777216.f) - 2.f;
+    }
+    w[e] = pack_bf16x2(v[0], v[1]);
+  }
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+// Register-only throughput of the GEMM kernels' wave tile: `steps` 16-wide K
+// steps of 4 x 2 v_mfma_f32_32x32x16_bf16 per wave (two waves per SIMD, as in
+// the GEMM kernels), cycling through four operand sets held in registers; no
+// memory traffic in the loop. The accumulators are summed into out (one float
+// per thread) so that nothing is elided.
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                               amdgpu_waves_per_eu(2, 2)))
+mfma_probe_kernel(int steps, int zero, float* __restrict__ out) {
+  const uint32_t id = blockIdx.x * kThreads + threadIdx.x;
+  bf16x8_t a[4][4], b[4][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[s][i] = probe_frag(id * 24u + (uint32_t)(s * 6 + i), zero != 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[s][j] = probe_frag(id * 24u + (uint32_t)(s * 6 + 4 + j), zero != 0);
+  }
+  Acc acc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  for (int t = 0; t < steps; t += 4) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s][i], b[s][j], acc[i][j], 0, 0, 0);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += acc[i][j][r];
+  out[id] = sum;
+}
+
 // Writes zeros (used for empty inputs; a kernel rather than a memset so the
 // enqueued work is plain kernels only).
 __global__ void __launch_bounds__(256) fill_zero_kernel(uint32_t* __restrict__ p, int64_t n32) {

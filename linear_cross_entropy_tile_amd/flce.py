@@ -28,7 +28,7 @@ __all__ = [
     "flce_workspace_size", "flce_forward", "flce_backward", "flce_forward_ex",
     "flce_backward_ex", "flce_fused_workspace_size", "flce_forward_backward", "flce_get_status",
     "flce_status_string", "flce_version", "flce_profile_enable", "flce_profile_reset",
-    "flce_profile_kinds", "flce_profile_read", "profile_table",
+    "flce_profile_kinds", "flce_profile_read", "profile_table", "flce_probe_mfma_rate",
     "forward", "backward", "forward_backward", "workspace_bytes",
 ]
 
@@ -96,6 +96,8 @@ _SIG = {
     "flce_profile_kinds": (ctypes.c_int, []),
     "flce_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                          ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]),
+    "flce_probe_mfma_rate": (ctypes.c_int, [ctypes.c_int, _I64, ctypes.POINTER(ctypes.c_double),
+                                            _P, ctypes.c_size_t, _P]),
 }
 
 
@@ -262,6 +264,16 @@ def flce_profile_read(kind: int):
     _check(lib().flce_profile_read(kind, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms)),
            "flce_profile_read")
     return name.value.decode(), n.value, ms.value
+
+
+def flce_probe_mfma_rate(zero_operands: bool, steps: int, workspace, workspace_bytes,
+                         stream) -> float:
+    """Sustained bf16 MFMA TFLOP/s of the GEMM wave tile with no memory traffic
+    (synchronises the stream)."""
+    t = ctypes.c_double(0.0)
+    _check(lib().flce_probe_mfma_rate(1 if zero_operands else 0, steps, ctypes.byref(t), workspace,
+                                      workspace_bytes, stream), "flce_probe_mfma_rate")
+    return t.value
 
 
 def profile_table() -> dict:

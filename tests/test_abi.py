@@ -265,3 +265,13 @@ def test_fused_workspace_size():
             == flce.flce_fused_workspace_size(32768, 4096, 128256, o, 8192))
     with pytest.raises(flce.FlceError):
         flce.flce_fused_workspace_size(8, 8, (1 << 21) + 8, o, 0)
+
+
+def test_probe_mfma_rejects():
+    L = flce.lib()
+    t = ctypes.c_double(0.0)
+    assert L.flce_probe_mfma_rate(0, 1000, None, A, BIG, None) == 1
+    assert L.flce_probe_mfma_rate(0, 1000, ctypes.byref(t), None, BIG, None) == 1
+    assert L.flce_probe_mfma_rate(0, 2, ctypes.byref(t), A, BIG, None) == 2
+    assert L.flce_probe_mfma_rate(0, (1 << 24) + 4, ctypes.byref(t), A, BIG, None) == 2
+    assert L.flce_probe_mfma_rate(0, 1000, ctypes.byref(t), A, 1024, None) == 5
