@@ -1,0 +1,76 @@
+"""The autograd wrapper linear_cross_entropy against the float64 oracle: the
+two outputs under each reduction, and the gradients that torch's backward
+produces for a loss built from both outputs (tolerances as in the other
+parity tests)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gpu_helpers as G
+from linear_cross_entropy_tile_amd import workloads as W
+from linear_cross_entropy_tile_amd.function import linear_cross_entropy
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,reduction", [("odd_tails", "mean"), ("mean_ignore", "mean"),
+                                            ("tiny", "none"), ("dw_split", "sum")])
+def test_autograd_matches_oracle(name, reduction):
+    wl = W.WORKLOADS[name]
+    x = W.make_inputs(wl)
+    t = G.upload(x)
+    h = t["hidden"].clone().requires_grad_(True)
+    w = t["weight"].clone().requires_grad_(True)
+    lp, ent = linear_cross_entropy(h, w, t["labels"], reduction=reduction,
+                                   ignore_index=wl.ignore_index, softcap=wl.softcap)
+    rng = np.random.default_rng(wl.seed + 3)
+    if reduction == "none":
+        a = rng.standard_normal(wl.N).astype(np.float32)
+        b = rng.standard_normal(wl.N).astype(np.float32)
+        loss = (lp * torch.from_numpy(a).to(G.dev())).sum() + (ent * torch.from_numpy(b).to(G.dev())).sum()
+        ga, gb = a, b
+    else:
+        a, b = -1.0, 0.01  # a loss -logprob + 0.01 entropy
+        loss = a * lp + b * ent
+        ga, gb = np.array([a], np.float32), np.array([b], np.float32)
+    loss.backward()
+    torch.cuda.synchronize()
+    hf = W.bf16_bits_to_f32(x["hidden"])
+    wf = W.bf16_bits_to_f32(x["weight"])
+    fw = oracle.forward(hf, wf, x["labels"], ignore_index=wl.ignore_index, softcap_c=wl.softcap,
+                        reduction=reduction)
+    dh, dw = oracle.backward(hf, wf, x["labels"], ignore_index=wl.ignore_index,
+                             softcap_c=wl.softcap, reduction=reduction, grad_logprob=ga,
+                             grad_entropy=gb)
+    if reduction == "none":
+        assert G.stat_err(lp.detach().cpu().numpy(), fw["logprob"]) <= 1.0
+        assert G.stat_err(ent.detach().cpu().numpy(), fw["entropy"]) <= 1.0
+    else:
+        assert lp.dim() == 0 and ent.dim() == 0
+        assert G.stat_err([lp.item()], [fw[f"logprob_{reduction}"]]) <= 1.0
+        assert G.stat_err([ent.item()], [fw[f"entropy_{reduction}"]]) <= 1.0
+    assert h.grad.dtype == torch.bfloat16 and w.grad.dtype == torch.bfloat16
+    e = G.rel_l2(h.grad.float().cpu().numpy(), dh)
+    assert e <= G.GRAD_REL_L2, f"{name} grad_hidden rel L2 {e:.2e}"
+    e = G.rel_l2(w.grad.float().cpu().numpy(), dw)
+    assert e <= G.GRAD_REL_L2, f"{name} grad_weight rel L2 {e:.2e}"
+
+
+def test_autograd_one_output_used():
+    """Only the entropy enters the loss: the logprob gradient is None."""
+    wl = W.WORKLOADS["odd_tails"]
+    x = W.make_inputs(wl)
+    t = G.upload(x)
+    h = t["hidden"].clone().requires_grad_(True)
+    w = t["weight"].clone().requires_grad_(True)
+    _, ent = linear_cross_entropy(h, w, t["labels"], reduction="mean", ignore_index=wl.ignore_index)
+    ent.backward()
+    torch.cuda.synchronize()
+    hf = W.bf16_bits_to_f32(x["hidden"])
+    wf = W.bf16_bits_to_f32(x["weight"])
+    dh, dw = oracle.backward(hf, wf, x["labels"], ignore_index=wl.ignore_index, reduction="mean",
+                             grad_logprob=np.array([0.0], np.float32),
+                             grad_entropy=np.array([1.0], np.float32))
+    assert G.rel_l2(h.grad.float().cpu().numpy(), dh) <= G.GRAD_REL_L2
+    assert G.rel_l2(w.grad.float().cpu().numpy(), dw) <= G.GRAD_REL_L2
