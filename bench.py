@@ -18,6 +18,7 @@ Prints one JSON line. Besides the throughput it reports:
                 launch stream during the timed region) against the bf16 dense
                 MFMA peak;
   kernels       the same figures for every kernel kind;
+  fwd_ms, bwd_ms  flce_forward and flce_backward timed on their own;
   cpu_baseline  the float64 CPU oracle timed on a bounded token sample;
   mfma_sustained  the bf16 MFMA rate the device sustains in the kernels' wave
                 tile with no memory traffic, on pseudo-random and on zero
@@ -288,14 +289,20 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     P = {k: v.data_ptr() for k, v in t.items()}
 
-    def step_recompute():
+    def fwd_only():
         flce.flce_forward(P["hidden"], P["weight"], P["labels"], N, H, V, wl.ignore_index,
                           wl.softcap, red, lse.data_ptr(), lp.data_ptr(), ent.data_ptr(),
                           lpm.data_ptr(), entm.data_ptr(), wsf.data_ptr(), fbytes, stream)
+
+    def bwd_only():
         flce.flce_backward(P["hidden"], P["weight"], P["labels"], N, H, V, wl.ignore_index,
                            wl.softcap, red, lse.data_ptr(), ent.data_ptr(), P["grad_logprob"],
                            P["grad_entropy"], gh.data_ptr(), gw.data_ptr(), wsb.data_ptr(),
                            bbytes, stream)
+
+    def step_recompute():
+        fwd_only()
+        bwd_only()
 
     opt = flce.FlceOptions(wl.ignore_index, wl.softcap, red, 0.0, flce.FLCE_GRAD_BF16)
     reduced = torch.empty(4, **f32)
@@ -369,6 +376,10 @@ def main():
     }
     # The rate the matrix cores sustain here on varying data (context for
     # the roofline fraction against the published peak).
+    if args.path == "recompute":
+        # The step's two halves timed on their own (same stream, events).
+        out["fwd_ms"], _ = timed(fwd_only, args.steps, 1)
+        out["bwd_ms"], _ = timed(bwd_only, args.steps, 1)
     # Context measurements below never keep the line from being printed.
     try:
         probe_ws = torch.empty(256 * 512 * 4, dtype=torch.uint8, device=dev)
