@@ -255,7 +255,7 @@ def peak_of(step):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
