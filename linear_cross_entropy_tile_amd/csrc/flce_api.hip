@@ -381,6 +381,58 @@ flce_status_t pack_cols(int kind, const void* src, int64_t R, int64_t K, int64_t
   });
 }
 
+// dH tiles in `mode` (DX_ONLY / FIRST / MID / LAST), bf16 or fp32 output.
+flce_status_t launch_dx(const DxArgs& x, int mode, bool f32, int grid, hipStream_t st) {
+  return launch(K_BWD_DX, st, [&] {
+    switch (mode * 2 + (f32 ? 1 : 0)) {
+      case DX_ONLY * 2: bwd_dx_kernel<DX_ONLY, false><<<grid, kThreads, 0, st>>>(x); break;
+      case DX_ONLY * 2 + 1: bwd_dx_kernel<DX_ONLY, true><<<grid, kThreads, 0, st>>>(x); break;
+      case DX_FIRST * 2: bwd_dx_kernel<DX_FIRST, false><<<grid, kThreads, 0, st>>>(x); break;
+      case DX_FIRST * 2 + 1: bwd_dx_kernel<DX_FIRST, true><<<grid, kThreads, 0, st>>>(x); break;
+      case DX_MID * 2: bwd_dx_kernel<DX_MID, false><<<grid, kThreads, 0, st>>>(x); break;
+      case DX_MID * 2 + 1: bwd_dx_kernel<DX_MID, true><<<grid, kThreads, 0, st>>>(x); break;
+      case DX_LAST * 2: bwd_dx_kernel<DX_LAST, false><<<grid, kThreads, 0, st>>>(x); break;
+      default: bwd_dx_kernel<DX_LAST, true><<<grid, kThreads, 0, st>>>(x); break;
+    }
+  });
+}
+
+// grad_hidden rows of compacted rows [r0, r0 + rows) from the K-split dH
+// accumulators (`splits` of rows x H each).
+flce_status_t launch_dx_finalize(const float* acc, int splits, int64_t rows, int64_t H,
+                                 const int32_t* idx, const int32_t* nvalid, int64_t r0, void* gh,
+                                 bool f32, hipStream_t st) {
+  const int64_t work = rows * (H / 4);
+  const int fb = (int)(ceil_div(work, 256) < 16384 ? ceil_div(work, 256) : 16384);
+  return launch(K_DX_FINALIZE, st, [&] {
+    if (f32)
+      dx_finalize_kernel<true><<<fb, 256, 0, st>>>(acc, splits, rows, H, idx, nvalid, r0, gh);
+    else
+      dx_finalize_kernel<false><<<fb, 256, 0, st>>>(acc, splits, rows, H, idx, nvalid, r0, gh);
+  });
+}
+
+// The reduced outputs (reduced[k] may be null) from the nb combine blocks'
+// sums; header[1] is the valid count for the mean.
+flce_status_t launch_fwd_reduce(const double4* bsum, int nb, const int32_t* header, bool mean,
+                                float* const (&reduced)[4], hipStream_t st) {
+  return launch(K_FWD_REDUCE, st, [&] {
+    fwd_reduce_kernel<<<1, 256, 0, st>>>(bsum, nb, header, mean ? 1 : 0, reduced[0], reduced[1],
+                                         reduced[2], reduced[3]);
+  });
+}
+
+// Zero rows (row_bytes each) of `out` for ignored or invalid tokens.
+flce_status_t launch_zero_ignored(const int64_t* labels, int64_t N, int64_t V_total,
+                                  int64_t ignore_index, void* out, int64_t row_bytes,
+                                  hipStream_t st) {
+  const int zb = (int)(N < 16384 ? N : 16384);
+  return launch(K_FILL, st, [&] {
+    zero_ignored_rows_kernel<<<zb, 256, 0, st>>>(labels, N, V_total, ignore_index,
+                                                 static_cast<char*>(out), row_bytes);
+  });
+}
+
 }  // namespace
 
 extern "C" {
@@ -514,13 +566,9 @@ flce_status_t forward_impl(const void* hidden, const void* weight, const int64_t
       fwd_combine_kernel<<<nb, 64 * kCombineWaves, 0, st>>>(c);
     }));
   }
-  if (reduce) {
-    const int mean = reduction == FLCE_REDUCTION_MEAN;
-    FLCE_TRY(launch(K_FWD_REDUCE, st, [&] {
-      fwd_reduce_kernel<<<1, 256, 0, st>>>(bsum, N > 0 ? nb : 0, header, mean, reduced[0],
-                                           reduced[1], reduced[2], reduced[3]);
-    }));
-  }
+  if (reduce)
+    FLCE_TRY(launch_fwd_reduce(bsum, N > 0 ? nb : 0, header, reduction == FLCE_REDUCTION_MEAN,
+                               reduced, st));
   return FLCE_OK;
 }
 
@@ -584,12 +632,8 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
   pa.header = header;
   FLCE_TRY(launch(K_BWD_PREP, st, [&] { bwd_prep_kernel<<<1, 1024, 0, st>>>(pa); }));
   // Rows of ignored tokens are never written by the compacted contractions.
-  const int zb = (int)(N < 16384 ? N : 16384);
-  FLCE_TRY(launch(K_FILL, st, [&] {
-    zero_ignored_rows_kernel<<<zb, 256, 0, st>>>(labels, N, V_total, o.ignore_index,
-                                                 static_cast<char*>(grad_hidden),
-                                                 (int64_t)out_elem * H);
-  }));
+  FLCE_TRY(launch_zero_ignored(labels, N, V_total, o.ignore_index, grad_hidden,
+                               (int64_t)out_elem * H, st));
 
   // Blocked operands, over the valid tokens compacted in token order: hidden
   // (tokens x H) for the recompute, hidden^T (H x tokens) for dW, and per
@@ -658,37 +702,9 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
                            : (p.nchunks == 1 ? DX_ONLY
                                              : (c == 0 ? DX_FIRST
                                                        : (c == p.nchunks - 1 ? DX_LAST : DX_MID)));
-    const int gx = p.TB * p.HT * p.dx_splits;
-    FLCE_TRY(launch(K_BWD_DX, st, [&] {
-      if (f32) {
-        switch (mode) {
-          case DX_ONLY: bwd_dx_kernel<DX_ONLY, true><<<gx, kThreads, 0, st>>>(x); break;
-          case DX_FIRST: bwd_dx_kernel<DX_FIRST, true><<<gx, kThreads, 0, st>>>(x); break;
-          case DX_MID: bwd_dx_kernel<DX_MID, true><<<gx, kThreads, 0, st>>>(x); break;
-          default: bwd_dx_kernel<DX_LAST, true><<<gx, kThreads, 0, st>>>(x); break;
-        }
-      } else {
-        switch (mode) {
-          case DX_ONLY: bwd_dx_kernel<DX_ONLY, false><<<gx, kThreads, 0, st>>>(x); break;
-          case DX_FIRST: bwd_dx_kernel<DX_FIRST, false><<<gx, kThreads, 0, st>>>(x); break;
-          case DX_MID: bwd_dx_kernel<DX_MID, false><<<gx, kThreads, 0, st>>>(x); break;
-          default: bwd_dx_kernel<DX_LAST, false><<<gx, kThreads, 0, st>>>(x); break;
-        }
-      }
-    }));
-
-    if (split && c == p.nchunks - 1) {
-      const int64_t work = N * (H / 4);
-      const int fb = (int)(ceil_div(work, 256) < 16384 ? ceil_div(work, 256) : 16384);
-      FLCE_TRY(launch(K_DX_FINALIZE, st, [&] {
-        if (f32)
-          dx_finalize_kernel<true><<<fb, 256, 0, st>>>(acc, p.dx_splits, N, H, idx, nvalid, 0,
-                                                       grad_hidden);
-        else
-          dx_finalize_kernel<false><<<fb, 256, 0, st>>>(acc, p.dx_splits, N, H, idx, nvalid, 0,
-                                                        grad_hidden);
-      }));
-    }
+    FLCE_TRY(launch_dx(x, mode, f32, p.TB * p.HT * p.dx_splits, st));
+    if (split && c == p.nchunks - 1)
+      FLCE_TRY(launch_dx_finalize(acc, p.dx_splits, N, H, idx, nvalid, 0, grad_hidden, f32, st));
 
     DwArgs w{};
     w.xtb = xtb;
@@ -807,12 +823,8 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
   if (N == 0) {
     FLCE_TRY(zero_fill(grad_weight, out_elem * (size_t)H * (size_t)V, st));
   } else {
-    const int zb = (int)(N < 16384 ? N : 16384);
-    FLCE_TRY(launch(K_FILL, st, [&] {
-      zero_ignored_rows_kernel<<<zb, 256, 0, st>>>(labels, N, V, o.ignore_index,
-                                                   static_cast<char*>(grad_hidden),
-                                                   (int64_t)out_elem * H);
-    }));
+    FLCE_TRY(launch_zero_ignored(labels, N, V, o.ignore_index, grad_hidden,
+                                 (int64_t)out_elem * H, st));
     // Blocked operands over the valid tokens compacted in token order: hidden
     // (K = H) for the logit tiles, hidden^T (K = tokens) for dW, and the
     // weight (H rows, K = vocabulary) for dH.
@@ -924,33 +936,13 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
       x.nvalid = nvalid;
       x.splits = f.dx_splits;
       x.r0 = r0;
+      // One vocabulary range per chunk: the output directly, or K-split
+      // accumulators and their sum.
       const bool split = f.dx_splits > 1;
-      const int gx = tbc * p.HT * f.dx_splits;
-      FLCE_TRY(launch(K_BWD_DX, st, [&] {
-        if (split) {
-          if (f32)
-            bwd_dx_kernel<DX_FIRST, true><<<gx, kThreads, 0, st>>>(x);
-          else
-            bwd_dx_kernel<DX_FIRST, false><<<gx, kThreads, 0, st>>>(x);
-        } else {
-          if (f32)
-            bwd_dx_kernel<DX_ONLY, true><<<gx, kThreads, 0, st>>>(x);
-          else
-            bwd_dx_kernel<DX_ONLY, false><<<gx, kThreads, 0, st>>>(x);
-        }
-      }));
-      if (split) {
-        const int64_t work = rows * (H / 4);
-        const int fb = (int)(ceil_div(work, 256) < 16384 ? ceil_div(work, 256) : 16384);
-        FLCE_TRY(launch(K_DX_FINALIZE, st, [&] {
-          if (f32)
-            dx_finalize_kernel<true><<<fb, 256, 0, st>>>(dxacc, f.dx_splits, rows, H, idx + r0,
-                                                         nvalid, r0, grad_hidden);
-          else
-            dx_finalize_kernel<false><<<fb, 256, 0, st>>>(dxacc, f.dx_splits, rows, H, idx + r0,
-                                                          nvalid, r0, grad_hidden);
-        }));
-      }
+      FLCE_TRY(launch_dx(x, split ? DX_FIRST : DX_ONLY, f32, tbc * p.HT * f.dx_splits, st));
+      if (split)
+        FLCE_TRY(launch_dx_finalize(dxacc, f.dx_splits, rows, H, idx + r0, nvalid, r0,
+                                    grad_hidden, f32, st));
 
       DwArgs w{};
       w.xtb = xtb;
@@ -989,11 +981,9 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
     }
   }
   if (reduce) {
-    const int mean = reduction == FLCE_REDUCTION_MEAN;
-    FLCE_TRY(launch(K_FWD_REDUCE, st, [&] {
-      fwd_reduce_kernel<<<1, 256, 0, st>>>(bsum, N > 0 ? nb : 0, header, mean, reduced,
-                                           reduced + 1, reduced + 2, reduced + 3);
-    }));
+    float* const red[4] = {reduced, reduced + 1, reduced + 2, reduced + 3};
+    FLCE_TRY(launch_fwd_reduce(bsum, N > 0 ? nb : 0, header, reduction == FLCE_REDUCTION_MEAN,
+                               red, st));
   }
   return FLCE_OK;
 }
@@ -1177,13 +1167,10 @@ flce_status_t flce_merge_shards(const float* states, const float* label_logits, 
     }));
   }
   if (reduce) {
-    const int mean = opt->reduction == FLCE_REDUCTION_MEAN;
-    FLCE_TRY(launch(K_FWD_REDUCE, st, [&] {
-      fwd_reduce_kernel<<<1, 256, 0, st>>>(bsum, N > 0 ? nb : 0, header, mean, reduced,
-                                           reduced ? reduced + 1 : nullptr,
-                                           reduced ? reduced + 2 : nullptr,
-                                           reduced ? reduced + 3 : nullptr);
-    }));
+    float* const red[4] = {reduced, reduced ? reduced + 1 : nullptr,
+                           reduced ? reduced + 2 : nullptr, reduced ? reduced + 3 : nullptr};
+    FLCE_TRY(launch_fwd_reduce(bsum, N > 0 ? nb : 0, header,
+                               opt->reduction == FLCE_REDUCTION_MEAN, red, st));
   }
   return FLCE_OK;
 }
