@@ -53,6 +53,18 @@ Readings taken where the pages are silent or ambiguous:
       uniform distribution; the smoothed cross-entropy with weight eps is
       (1 - eps) * (-logprob) + eps * uniform_ce, which is how
       torch.nn.functional.cross_entropy defines label_smoothing.
+  R10 Target (class) weights. The [liger-551] review lists target weights
+      among the fused options and, for the weighted case, normalises by the
+      sum of the weights of the non-ignored tokens instead of their count.
+      Taken here as: an optional weight per class; a valid token i carries
+      omega_i = class_weight[y_i]; under "mean" every output's mean is
+      sum_i omega_i x_i / sum_i omega_i (0 when that sum is 0), under "sum"
+      it is sum_i omega_i x_i, and the scalar upstream gradients reach token i
+      multiplied by omega_i (and divided by the weight sum under "mean"). This
+      is torch.nn.functional.cross_entropy's ``weight`` for the cross-entropy
+      term, and the same per-token weight for the entropy and the auxiliary
+      outputs. Per-token vectors stay unweighted; under "none" no weights are
+      taken (a caller folds them into its per-token gradients).
 """
 from __future__ import annotations
 
@@ -139,22 +151,39 @@ _REDUCTIONS = ("none", "mean", "sum")
 _OUTPUTS = ("logprob", "entropy", "uniform_ce", "z_loss")
 
 
+def _token_weights(labels, valid, reduction, class_weight):
+    """omega_i = class_weight[y_i] on valid tokens, 1 without class weights,
+    0 on ignored tokens (reading R10)."""
+    if class_weight is None:
+        return valid.astype(np.float64)
+    if reduction == "none":
+        raise ValueError("class weights apply to the 'mean' and 'sum' reductions (reading R10)")
+    cw = _as_f64(class_weight).reshape(-1)
+    om = np.zeros(labels.shape[0])
+    om[valid] = cw[labels[valid]]
+    return om
+
+
 def forward(hidden, weight, labels, ignore_index=-100, softcap_c=0.0,
-            reduction="none", z_loss_scale=0.0, row_block=_ROW_BLOCK):
+            reduction="none", z_loss_scale=0.0, row_block=_ROW_BLOCK, class_weight=None):
     """Per-token lse, logprob, entropy, uniform_ce and z_loss, plus their
     reductions under "mean" (keys ``<output>_mean``) and "sum" (``<output>_sum``).
 
     [verl-462] "Equivalent compute logic" (lse and entropy per token;
     logprobs = -cross_entropy) with the cap of [liger-127], the ignore rule and
     the mean of [liger-551] (readings R1 to R4), per-token outputs under
-    "none" as in [liger-435] Summary, the sum of R7 and the two auxiliary
-    outputs of R8 and R9.
+    "none" as in [liger-435] Summary, the sum of R7, the two auxiliary
+    outputs of R8 and R9 and the class weights of R10 (``weight_sum`` is
+    the weight of the valid tokens, n without class weights).
     """
     if reduction not in _REDUCTIONS:
         raise ValueError("reduction must be 'none', 'mean' or 'sum'")
     N = hidden.shape[0]
     V = weight.shape[1]
     labels, valid = _valid_mask(labels, V, ignore_index)
+    if class_weight is not None and _as_f64(class_weight).size != V:
+        raise ValueError("class_weight needs one weight per class")
+    omega = _token_weights(labels, valid, reduction, class_weight)
     w = _as_f64(weight)
     lse = np.zeros(N)
     lp = np.zeros(N)
@@ -173,27 +202,30 @@ def forward(hidden, weight, labels, ignore_index=-100, softcap_c=0.0,
         uce[rows] = l_ - zc.mean(axis=1)
     zl = z_loss_scale * lse * lse
     n = int(valid.sum())
+    wsum = float(omega[valid].sum())
     out = {"lse": lse, "logprob": lp, "entropy": ent, "uniform_ce": uce, "z_loss": zl,
-           "n_valid": n}
+           "n_valid": n, "weight_sum": wsum}
     for name in _OUTPUTS:
-        tot = float(out[name][valid].sum())
+        tot = float((omega[valid] * out[name][valid]).sum())
         if reduction == "mean":
-            out[name + "_mean"] = tot / n if n else 0.0
+            out[name + "_mean"] = tot / wsum if wsum != 0.0 else 0.0
         elif reduction == "sum":
             out[name + "_sum"] = tot
     return out
 
 
-def _token_grads(labels, valid, reduction, *grads):
+def _token_grads(labels, valid, reduction, class_weight, *grads):
     """Per-token upstream gradients of the outputs, in the order given.
 
     "none": one value per token ([liger-435], "Why we pass gradient to
     output.backward()"); None means zero. "mean": the scalar gradient of each
-    mean, divided by n on valid tokens (reading R3). "sum": the scalar
-    gradient of each sum (reading R7). Ignored tokens get 0.
+    mean, times omega_i / sum omega on valid tokens (omega_i = 1 without class
+    weights, so 1/n: readings R3, R10). "sum": the scalar gradient of each
+    sum, times omega_i (readings R7, R10). Ignored tokens get 0.
     """
     N = labels.shape[0]
-    n = int(valid.sum())
+    omega = _token_weights(labels, valid, reduction, class_weight)
+    wsum = float(omega[valid].sum())
 
     def expand(g):
         if g is None:
@@ -206,8 +238,8 @@ def _token_grads(labels, valid, reduction, *grads):
         if g.size != 1:
             raise ValueError("reduction='%s' needs one scalar gradient" % reduction)
         if reduction == "sum":
-            return np.full(N, g[0])
-        return np.full(N, g[0] / n if n else 0.0)
+            return g[0] * omega
+        return g[0] * omega / wsum if wsum != 0.0 else np.zeros(N)
 
     out = []
     for g in grads:
@@ -252,7 +284,7 @@ def _block_dz(hidden, w, labels, rows, grads, softcap_c, z_loss_scale):
 def backward(hidden, weight, labels, ignore_index=-100, softcap_c=0.0,
              reduction="none", grad_logprob=None, grad_entropy=None,
              grad_uniform_ce=None, grad_z_loss=None, z_loss_scale=0.0,
-             row_block=_ROW_BLOCK):
+             row_block=_ROW_BLOCK, class_weight=None):
     """dHidden [N,H] and dWeight [H,V] in float64.
 
     Recomputes the logits of each row block, forms dlogits (see ``dlogits``)
@@ -262,7 +294,7 @@ def backward(hidden, weight, labels, ignore_index=-100, softcap_c=0.0,
     N, H = hidden.shape
     V = weight.shape[1]
     labels, valid = _valid_mask(labels, V, ignore_index)
-    grads = _token_grads(labels, valid, reduction, grad_logprob, grad_entropy,
+    grads = _token_grads(labels, valid, reduction, class_weight, grad_logprob, grad_entropy,
                          grad_uniform_ce, grad_z_loss)
     w = _as_f64(weight)
     dh = np.zeros((N, H))
@@ -280,12 +312,12 @@ def backward(hidden, weight, labels, ignore_index=-100, softcap_c=0.0,
 
 def dhidden_rows(hidden, weight, labels, rows, ignore_index=-100, softcap_c=0.0,
                  reduction="none", grad_logprob=None, grad_entropy=None,
-                 grad_uniform_ce=None, grad_z_loss=None, z_loss_scale=0.0):
+                 grad_uniform_ce=None, grad_z_loss=None, z_loss_scale=0.0, class_weight=None):
     """Rows ``rows`` of dHidden. A row of dH depends only on its own token
     (and on n under "mean", so all labels are passed)."""
     V = weight.shape[1]
     labels, valid = _valid_mask(labels, V, ignore_index)
-    grads = _token_grads(labels, valid, reduction, grad_logprob, grad_entropy,
+    grads = _token_grads(labels, valid, reduction, class_weight, grad_logprob, grad_entropy,
                          grad_uniform_ce, grad_z_loss)
     rows = np.asarray(rows, dtype=np.int64)
     out = np.zeros((rows.size, hidden.shape[1]))
@@ -300,7 +332,7 @@ def dhidden_rows(hidden, weight, labels, rows, ignore_index=-100, softcap_c=0.0,
 def dweight_columns(hidden, weight, labels, cols, ignore_index=-100, softcap_c=0.0,
                     reduction="none", grad_logprob=None, grad_entropy=None,
                     grad_uniform_ce=None, grad_z_loss=None, z_loss_scale=0.0,
-                    row_block=_ROW_BLOCK):
+                    row_block=_ROW_BLOCK, class_weight=None):
     """Columns ``cols`` of dWeight, i.e. dW[:, cols] = hidden^T @ dZ[:, cols].
 
     Each column sums over every token, and each token's dZ needs its full
@@ -308,7 +340,7 @@ def dweight_columns(hidden, weight, labels, cols, ignore_index=-100, softcap_c=0
     N, H = hidden.shape
     V = weight.shape[1]
     labels, valid = _valid_mask(labels, V, ignore_index)
-    grads = _token_grads(labels, valid, reduction, grad_logprob, grad_entropy,
+    grads = _token_grads(labels, valid, reduction, class_weight, grad_logprob, grad_entropy,
                          grad_uniform_ce, grad_z_loss)
     cols = np.asarray(cols, dtype=np.int64)
     w = _as_f64(weight)

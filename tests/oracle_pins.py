@@ -9,8 +9,8 @@ Sources of truth used here, none of which is the oracle's own code path:
     logits, zero-weight gradient);
   * invariants of softmax, entropy and the tanh cap;
   * torch float64 library routines on the CPU (logsumexp, cross_entropy with
-    ignore_index, reductions and label_smoothing, Categorical.entropy,
-    autograd);
+    ignore_index, reductions, label_smoothing and class weights,
+    Categorical.entropy, autograd);
   * central finite differences of the oracle's forward.
 """
 from __future__ import annotations
@@ -428,7 +428,158 @@ def pin_aux_finite_differences():
     return worst, TOL_FD
 
 
+# ---------------------------------------------------------------- class weights (reading R10)
+
+def _class_weights(seed, V, zero=()):
+    cw = np.random.default_rng(seed).uniform(0.2, 3.0, size=V)
+    for j in zero:
+        cw[j] = 0.0
+    return cw
+
+
+def pin_library_class_weights():
+    """Class weights: logprob_mean = -F.cross_entropy(weight=cw, 'mean') and
+    logprob_sum = -F.cross_entropy(weight=cw, 'sum') (float64), cap off and
+    on, with ignored tokens; the weight sum is sum_i cw[y_i] over valid
+    tokens."""
+    err = 0.0
+    for seed, c in ((70, 0.0), (71, 2.2)):
+        h, w, y, _ = _rand_case(seed, N=11, H=6, V=10, wstd=1.1, ignore_rows=(1, 7), c=c)
+        cw = _class_weights(seed, 10)
+        z, _, _, _ = _torch_forward(h, w, y, c)
+        yt = torch.as_tensor(y)
+        cwt = torch.as_tensor(cw)
+        for red in ("mean", "sum"):
+            out = O.forward(h, w, y, softcap_c=c, reduction=red, class_weight=cw)
+            ref = F.cross_entropy(z, yt, weight=cwt, ignore_index=-100, reduction=red).item()
+            err = max(err, abs(out["logprob_" + red] + ref))
+        valid = y != -100
+        err = max(err, abs(out["weight_sum"] - cw[y[valid]].sum()))
+    return err, TOL_LIB
+
+
+def _masked_labels(y, cw):
+    """Labels whose class weight is 0 turned into ignore_index."""
+    ym = y.copy()
+    v = ym != -100
+    ym[v & (cw[np.where(v, ym, 0)] == 0.0)] = -100
+    return ym
+
+
+def pin_class_weights_as_mask():
+    """0/1 class weights give exactly the unweighted results with the
+    weight-0 classes' tokens ignored (all four reduced outputs and both
+    gradients, mean and sum); a constant weight k leaves every mean unchanged
+    and multiplies every sum by k."""
+    err = 0.0
+    for seed, c in ((72, 0.0), (73, 1.8)):
+        h, w, y, _ = _rand_case(seed, N=12, H=5, V=6, wstd=1.0, ignore_rows=(9,), c=c)
+        y[:6] = np.arange(6)          # every class occurs
+        mask = np.array([1.0, 0.0, 1.0, 1.0, 0.0, 1.0])
+        ym = _masked_labels(y, mask)
+        names = ("logprob", "entropy", "uniform_ce", "z_loss")
+        g = [np.array([0.8]), np.array([-1.1]), np.array([0.3]), np.array([0.5])]
+        for red in ("mean", "sum"):
+            a = O.forward(h, w, y, softcap_c=c, reduction=red, z_loss_scale=0.2, class_weight=mask)
+            b = O.forward(h, w, ym, softcap_c=c, reduction=red, z_loss_scale=0.2)
+            err = max(err, max(abs(a[k + "_" + red] - b[k + "_" + red]) for k in names))
+            kw = dict(softcap_c=c, reduction=red, grad_logprob=g[0], grad_entropy=g[1],
+                      grad_uniform_ce=g[2], grad_z_loss=g[3], z_loss_scale=0.2)
+            dha, dwa = O.backward(h, w, y, class_weight=mask, **kw)
+            dhb, dwb = O.backward(h, w, ym, **kw)
+            err = max(err, np.abs(dha - dhb).max(), np.abs(dwa - dwb).max())
+            k = 2.5
+            cst = np.full(6, k)
+            a = O.forward(h, w, y, softcap_c=c, reduction=red, z_loss_scale=0.2, class_weight=cst)
+            b = O.forward(h, w, y, softcap_c=c, reduction=red, z_loss_scale=0.2)
+            f = 1.0 if red == "mean" else k
+            err = max(err, max(abs(a[n + "_" + red] - f * b[n + "_" + red]) for n in names))
+    return err, TOL_CLOSED
+
+
+def pin_library_class_weight_grads():
+    """Gradients vs torch autograd (float64) of
+    g * -F.cross_entropy(weight=cw, ignore_index) + e * (class-weighted
+    entropy), mean and sum, cap off and on."""
+    err = 0.0
+    for seed, c, red in ((74, 0.0, "mean"), (75, 2.0, "mean"), (76, 1.5, "sum")):
+        h, w, y, _ = _rand_case(seed, N=7, H=4, V=8, wstd=1.0, ignore_rows=(3,), c=c)
+        cw = _class_weights(seed, 8, zero=(int(y[0]),))
+        ht = torch.tensor(h, requires_grad=True)
+        wt = torch.tensor(w, requires_grad=True)
+        z = ht @ wt
+        if c > 0:
+            z = c * torch.tanh(z / c)
+        yt = torch.as_tensor(y)
+        valid = yt != -100
+        om = torch.where(valid, torch.as_tensor(cw)[torch.where(valid, yt, 0)], 0.0)
+        ce = F.cross_entropy(z, yt, weight=torch.as_tensor(cw), ignore_index=-100, reduction=red)
+        ent = (torch.distributions.Categorical(logits=z).entropy() * om).sum()
+        if red == "mean":
+            ent = ent / om.sum()
+        g, e = 0.9, -1.4
+        (-g * ce + e * ent).backward()
+        dh, dw = O.backward(h, w, y, softcap_c=c, reduction=red, grad_logprob=np.array([g]),
+                            grad_entropy=np.array([e]), class_weight=cw)
+        scale = max(np.abs(ht.grad.numpy()).max(), np.abs(wt.grad.numpy()).max())
+        err = max(err, np.abs(dh - ht.grad.numpy()).max() / scale,
+                  np.abs(dw - wt.grad.numpy()).max() / scale)
+    return err, TOL_LIB
+
+
+def pin_class_weight_finite_differences():
+    """Central differences of the class-weighted objective (mean and sum, cap
+    off and on, an ignored token, z-loss) vs the backward."""
+    worst = 0.0
+    step = 1e-6
+    names = ("logprob", "entropy", "uniform_ce", "z_loss")
+    for seed, c, red in ((77, 0.0, "mean"), (78, 2.0, "sum")):
+        h, w, y, _ = _rand_case(seed, N=4, H=3, V=5, wstd=1.0, ignore_rows=(1,), c=c)
+        cw = _class_weights(seed, 5)
+        rng = np.random.default_rng(seed + 3)
+        gs = [rng.standard_normal(1) for _ in range(4)]
+
+        def obj():
+            out = O.forward(h, w, y, softcap_c=c, reduction=red, z_loss_scale=0.4, class_weight=cw)
+            return float(sum(g[0] * out[k + "_" + red] for g, k in zip(gs, names)))
+
+        dh, dw = O.backward(h, w, y, softcap_c=c, reduction=red, grad_logprob=gs[0],
+                            grad_entropy=gs[1], grad_uniform_ce=gs[2], grad_z_loss=gs[3],
+                            z_loss_scale=0.4, class_weight=cw)
+        fdh = np.zeros_like(h)
+        fdw = np.zeros_like(w)
+        for arr, out in ((h, fdh), (w, fdw)):
+            for idx in np.ndindex(arr.shape):
+                old = arr[idx]
+                arr[idx] = old + step
+                fp = obj()
+                arr[idx] = old - step
+                fm = obj()
+                arr[idx] = old
+                out[idx] = (fp - fm) / (2 * step)
+        scale = max(np.abs(fdh).max(), np.abs(fdw).max())
+        worst = max(worst, np.abs(dh - fdh).max() / scale, np.abs(dw - fdw).max() / scale)
+    return worst, TOL_FD
+
+
+def pin_class_weights_zero_sum():
+    """Every valid token's class weight 0: the means are 0 and the gradients 0
+    (as for a mean over no tokens)."""
+    h, w, y, _ = _rand_case(79, N=5, H=3, V=4, ignore_rows=(2,))
+    cw = np.zeros(4)
+    out = O.forward(h, w, y, reduction="mean", class_weight=cw)
+    dh, dw = O.backward(h, w, y, reduction="mean", grad_logprob=np.array([1.0]),
+                        grad_entropy=np.array([1.0]), class_weight=cw)
+    err = max(abs(out["logprob_mean"]), abs(out["entropy_mean"]), np.abs(dh).max(), np.abs(dw).max())
+    return err, 0.0
+
+
 ALL_PINS = [
+    pin_library_class_weights,
+    pin_class_weights_as_mask,
+    pin_library_class_weight_grads,
+    pin_class_weight_finite_differences,
+    pin_class_weights_zero_sum,
     pin_aux_closed_forms,
     pin_library_label_smoothing,
     pin_library_sum,

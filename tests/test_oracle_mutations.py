@@ -136,7 +136,44 @@ def _uniform_ce_sums_logits(mp):
     mp.setattr(O, "forward", bad)
 
 
-MUTATIONS = [_entropy_sign, _drop_cap_factor, _cap_factor_not_squared, _label_off_by_one,
+def _weighted_mean_divides_by_n(mp):
+    orig = O.forward
+
+    def bad(h, w, y, *a, **k):
+        out = orig(h, w, y, *a, **k)
+        n, ws = out["n_valid"], out["weight_sum"]
+        for key in list(out):
+            if key.endswith("_mean") and n and ws:
+                out[key] = out[key] * ws / n
+        return out
+    mp.setattr(O, "forward", bad)
+
+
+def _grads_ignore_class_weights(mp):
+    orig = O._token_grads
+
+    def bad(labels, valid, reduction, class_weight, *grads):
+        if class_weight is None or reduction != "mean":
+            return orig(labels, valid, reduction, class_weight, *grads)
+        n = int(valid.sum())
+        out = orig(labels, valid, reduction, None, *grads)
+        ws = float(np.asarray(class_weight)[labels[valid]].sum())
+        return tuple(g * n / ws if ws else g for g in out)
+    mp.setattr(O, "_token_grads", bad)
+
+
+def _class_weight_of_next_class(mp):
+    orig = O._token_weights
+
+    def bad(labels, valid, reduction, class_weight):
+        if class_weight is None:
+            return orig(labels, valid, reduction, class_weight)
+        return orig(labels, valid, reduction, np.roll(np.asarray(class_weight), -1))
+    mp.setattr(O, "_token_weights", bad)
+
+
+MUTATIONS = [_weighted_mean_divides_by_n, _grads_ignore_class_weights,
+             _class_weight_of_next_class, _entropy_sign, _drop_cap_factor, _cap_factor_not_squared, _label_off_by_one,
              _entropy_plus, _mean_over_all_tokens, _no_cap_in_logits, _entropy_grad_uses_lse,
              _onehot_dropped, _transposed_weight_in_dh, _uniform_grad_drops_inv_v,
              _zloss_grad_no_factor2, _sum_divides_by_n, _uniform_ce_sums_logits]
