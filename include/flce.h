@@ -164,7 +164,26 @@ typedef struct flce_options {
   int reduction;         /* FLCE_REDUCTION_NONE, _MEAN or _SUM */
   float z_loss_scale;    /* lam >= 0 (finite) of z_loss = lam * lse^2 */
   int grad_dtype;        /* FLCE_GRAD_BF16 or FLCE_GRAD_F32: type of grad_hidden/grad_weight */
+  const float* class_weight; /* NULL, or device fp32 [V] (the whole vocabulary; 4-byte
+                              * aligned, finite values): target weights of the MEAN and
+                              * SUM reductions, see below; FLCE_ERR_BAD_OPTION under NONE */
 } flce_options_t;
+
+/* Target (class) weights. The Liger-Kernel PR #551 review ("[Verl] Add
+ * entropy loss to cross_entropy_loss and fused_linear_cross_entropy_loss")
+ * lists target weights among the fused options and normalises the weighted
+ * case by the weight of the non-ignored tokens instead of their count. With
+ * class_weight set, a valid token t carries w_t = class_weight[labels[t]]:
+ *   MEAN  reduced[k] = sum_t w_t x_t / sum_t w_t  (0 when the weight sum is 0),
+ *         and the scalar upstream gradient g of output k reaches token t as
+ *         g * w_t / sum_t w_t;
+ *   SUM   reduced[k] = sum_t w_t x_t, gradient g * w_t,
+ * for all four outputs x (logprob, entropy, uniform_ce, z_loss). For the
+ * cross-entropy this is torch.nn.functional.cross_entropy(weight=...). The
+ * per-token vectors stay unweighted. The weight sum is accumulated in
+ * float64 in a fixed order. The sharded calls take the same weights (over
+ * V_total) in flce_merge_shards and flce_backward_shard; flce_forward_shard
+ * ignores them. */
 
 /* Extended forward. As flce_forward, plus
  *   uniform_ce, z_loss  device fp32 [N] outputs, each optional (NULL = not

@@ -413,12 +413,13 @@ flce_status_t launch_dx_finalize(const float* acc, int splits, int64_t rows, int
 }
 
 // The reduced outputs (reduced[k] may be null) from the nb combine blocks'
-// sums; header[1] is the valid count for the mean.
+// sums; the mean divides by the valid count header[1], or with class weights
+// by their sum in the header.
 flce_status_t launch_fwd_reduce(const double4* bsum, int nb, const int32_t* header, bool mean,
-                                float* const (&reduced)[4], hipStream_t st) {
+                                bool weighted, float* const (&reduced)[4], hipStream_t st) {
   return launch(K_FWD_REDUCE, st, [&] {
-    fwd_reduce_kernel<<<1, 256, 0, st>>>(bsum, nb, header, mean ? 1 : 0, reduced[0], reduced[1],
-                                         reduced[2], reduced[3]);
+    fwd_reduce_kernel<<<1, 256, 0, st>>>(bsum, nb, header, mean ? 1 : 0, weighted ? 1 : 0,
+                                         reduced[0], reduced[1], reduced[2], reduced[3]);
   });
 }
 
@@ -457,6 +458,9 @@ flce_status_t check_options(const flce_options_t* o) {
   if (!std::isfinite(o->softcap)) return FLCE_ERR_BAD_SOFTCAP;
   if (!std::isfinite(o->z_loss_scale) || o->z_loss_scale < 0.f) return FLCE_ERR_BAD_OPTION;
   if (o->grad_dtype != FLCE_GRAD_BF16 && o->grad_dtype != FLCE_GRAD_F32) return FLCE_ERR_BAD_OPTION;
+  // Class weights only enter the mean and sum reductions.
+  if (o->class_weight != nullptr && o->reduction == FLCE_REDUCTION_NONE) return FLCE_ERR_BAD_OPTION;
+  if (((uintptr_t)o->class_weight & 3u) != 0) return FLCE_ERR_MISALIGNED;
   return FLCE_OK;
 }
 
@@ -514,6 +518,8 @@ flce_status_t forward_impl(const void* hidden, const void* weight, const int64_t
   pr.state_out = state_out;
   pr.label_logit = shard ? label_logit : nullptr;
   pr.header = header;
+  const float* cw = reduce ? o.class_weight : nullptr;
+  pr.cw = cw;
   FLCE_TRY(launch(K_FWD_PREP, st, [&] { fwd_prep_kernel<<<1, 1024, 0, st>>>(pr); }));
   const int nb = (int)ceil_div(N, kCombineTokens);
   if (N > 0) {
@@ -562,13 +568,15 @@ flce_status_t forward_impl(const void* hidden, const void* weight, const int64_t
     c.uniform_ce = uniform_ce;
     c.z_loss = z_loss;
     c.bsum = bsum;
+    c.labels = labels;
+    c.cw = cw;
     FLCE_TRY(launch(K_FWD_COMBINE, st, [&] {
       fwd_combine_kernel<<<nb, 64 * kCombineWaves, 0, st>>>(c);
     }));
   }
   if (reduce)
     FLCE_TRY(launch_fwd_reduce(bsum, N > 0 ? nb : 0, header, reduction == FLCE_REDUCTION_MEAN,
-                               reduced, st));
+                               cw != nullptr, reduced, st));
   return FLCE_OK;
 }
 
@@ -630,6 +638,7 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
   pa.lab32 = lab32;
   pa.idx = idx;
   pa.header = header;
+  pa.cw = reduction != FLCE_REDUCTION_NONE ? o.class_weight : nullptr;
   FLCE_TRY(launch(K_BWD_PREP, st, [&] { bwd_prep_kernel<<<1, 1024, 0, st>>>(pa); }));
   // Rows of ignored tokens are never written by the compacted contractions.
   FLCE_TRY(launch_zero_ignored(labels, N, V_total, o.ignore_index, grad_hidden,
@@ -818,6 +827,8 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
   pr.uniform_ce = uniform_ce;
   pr.z_loss = z_loss;
   pr.header = header;
+  const float* cw = reduce ? o.class_weight : nullptr;
+  pr.cw = cw;
   FLCE_TRY(launch(K_FWD_PREP, st, [&] { fwd_prep_kernel<<<1, 1024, 0, st>>>(pr); }));
   const int nb = p.TB * (kTile / kCombineTokens);
   if (N == 0) {
@@ -890,6 +901,8 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
       cb.gzl = grad_z_loss;
       cb.reduction = reduction;
       cb.header = header;
+      cb.labels = labels;
+      cb.cw = cw;
       FLCE_TRY(launch(K_FWD_COMBINE, st, [&] {
         fwd_combine_kernel<<<(int)(rows / kCombineTokens), 64 * kCombineWaves, 0, st>>>(cb);
       }));
@@ -983,7 +996,7 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
   if (reduce) {
     float* const red[4] = {reduced, reduced + 1, reduced + 2, reduced + 3};
     FLCE_TRY(launch_fwd_reduce(bsum, N > 0 ? nb : 0, header, reduction == FLCE_REDUCTION_MEAN,
-                               red, st));
+                               cw != nullptr, red, st));
   }
   return FLCE_OK;
 }
@@ -998,7 +1011,7 @@ flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t
                            float* entropy, float* logprob_mean, float* entropy_mean,
                            void* workspace, size_t workspace_bytes, void* stream) {
   FLCE_TRY(check_shape(N, H, V));
-  const flce_options_t o{ignore_index, softcap, reduction, 0.f, FLCE_GRAD_BF16};
+  const flce_options_t o{ignore_index, softcap, reduction, 0.f, FLCE_GRAD_BF16, nullptr};
   FLCE_TRY(check_options(&o));
   if (reduction != FLCE_REDUCTION_NONE && (logprob_mean == nullptr || entropy_mean == nullptr))
     return FLCE_ERR_NULL_POINTER;
@@ -1029,7 +1042,7 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
                             const float* grad_entropy, void* grad_hidden, void* grad_weight,
                             void* workspace, size_t workspace_bytes, void* stream) {
   FLCE_TRY(check_shape(N, H, V));
-  const flce_options_t o{ignore_index, softcap, reduction, 0.f, FLCE_GRAD_BF16};
+  const flce_options_t o{ignore_index, softcap, reduction, 0.f, FLCE_GRAD_BF16, nullptr};
   FLCE_TRY(check_options(&o));
   return backward_impl(hidden, weight, labels, N, H, V, 0, V, o, lse, entropy, grad_logprob,
                        grad_entropy, nullptr, nullptr, grad_hidden, grad_weight, workspace,
@@ -1142,6 +1155,8 @@ flce_status_t flce_merge_shards(const float* states, const float* label_logits, 
   pr.labc = reinterpret_cast<int32_t*>(wsp(workspace, merge_labc_off(N)));
   pr.zlab = reinterpret_cast<float*>(wsp(workspace, merge_zlab_off(N)));
   pr.header = header;
+  const float* cw = reduce ? opt->class_weight : nullptr;
+  pr.cw = cw;
   FLCE_TRY(launch(K_FWD_PREP, st, [&] { fwd_prep_kernel<<<1, 1024, 0, st>>>(pr); }));
   const int nb = (int)ceil_div(N, kCombineTokens);
   if (N > 0) {
@@ -1162,6 +1177,7 @@ flce_status_t flce_merge_shards(const float* states, const float* label_logits, 
     c.uniform_ce = uniform_ce;
     c.z_loss = z_loss;
     c.bsum = bsum;
+    c.cw = cw;
     FLCE_TRY(launch(K_FWD_COMBINE, st, [&] {
       fwd_combine_kernel<<<nb, 64 * kCombineWaves, 0, st>>>(c);
     }));
@@ -1170,7 +1186,7 @@ flce_status_t flce_merge_shards(const float* states, const float* label_logits, 
     float* const red[4] = {reduced, reduced ? reduced + 1 : nullptr,
                            reduced ? reduced + 2 : nullptr, reduced ? reduced + 3 : nullptr};
     FLCE_TRY(launch_fwd_reduce(bsum, N > 0 ? nb : 0, header,
-                               opt->reduction == FLCE_REDUCTION_MEAN, red, st));
+                               opt->reduction == FLCE_REDUCTION_MEAN, cw != nullptr, red, st));
   }
   return FLCE_OK;
 }
@@ -1219,7 +1235,7 @@ const char* flce_status_string(flce_status_t s) {
   return "unknown status";
 }
 
-int flce_version(void) { return 210; }
+int flce_version(void) { return 211; }
 
 flce_status_t flce_probe_mfma_rate(int zero_operands, int64_t steps, double* tflops,
                                    void* workspace, size_t workspace_bytes, void* stream) {

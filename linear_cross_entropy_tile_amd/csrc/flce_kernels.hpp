@@ -104,14 +104,27 @@ struct FwdPrepArgs {
   float4* state_out;       // slice mode: the empty state at ignored tokens
   float* label_logit;      // slice mode: zeroed for every token
   int32_t* header;         // [0] invalid labels, [1] valid tokens n
+  const float* cw;         // optional class weights [V_total]: their sum over valid
+                           // tokens goes to header_wsum(header)
 };
+
+// The float64 sum of the class weights of the valid tokens, kept in the
+// header after the two counts (bytes 16..23).
+__host__ __device__ __forceinline__ double* header_wsum(int32_t* h) {
+  return reinterpret_cast<double*>(h + 4);
+}
+__host__ __device__ __forceinline__ const double* header_wsum(const int32_t* h) {
+  return reinterpret_cast<const double*>(h + 4);
+}
 
 // One block of 1024 threads: compacts the valid tokens (in token order) and
 // writes the per-token outputs of ignored tokens, which no later kernel
 // touches.
 __global__ void __launch_bounds__(1024) fwd_prep_kernel(FwdPrepArgs a) {
   __shared__ int sh[1024];
+  __shared__ double shd[1024];
   int inv = 0, base = 0;
+  double ws = 0.0;
   for (int64_t c0 = 0; c0 < a.N; c0 += 1024) {
     const int64_t t = c0 + threadIdx.x;
     bool bad = false;
@@ -125,6 +138,7 @@ __global__ void __launch_bounds__(1024) fwd_prep_kernel(FwdPrepArgs a) {
     if (valid) {
       a.idx[r] = (int32_t)t;
       a.labc[r] = code;
+      if (a.cw != nullptr) ws += (double)a.cw[a.labels[t]];
     } else if (t < a.N) {
       if (a.lse) a.lse[t] = 0.f;
       if (a.logprob) a.logprob[t] = 0.f;
@@ -141,9 +155,11 @@ __global__ void __launch_bounds__(1024) fwd_prep_kernel(FwdPrepArgs a) {
   }
   for (int64_t r = base + threadIdx.x; r < a.N; r += 1024) a.labc[r] = -1;
   inv = block_sum<int, 1024>(inv, sh);
+  if (a.cw != nullptr) ws = block_sum<double, 1024>(ws, shd);
   if (threadIdx.x == 0) {
     a.header[0] = inv;
     a.header[1] = base;
+    if (a.cw != nullptr) *header_wsum(a.header) = ws;
   }
 }
 
@@ -489,6 +505,13 @@ __device__ __forceinline__ void merge_state(float& m, float& s, float& u, float 
   m = mn;
 }
 
+// 1 / (the mean's divisor): the valid count n, or the class-weight sum with
+// class weights; 0 when that divisor is 0 (every mean and gradient then 0).
+__device__ __forceinline__ float mean_divisor_inv(const int32_t* header, bool weighted) {
+  const double d = weighted ? *header_wsum(header) : (double)header[1];
+  return d != 0.0 ? (float)(1.0 / d) : 0.f;
+}
+
 // Per-token constants of the logit gradient (see bwd_dlogits_kernel):
 //   dz'_v = gbar [v == y] + k0 - p_v (ebar z'_v + cs),
 //   cs = gbar - ebar S - gu - 2 lam gz lse,  k0 = -gu / V,
@@ -538,16 +561,25 @@ struct CombineArgs {
   const float *glp, *gent, *guce, *gzl;
   int reduction;
   const int32_t* header;
+  // Optional class weights [V]: token t's block sums and (fused path) its
+  // scalar gradients carry cw[labels[t]]; the mean divides by the weight sum
+  // header_wsum(header). labels must then be set in compacted mode too.
+  const float* cw;
 };
+
+// Class weight of valid token t (1 without class weights).
+__device__ __forceinline__ float token_weight(const float* cw, const int64_t* labels, int64_t t) {
+  return cw == nullptr ? 1.f : cw[labels[t]];
+}
 
 // Gradient constants of valid token t with lse l and entropy e (fused path;
 // the same arithmetic as bwd_prep_kernel, every label inside the vocabulary).
 __device__ __forceinline__ DzToken token_coef(const CombineArgs& a, int64_t t, float l, float e) {
   const bool scalar = a.reduction != 0;
-  const int nv = a.header[1];
-  const float div = a.reduction == 1 ? (nv > 0 ? 1.f / (float)nv : 0.f) : 1.f;
+  const float div = a.reduction == 1 ? mean_divisor_inv(a.header, a.cw != nullptr) : 1.f;
+  const float om = scalar ? token_weight(a.cw, a.labels, t) * div : 1.f;
   auto grad = [&](const float* g) {
-    return g == nullptr ? 0.f : (scalar ? g[0] * div : g[t]);
+    return g == nullptr ? 0.f : (scalar ? g[0] * om : g[t]);
   };
   const float g = grad(a.glp), ge = grad(a.gent), gu = grad(a.guce), gz = grad(a.gzl);
   const float S = l - e;
@@ -614,10 +646,11 @@ __global__ void __launch_bounds__(1024) fwd_combine_kernel(CombineArgs a) {
     a.logprob[t] = lp;
     if (a.uniform_ce) a.uniform_ce[t] = uc;
     if (a.z_loss) a.z_loss[t] = zl;
-    r0 = lp;
-    r1 = e;
-    r2 = uc;
-    r3 = zl;
+    const double om = a.bsum != nullptr ? (double)token_weight(a.cw, a.labels, t) : 1.0;
+    r0 = om * lp;
+    r1 = om * e;
+    r2 = om * uc;
+    r3 = om * zl;
     if (a.coef != nullptr) a.coef[r] = token_coef(a, t, l, e);
   } else if (a.coef != nullptr) {
     a.coef[r] = DzToken{1e30f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -641,12 +674,14 @@ __global__ void __launch_bounds__(1024) fwd_combine_kernel(CombineArgs a) {
 }
 
 // One block: sums the per-block partial sums in a fixed order; under "mean"
-// divides by the number of valid tokens (0 when there are none). Writes each
-// of the four reduced outputs whose pointer is not null.
+// divides by the number of valid tokens, or with class weights by their sum
+// (0 when that divisor is 0). Writes each of the four reduced outputs whose
+// pointer is not null.
 __global__ void __launch_bounds__(256) fwd_reduce_kernel(const double4* __restrict__ bsum, int nb,
                                                          const int32_t* __restrict__ header,
-                                                         int mean, float* out_lp, float* out_ent,
-                                                         float* out_uce, float* out_zl) {
+                                                         int mean, int weighted, float* out_lp,
+                                                         float* out_ent, float* out_uce,
+                                                         float* out_zl) {
   __shared__ double sh[256];
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
   for (int i = threadIdx.x; i < nb; i += 256) {
@@ -661,9 +696,8 @@ __global__ void __launch_bounds__(256) fwd_reduce_kernel(const double4* __restri
   a2 = block_sum<double, 256>(a2, sh);
   a3 = block_sum<double, 256>(a3, sh);
   if (threadIdx.x == 0) {
-    const int n = header[1];
-    const double d = mean ? (n > 0 ? (double)n : 0.0) : 1.0;
-    const double f = d > 0.0 ? 1.0 / d : 0.0;
+    const double d = mean ? (weighted ? *header_wsum(header) : (double)header[1]) : 1.0;
+    const double f = d != 0.0 ? 1.0 / d : 0.0;
     if (out_lp) out_lp[0] = (float)(a0 * f);
     if (out_ent) out_ent[0] = (float)(a1 * f);
     if (out_uce) out_uce[0] = (float)(a2 * f);
@@ -686,6 +720,7 @@ struct PrepArgs {
   DzToken* coef;
   int32_t* lab32;
   int32_t* header;
+  const float* cw;             // optional class weights [V] (mean, sum)
 };
 
 // One block of 1024: compacts the valid tokens (in token order) and writes
@@ -695,18 +730,26 @@ struct PrepArgs {
 // but keeps the token's other terms.
 __global__ void __launch_bounds__(1024) bwd_prep_kernel(PrepArgs a) {
   __shared__ int sh[1024];
+  __shared__ double shd[1024];
   int inv = 0, nv = 0;
+  double ws = 0.0;
   for (int64_t t = threadIdx.x; t < a.N; t += 1024) {
     bool bad;
-    if (label_code(a.labels[t], a.ignore_index, a.V, a.v_begin, a.Vs, bad) != -1) ++nv;
+    if (label_code(a.labels[t], a.ignore_index, a.V, a.v_begin, a.Vs, bad) != -1) {
+      ++nv;
+      if (a.cw != nullptr) ws += (double)a.cw[a.labels[t]];
+    }
     inv += bad ? 1 : 0;
   }
   inv = block_sum<int, 1024>(inv, sh);
   nv = block_sum<int, 1024>(nv, sh);
-  // Scalar gradients of a mean are spread over the n valid tokens; those of
-  // a sum apply as they are.
+  if (a.cw != nullptr) ws = block_sum<double, 1024>(ws, shd);
+  // Scalar gradients of a mean are spread over the n valid tokens (with class
+  // weights: token t takes the share cw[y_t] / sum of the weights); those of
+  // a sum apply as they are (times cw[y_t]).
   const bool scalar = a.reduction != 0;
-  const float div = a.reduction == 1 ? (nv > 0 ? 1.f / (float)nv : 0.f) : 1.f;
+  const double dv = a.cw != nullptr ? ws : (double)nv;
+  const float div = a.reduction == 1 ? (dv != 0.0 ? (float)(1.0 / dv) : 0.f) : 1.f;
   auto scal = [&](const float* g) { return (scalar && g != nullptr) ? g[0] * div : 0.f; };
   const float g0 = scal(a.glp), e0 = scal(a.gent), u0 = scal(a.guce), z0 = scal(a.gzl);
   const float invV = 1.f / (float)a.V;
@@ -720,7 +763,10 @@ __global__ void __launch_bounds__(1024) bwd_prep_kernel(PrepArgs a) {
     int total;
     const int r = base + chunk_rank(valid, sh, total);
     if (valid) {
-      auto per = [&](const float* g, float s0) { return scalar ? s0 : (g != nullptr ? g[t] : 0.f); };
+      const float om = (scalar && a.cw != nullptr) ? a.cw[a.labels[t]] : 1.f;
+      auto per = [&](const float* g, float s0) {
+        return scalar ? s0 * om : (g != nullptr ? g[t] : 0.f);
+      };
       const float g = per(a.glp, g0), e = per(a.gent, e0), u = per(a.guce, u0), z = per(a.gzl, z0);
       const float l = a.lse[t];
       const float S = l - a.entropy[t];

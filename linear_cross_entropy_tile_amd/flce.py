@@ -55,7 +55,7 @@ class FlceOptions(ctypes.Structure):
     """flce_options_t."""
     _fields_ = [("ignore_index", ctypes.c_int64), ("softcap", ctypes.c_float),
                 ("reduction", ctypes.c_int), ("z_loss_scale", ctypes.c_float),
-                ("grad_dtype", ctypes.c_int)]
+                ("grad_dtype", ctypes.c_int), ("class_weight", ctypes.c_void_p)]
 
 # Every exported symbol with its (restype, argtypes).
 _P = ctypes.c_void_p
@@ -318,15 +318,24 @@ def _ptr(t):
     return t.data_ptr() if t is not None else None
 
 
+def _check_class_weight(cw, V):
+    if cw is not None:
+        _require(cw, _torch().float32, 1, "class_weight")
+        if cw.shape[0] != V:
+            raise ValueError("class_weight must have one weight per class (V)")
+
+
 def forward(hidden, weight, labels, ignore_index: int = -100, softcap: float = 0.0,
             reduction: str = "none", z_loss_scale: float = 0.0, aux: bool = False,
-            workspace=None) -> dict:
+            class_weight=None, workspace=None) -> dict:
     """lse, logprob, entropy [N] (fp32); with ``aux`` also uniform_ce and
     z_loss [N]; under "mean" / "sum" the reductions as ``<name>_mean`` /
     ``<name>_sum`` (fp32 [1]).
 
-    hidden: bf16 [N,H]; weight: bf16 [H,V]; labels: int64 [N]. Without aux,
-    z-loss and "sum" this calls flce_forward, else flce_forward_ex.
+    hidden: bf16 [N,H]; weight: bf16 [H,V]; labels: int64 [N];
+    class_weight: optional fp32 [V] target weights of the "mean" / "sum"
+    reductions. Without aux, z-loss, "sum" and class weights this calls
+    flce_forward, else flce_forward_ex.
     """
     torch = _torch()
     _require(hidden, torch.bfloat16, 2, "hidden")
@@ -346,7 +355,8 @@ def forward(hidden, weight, labels, ignore_index: int = -100, softcap: float = 0
     lp = torch.empty(N, **f32)
     ent = torch.empty(N, **f32)
     out = {"lse": lse, "logprob": lp, "entropy": ent, "workspace": workspace}
-    extended = aux or z_loss_scale != 0.0 or red == FLCE_REDUCTION_SUM
+    _check_class_weight(class_weight, V)
+    extended = aux or z_loss_scale != 0.0 or red == FLCE_REDUCTION_SUM or class_weight is not None
     if not extended:
         lpm = entm = None
         if red == FLCE_REDUCTION_MEAN:
@@ -362,7 +372,8 @@ def forward(hidden, weight, labels, ignore_index: int = -100, softcap: float = 0
     uce = torch.empty(N, **f32) if aux else None
     zl = torch.empty(N, **f32) if aux else None
     reduced = torch.empty(4, **f32) if red != FLCE_REDUCTION_NONE else None
-    opt = FlceOptions(int(ignore_index), float(softcap), red, float(z_loss_scale), FLCE_GRAD_BF16)
+    opt = FlceOptions(int(ignore_index), float(softcap), red, float(z_loss_scale), FLCE_GRAD_BF16,
+                      _ptr(class_weight))
     flce_forward_ex(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), N, H, V, opt,
                     lse.data_ptr(), lp.data_ptr(), ent.data_ptr(), _ptr(uce), _ptr(zl),
                     _ptr(reduced), workspace.data_ptr(), workspace.numel(), _stream())
@@ -378,12 +389,13 @@ def forward(hidden, weight, labels, ignore_index: int = -100, softcap: float = 0
 def backward(hidden, weight, labels, lse, entropy, grad_logprob=None, grad_entropy=None,
              ignore_index: int = -100, softcap: float = 0.0, reduction: str = "none",
              grad_uniform_ce=None, grad_z_loss=None, z_loss_scale: float = 0.0,
-             grad_dtype: str = "bf16", workspace=None):
+             grad_dtype: str = "bf16", class_weight=None, workspace=None):
     """(grad_hidden [N,H], grad_weight [H,V]), bf16 or fp32 (``grad_dtype``).
 
     Upstream gradients: fp32 [N] under "none", fp32 [1] under "mean" and
-    "sum", or None for zero. Without the auxiliary gradients, z-loss, "sum"
-    and fp32 outputs this calls flce_backward, else flce_backward_ex.
+    "sum", or None for zero; class_weight as for ``forward``. Without the
+    auxiliary gradients, z-loss, "sum", class weights and fp32 outputs this
+    calls flce_backward, else flce_backward_ex.
     """
     torch = _torch()
     _require(hidden, torch.bfloat16, 2, "hidden")
@@ -409,15 +421,17 @@ def backward(hidden, weight, labels, lse, entropy, grad_logprob=None, grad_entro
     odt = torch.float32 if gdt == FLCE_GRAD_F32 else torch.bfloat16
     gh = torch.empty((N, H), dtype=odt, device=hidden.device)
     gw = torch.empty((H, V), dtype=odt, device=hidden.device)
+    _check_class_weight(class_weight, V)
     extended = (grad_uniform_ce is not None or grad_z_loss is not None or z_loss_scale != 0.0
-                or red == FLCE_REDUCTION_SUM or gdt != FLCE_GRAD_BF16)
+                or red == FLCE_REDUCTION_SUM or gdt != FLCE_GRAD_BF16 or class_weight is not None)
     if not extended:
         flce_backward(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), N, H, V,
                       int(ignore_index), float(softcap), red, lse.data_ptr(), entropy.data_ptr(),
                       _ptr(grad_logprob), _ptr(grad_entropy), gh.data_ptr(), gw.data_ptr(),
                       workspace.data_ptr(), workspace.numel(), _stream())
         return gh, gw
-    opt = FlceOptions(int(ignore_index), float(softcap), red, float(z_loss_scale), gdt)
+    opt = FlceOptions(int(ignore_index), float(softcap), red, float(z_loss_scale), gdt,
+                      _ptr(class_weight))
     flce_backward_ex(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), N, H, V, opt,
                      lse.data_ptr(), entropy.data_ptr(), _ptr(grad_logprob), _ptr(grad_entropy),
                      _ptr(grad_uniform_ce), _ptr(grad_z_loss), gh.data_ptr(), gw.data_ptr(),
@@ -429,7 +443,7 @@ def forward_backward(hidden, weight, labels, grad_logprob=None, grad_entropy=Non
                      ignore_index: int = -100, softcap: float = 0.0, reduction: str = "none",
                      grad_uniform_ce=None, grad_z_loss=None, z_loss_scale: float = 0.0,
                      grad_dtype: str = "bf16", aux: bool = False, chunk_tokens: int = 0,
-                     workspace=None) -> dict:
+                     class_weight=None, workspace=None) -> dict:
     """The fused forward + backward (flce_forward_backward): the outputs of
     ``forward`` and, under "grad_hidden" / "grad_weight", the gradients of
     ``backward`` for upstream gradients known before the call (fp32 [N] under
@@ -453,7 +467,9 @@ def forward_backward(hidden, weight, labels, grad_logprob=None, grad_entropy=Non
             _require(g, torch.float32, 1, name)
             if g.shape[0] != want:
                 raise ValueError(f"{name} must have {want} element(s) under '{reduction}'")
-    opt = FlceOptions(int(ignore_index), float(softcap), red, float(z_loss_scale), gdt)
+    _check_class_weight(class_weight, V)
+    opt = FlceOptions(int(ignore_index), float(softcap), red, float(z_loss_scale), gdt,
+                      _ptr(class_weight))
     nbytes = flce_fused_workspace_size(N, H, V, opt, int(chunk_tokens))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=hidden.device)

@@ -19,7 +19,7 @@ import math
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "f32_to_bf16_bits",
-           "bf16_bits_to_f32", "sample_indices"]
+           "bf16_bits_to_f32", "sample_indices", "make_class_weights"]
 
 
 @dataclass(frozen=True)
@@ -217,3 +217,14 @@ def sample_indices(n: int, k: int, seed: int) -> np.ndarray:
             break
         pick.add(int(e))
     return np.array(sorted(pick), dtype=np.int64)
+
+
+def make_class_weights(V: int, seed: int, zero_fraction: float = 0.0) -> np.ndarray:
+    """Seeded per-class target weights, float32 [V]: uniform in [0.2, 3.0),
+    with round(zero_fraction * V) classes (a seeded choice) set to 0."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    cw = rng.uniform(0.2, 3.0, size=V).astype(np.float32)
+    k = int(round(zero_fraction * V))
+    if k:
+        cw[rng.permutation(V)[:k]] = 0.0
+    return cw

@@ -124,10 +124,11 @@ def test_profile_hooks_host_only():
 
 
 def _opt(**kw):
-    o = dict(ignore_index=-100, softcap=0.0, reduction=0, z_loss_scale=0.0, grad_dtype=0)
+    o = dict(ignore_index=-100, softcap=0.0, reduction=0, z_loss_scale=0.0, grad_dtype=0,
+             class_weight=None)
     o.update(kw)
     return flce.FlceOptions(o["ignore_index"], o["softcap"], o["reduction"], o["z_loss_scale"],
-                            o["grad_dtype"])
+                            o["grad_dtype"], o["class_weight"])
 
 
 def _fwd_ex(opt=None, **kw):
@@ -159,6 +160,8 @@ def _bwd_ex(opt=None, **kw):
     (dict(softcap=float("nan")), {}, 6),
     (dict(z_loss_scale=-0.5), {}, 9), (dict(z_loss_scale=float("inf")), {}, 9),
     (dict(grad_dtype=3), {}, 9),
+    (dict(class_weight=A), {}, 9),                          # class weights under "none"
+    (dict(reduction=2, class_weight=A + 2), dict(red=A), 4),  # class weights not 4-byte aligned
     (dict(), dict(N=-2), 2), (dict(), dict(V=12), 4), (dict(), dict(wsb=8), 5),
 ])
 def test_forward_ex_rejects(okw, kw, code):
@@ -170,6 +173,7 @@ def test_forward_ex_rejects(okw, kw, code):
     (dict(reduction=-3), {}, 3),
     (dict(z_loss_scale=float("nan")), {}, 9), (dict(grad_dtype=-1), {}, 9),
     (dict(grad_dtype=1), dict(V=(1 << 21) + 8), 2),           # fp32 gradients: V <= 2^21
+    (dict(class_weight=A), {}, 9), (dict(reduction=1, class_weight=A + 1), {}, 4),
     (dict(), dict(gw=None), 1), (dict(), dict(gh=A + 4), 4), (dict(), dict(wsb=8), 5),
 ])
 def test_backward_ex_rejects(okw, kw, code):
@@ -177,9 +181,11 @@ def test_backward_ex_rejects(okw, kw, code):
 
 
 def test_options_layout():
-    # flce_options_t: int64, float, int, float, int -> 24 bytes with natural alignment.
-    assert ctypes.sizeof(flce.FlceOptions) == 24
+    # flce_options_t: int64, float, int, float, int, pointer -> 32 bytes with
+    # natural alignment (4 bytes of padding before the pointer).
+    assert ctypes.sizeof(flce.FlceOptions) == 32
     assert flce.FlceOptions.reduction.offset == 12 and flce.FlceOptions.grad_dtype.offset == 20
+    assert flce.FlceOptions.class_weight.offset == 24
 
 
 def test_workspace_size_sum():
