@@ -22,10 +22,12 @@ class LinearCrossEntropy(torch.autograd.Function):
     """(logprob, entropy) of the fused head; see ``linear_cross_entropy``."""
 
     @staticmethod
-    def forward(ctx, hidden, weight, labels, reduction="mean", ignore_index=-100, softcap=0.0):
+    def forward(ctx, hidden, weight, labels, reduction="mean", ignore_index=-100, softcap=0.0,
+                class_weight=None):
         out = flce.forward(hidden, weight, labels, ignore_index=ignore_index, softcap=softcap,
-                           reduction=reduction)
+                           reduction=reduction, class_weight=class_weight)
         ctx.save_for_backward(hidden, weight, labels, out["lse"], out["entropy"])
+        ctx.class_weight = class_weight
         ctx.reduction = reduction
         ctx.ignore_index = ignore_index
         ctx.softcap = softcap
@@ -43,14 +45,19 @@ class LinearCrossEntropy(torch.autograd.Function):
 
         gh, gw = flce.backward(hidden, weight, labels, lse, entropy, prep(grad_logprob),
                                prep(grad_entropy), ignore_index=ctx.ignore_index,
-                               softcap=ctx.softcap, reduction=ctx.reduction)
-        return gh, gw, None, None, None, None
+                               softcap=ctx.softcap, reduction=ctx.reduction,
+                               class_weight=ctx.class_weight)
+        return gh, gw, None, None, None, None, None
 
 
 def linear_cross_entropy(hidden, weight, labels, reduction="mean", ignore_index=-100,
-                         softcap=0.0):
+                         softcap=0.0, class_weight=None):
     """(logprob, entropy) for hidden bf16 [N,H], weight bf16 [H,V], labels
     int64 [N]: per token ([N] fp32) under reduction "none", else the mean over
     the non-ignored tokens ("mean") or their sum ("sum"), 0-d fp32 tensors.
-    Differentiable with respect to hidden and weight (gradients in bf16)."""
-    return LinearCrossEntropy.apply(hidden, weight, labels, reduction, ignore_index, softcap)
+    class_weight (fp32 [V], "mean" / "sum" only) weights token t by
+    class_weight[labels[t]] in both reductions; the mean then divides by the
+    weight sum of the non-ignored tokens. Differentiable with respect to
+    hidden and weight (gradients in bf16)."""
+    return LinearCrossEntropy.apply(hidden, weight, labels, reduction, ignore_index, softcap,
+                                    class_weight)

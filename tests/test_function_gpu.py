@@ -74,3 +74,30 @@ def test_autograd_one_output_used():
                              grad_entropy=np.array([1.0], np.float32))
     assert G.rel_l2(h.grad.float().cpu().numpy(), dh) <= G.GRAD_REL_L2
     assert G.rel_l2(w.grad.float().cpu().numpy(), dw) <= G.GRAD_REL_L2
+
+
+def test_autograd_class_weights():
+    """Class weights through the autograd wrapper: the weighted means and the
+    gradients of -logprob + 0.01 entropy against the oracle."""
+    wl = W.WORKLOADS["odd_tails"]
+    x = W.make_inputs(wl)
+    t = G.upload(x)
+    cw = W.make_class_weights(wl.V, wl.seed + 9, 0.1)
+    h = t["hidden"].clone().requires_grad_(True)
+    w = t["weight"].clone().requires_grad_(True)
+    lp, ent = linear_cross_entropy(h, w, t["labels"], reduction="mean",
+                                   ignore_index=wl.ignore_index,
+                                   class_weight=torch.from_numpy(cw).to(G.dev()))
+    (-lp + 0.01 * ent).backward()
+    torch.cuda.synchronize()
+    hf = W.bf16_bits_to_f32(x["hidden"])
+    wf = W.bf16_bits_to_f32(x["weight"])
+    fw = oracle.forward(hf, wf, x["labels"], ignore_index=wl.ignore_index, reduction="mean",
+                        class_weight=cw)
+    dh, dw = oracle.backward(hf, wf, x["labels"], ignore_index=wl.ignore_index, reduction="mean",
+                             grad_logprob=np.array([-1.0], np.float32),
+                             grad_entropy=np.array([0.01], np.float32), class_weight=cw)
+    assert G.stat_err([lp.item()], [fw["logprob_mean"]]) <= 1.0
+    assert G.stat_err([ent.item()], [fw["entropy_mean"]]) <= 1.0
+    assert G.rel_l2(h.grad.float().cpu().numpy(), dh) <= G.GRAD_REL_L2
+    assert G.rel_l2(w.grad.float().cpu().numpy(), dw) <= G.GRAD_REL_L2
