@@ -4,7 +4,8 @@ For each full-size workload this runs the float64 CPU oracle (and nothing
 else) on the seeded inputs and stores, in tests/golden/<workload>.npz:
 
   lse, logprob, entropy   [N]   every token's statistics
-  logprob_mean, entropy_mean    (reduction "mean" only)
+  logprob_mean, entropy_mean    (reduction "mean" only; class-weighted for
+                                 the "_weighted" variant)
   rows, dhidden_rows      sampled rows of dHidden      [len(rows), H]
   cols, dweight_cols      sampled columns of dWeight   [H, len(cols)]
 
@@ -30,7 +31,10 @@ sys.path.insert(0, ROOT)
 import oracle.flce_oracle as O  # noqa: E402
 from linear_cross_entropy_tile_amd import workloads as W  # noqa: E402
 
-FULL = ["llama3_head", "gemma2_softcap", "rl_rollout"]
+FULL = ["llama3_head", "gemma2_softcap", "rl_rollout", "gemma2_softcap_weighted"]
+# Variants: stored name -> (workload, seed of the class weights, fraction of
+# zero class weights), drawn by workloads.make_class_weights.
+WEIGHTED = {"gemma2_softcap_weighted": ("gemma2_softcap", 4242, 0.05)}
 N_ROWS = 16
 N_COLS = 16
 
@@ -41,14 +45,24 @@ def sample(wl):
     return rows, cols
 
 
+def class_weights(name: str):
+    """The class weights of a stored variant (None for the plain workloads)."""
+    if name not in WEIGHTED:
+        return None
+    base, seed, zf = WEIGHTED[name]
+    return W.make_class_weights(W.WORKLOADS[base].V, seed, zf)
+
+
 def golden(name: str, block: int = 128) -> str:
-    wl = W.WORKLOADS[name]
+    wl = W.WORKLOADS[WEIGHTED[name][0] if name in WEIGHTED else name]
+    cw = class_weights(name)
     t0 = time.time()
     x = W.make_inputs(wl)
     h = W.bf16_bits_to_f32(x["hidden"])
     w = W.bf16_bits_to_f32(x["weight"]).astype(np.float64)
     labels, valid = O._valid_mask(x["labels"], wl.V, wl.ignore_index)
-    gb, eb = O._token_grads(labels, valid, wl.reduction, x["grad_logprob"], x["grad_entropy"])
+    gb, eb = O._token_grads(labels, valid, wl.reduction, cw, x["grad_logprob"],
+                            x["grad_entropy"])
     rows, cols = sample(wl)
     N, H = wl.N, wl.H
     lse = np.zeros(N)
@@ -78,9 +92,10 @@ def golden(name: str, block: int = 128) -> str:
            "entropy": ent.astype(np.float32), "rows": rows, "cols": cols,
            "dhidden_rows": dh_rows.astype(np.float32), "dweight_cols": dw_cols.astype(np.float32)}
     if wl.reduction == "mean":
-        n = int(valid.sum())
-        out["logprob_mean"] = np.array([lp[valid].sum() / n if n else 0.0])
-        out["entropy_mean"] = np.array([ent[valid].sum() / n if n else 0.0])
+        om = O._token_weights(labels, valid, wl.reduction, cw)[valid]
+        ws = om.sum()
+        out["logprob_mean"] = np.array([(om * lp[valid]).sum() / ws if ws else 0.0])
+        out["entropy_mean"] = np.array([(om * ent[valid]).sum() / ws if ws else 0.0])
     path = os.path.join(HERE, f"{name}.npz")
     np.savez_compressed(path, **out)
     print(f"wrote {path} in {time.time() - t0:.0f}s", flush=True)

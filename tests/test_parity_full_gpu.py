@@ -6,6 +6,9 @@ which calls only the oracle):
   * every token's lse / logprob / entropy (and the means under "mean"),
   * sampled rows of dHidden and sampled columns of dWeight.
 
+The Gemma2-shaped head is also run with seeded class weights (their stored
+variant gemma2_softcap_weighted).
+
 Tolerances: statistics within 2e-3 absolute or 1e-3 relative; gradients
 within 1e-2 relative L2 error over the sampled rows / columns.
 """
@@ -16,7 +19,7 @@ import pytest
 import torch
 
 import gpu_helpers as G
-from linear_cross_entropy_tile_amd import workloads as W
+from linear_cross_entropy_tile_amd import flce, workloads as W
 
 pytestmark = pytest.mark.gpu
 
@@ -53,3 +56,37 @@ def test_parity_full_size(name):
     if bool(ign.any()):
         assert torch.count_nonzero(got["grad_hidden"][ign]).item() == 0
     assert got["invalid_labels"] == 0
+
+
+def test_parity_full_size_class_weights():
+    """The Gemma2-shaped head (mean reduction) with seeded class weights, 5 %
+    of them zero: the class-weighted means and the sampled gradient rows and
+    columns against the stored oracle values of that variant."""
+    name = "gemma2_softcap_weighted"
+    path = os.path.join(HERE, "golden", f"{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    import sys
+    sys.path.insert(0, os.path.join(HERE, "golden"))
+    import make_golden
+    ref = np.load(path)
+    wl = W.WORKLOADS[make_golden.WEIGHTED[name][0]]
+    print(f"[full] {name} N={wl.N} H={wl.H} V={wl.V}", flush=True)
+    x = W.make_inputs(wl)
+    t = G.upload(x)
+    cw = torch.from_numpy(make_golden.class_weights(name)).to(G.dev())
+    out = flce.forward(t["hidden"], t["weight"], t["labels"], ignore_index=wl.ignore_index,
+                       softcap=wl.softcap, reduction=wl.reduction, class_weight=cw)
+    gh, gw = flce.backward(t["hidden"], t["weight"], t["labels"], out["lse"], out["entropy"],
+                           t["grad_logprob"], t["grad_entropy"], ignore_index=wl.ignore_index,
+                           softcap=wl.softcap, reduction=wl.reduction, class_weight=cw)
+    torch.cuda.synchronize()
+    for k in ("lse", "logprob", "entropy", "logprob_mean", "entropy_mean"):
+        e = G.stat_err(out[k].cpu().numpy(), ref[k])
+        assert e <= 1.0, f"{name} {k}: error {e:.3f} x tolerance"
+    rows = torch.from_numpy(ref["rows"]).to(G.dev())
+    cols = torch.from_numpy(ref["cols"]).to(G.dev())
+    e = G.rel_l2(gh.index_select(0, rows).float().cpu().numpy(), ref["dhidden_rows"])
+    assert e <= G.GRAD_REL_L2, f"{name} grad_hidden rows rel L2 {e:.2e}"
+    e = G.rel_l2(gw.index_select(1, cols).float().cpu().numpy(), ref["dweight_cols"])
+    assert e <= G.GRAD_REL_L2, f"{name} grad_weight cols rel L2 {e:.2e}"
