@@ -174,3 +174,56 @@ def test_zero_class_weights_give_zero():
         assert o["logprob_mean"].item() == 0.0 and o["entropy_mean"].item() == 0.0
     for a in (gh, gw, res["grad_hidden"], res["grad_weight"]):
         assert torch.count_nonzero(a).item() == 0
+
+
+def test_class_weights_invalid_labels():
+    """Labels outside [0, V) that are not ignore_index are treated as ignored
+    (their class weight is never read) and counted in the status word; the
+    weighted mean and gradients equal the oracle's with those tokens ignored."""
+    wl = W.WORKLOADS["odd_tails"]
+    x = W.make_inputs(wl)
+    bad = x["labels"].copy()
+    bad[3] = wl.V
+    bad[5] = -7
+    bad[6] = 10 ** 12
+    xb = dict(x)
+    xb["labels"] = bad
+    t = G.upload(xb)
+    cw = W.make_class_weights(wl.V, wl.seed + 34, 0.1)
+    cwt = torch.from_numpy(cw).to(G.dev())
+    grads = _scalars(wl.seed + 44)
+    g = [torch.from_numpy(a).to(G.dev()) for a in grads]
+    out = flce.forward(t["hidden"], t["weight"], t["labels"], reduction="mean", aux=True,
+                       class_weight=cwt)
+    gh, gw = flce.backward(t["hidden"], t["weight"], t["labels"], out["lse"], out["entropy"],
+                           g[0], g[1], reduction="mean", grad_uniform_ce=g[2],
+                           grad_z_loss=g[3], class_weight=cwt)
+    res = flce.forward_backward(t["hidden"], t["weight"], t["labels"], g[0], g[1],
+                                reduction="mean", grad_uniform_ce=g[2], grad_z_loss=g[3],
+                                aux=True, class_weight=cwt)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    assert flce.flce_get_status(out["workspace"].data_ptr(), stream) == 3
+    assert flce.flce_get_status(res["workspace"].data_ptr(), stream) == 3
+    xo = dict(x)
+    xo["labels"] = np.where((bad >= 0) & (bad < wl.V), bad, wl.ignore_index)
+    fw, dh, dw = _oracle(xo, wl, "mean", 0.0, 0.0, cw, grads)
+    _check("invalid labels", out, lambda k: out[f"{k}_mean"], gh, gw, fw, dh, dw, "mean")
+    _check("invalid labels fused", res, lambda k: res[f"{k}_mean"], res["grad_hidden"],
+           res["grad_weight"], fw, dh, dw, "mean")
+
+
+def test_class_weights_empty_batch():
+    """N = 0 with class weights: means 0, zero weight gradient."""
+    d = G.dev()
+    h = torch.empty((0, 64), dtype=torch.bfloat16, device=d)
+    w = torch.randn((64, 512), device=d).to(torch.bfloat16)
+    y = torch.empty(0, dtype=torch.int64, device=d)
+    cwt = torch.ones(512, dtype=torch.float32, device=d)
+    out = flce.forward(h, w, y, reduction="mean", class_weight=cwt)
+    g = torch.ones(1, device=d)
+    gh, gw = flce.backward(h, w, y, out["lse"], out["entropy"], g, g, reduction="mean",
+                           class_weight=cwt)
+    torch.cuda.synchronize()
+    assert out["logprob_mean"].item() == 0.0 and out["entropy_mean"].item() == 0.0
+    assert gh.shape == (0, 64) and torch.count_nonzero(gw).item() == 0
