@@ -157,7 +157,9 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
                             void* grad_hidden, void* grad_weight,
                             void* workspace, size_t workspace_bytes, void* stream);
 
-/* Options of the extended entry points. */
+/* Options of the extended entry points. class_weight was added in version
+ * 211 (flce_version); the struct grew from 24 to 32 bytes, so callers built
+ * against an older header must be rebuilt. */
 typedef struct flce_options {
   int64_t ignore_index;  /* label value that marks a skipped token */
   float softcap;         /* c > 0: z' = c*tanh(z/c); c <= 0: no cap; must be finite */
