@@ -227,3 +227,29 @@ def test_class_weights_empty_batch():
     torch.cuda.synchronize()
     assert out["logprob_mean"].item() == 0.0 and out["entropy_mean"].item() == 0.0
     assert gh.shape == (0, 64) and torch.count_nonzero(gw).item() == 0
+
+
+def test_class_weights_f32_gradients_round_to_bf16():
+    """fp32 gradient outputs under class weights: within tolerance of the
+    oracle, and the bf16 outputs are exactly their round-to-nearest-even (the
+    same fp32 arithmetic)."""
+    wl = W.WORKLOADS["dw_split"]
+    x = W.make_inputs(wl)
+    t = G.upload(x)
+    cw = W.make_class_weights(wl.V, wl.seed + 35, 0.1)
+    cwt = torch.from_numpy(cw).to(G.dev())
+    grads = _scalars(wl.seed + 45)
+    g = [torch.from_numpy(a).to(G.dev()) for a in grads]
+    out = flce.forward(t["hidden"], t["weight"], t["labels"], reduction="mean", class_weight=cwt)
+    res = {}
+    for dt in ("f32", "bf16"):
+        res[dt] = flce.backward(t["hidden"], t["weight"], t["labels"], out["lse"], out["entropy"],
+                                g[0], g[1], reduction="mean", grad_dtype=dt, class_weight=cwt)
+    torch.cuda.synchronize()
+    gh32, gw32 = res["f32"]
+    gh16, gw16 = res["bf16"]
+    assert gh32.dtype == torch.float32 and gh16.dtype == torch.bfloat16
+    assert torch.equal(gh32.to(torch.bfloat16), gh16) and torch.equal(gw32.to(torch.bfloat16), gw16)
+    _, dh, dw = _oracle(x, wl, "mean", 0.0, 0.0, cw, [grads[0], grads[1], None, None])
+    assert G.rel_l2(gh32.cpu().numpy(), dh) <= G.GRAD_REL_L2
+    assert G.rel_l2(gw32.cpu().numpy(), dw) <= G.GRAD_REL_L2
