@@ -65,3 +65,14 @@ def test_zipf_labels_and_prompt_mask():
 def test_sample_indices():
     s = W.sample_indices(1000, 16, 7)
     assert s[0] == 0 and s[-1] == 999 and len(set(s)) == len(s) == 16
+
+
+def test_class_weights_recipe():
+    a = W.make_class_weights(1000, 11, 0.05)
+    b = W.make_class_weights(1000, 11, 0.05)
+    assert a.dtype == np.float32 and a.shape == (1000,)
+    assert np.array_equal(a, b)                      # seeded: same bits
+    assert (a == 0).sum() == 50                      # round(0.05 * 1000) zeros
+    nz = a[a != 0]
+    assert nz.min() >= 0.2 and nz.max() < 3.0
+    assert not np.array_equal(a, W.make_class_weights(1000, 12, 0.05))
