@@ -217,6 +217,17 @@ def kernel_rows(table, steps, n_valid, H, V):
             row["gbps"] = nbytes / (per * 1e-3) / 1e9
             row["hbm_frac"] = row["gbps"] / PEAK_HBM_GBPS
         kernels[name] = row
+    # Chunks whose dH and dW tiles share one launch (bwd_dxdw) leave bwd_dx and
+    # bwd_dw with only part of the vocabulary: the three kinds are then rated
+    # together, 4 flop per valid token x H x V over their summed time.
+    group = [k for k in ("bwd_dx", "bwd_dw", "bwd_dxdw") if k in table]
+    if "bwd_dxdw" in table:
+        gms = sum(table[k][1] for k in group)
+        rate = 4 * n_valid * H * V * steps / (gms * 1e-3) / 1e12
+        for k in group:
+            kernels[k]["tflops"] = rate
+            kernels[k]["mfma_frac"] = rate / PEAK_BF16_TFLOPS
+            kernels[k]["rated_with"] = "+".join(group)
     return kernels
 
 

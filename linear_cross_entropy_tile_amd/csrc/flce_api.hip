@@ -272,12 +272,12 @@ constexpr int64_t kMaxVF32 = (int64_t)1 << 21;
 enum Kind {
   K_FWD_PREP, K_FWD_TILE, K_FWD_COMBINE, K_FWD_REDUCE, K_BWD_PREP, K_BWD_DLOGITS, K_BWD_DX,
   K_BWD_DW, K_DW_REDUCE, K_FILL, K_PACK_WEIGHT, K_PACK_HIDDEN, K_DX_FINALIZE, K_FUSED_TILE,
-  K_FUSED_DLOGITS, K_NUM
+  K_FUSED_DLOGITS, K_BWD_DXDW, K_NUM
 };
 const char* kKindNames[K_NUM] = {"fwd_prep", "fwd_tile", "fwd_combine", "fwd_reduce", "bwd_prep",
                                  "bwd_dlogits", "bwd_dx", "bwd_dw", "dw_reduce", "fill_zero",
                                  "pack_weight", "pack_hidden", "dx_finalize", "fused_tile",
-                                 "fused_dlogits"};
+                                 "fused_dlogits", "bwd_dxdw"};
 
 struct Pending {
   int kind;
@@ -395,6 +395,39 @@ flce_status_t launch_dx(const DxArgs& x, int mode, bool f32, int grid, hipStream
       default: bwd_dx_kernel<DX_LAST, true><<<grid, kThreads, 0, st>>>(x); break;
     }
   });
+}
+
+// dH tiles in `mode` and direct dW tiles of one chunk in one launch.
+flce_status_t launch_dxdw(const DxArgs& x, const DwArgs& w, int mode, bool f32, int grid,
+                          hipStream_t st) {
+  return launch(K_BWD_DXDW, st, [&] {
+    switch (mode * 2 + (f32 ? 1 : 0)) {
+      case DX_ONLY * 2: bwd_dxdw_kernel<DX_ONLY, false><<<grid, kThreads, 0, st>>>(x, w); break;
+      case DX_ONLY * 2 + 1: bwd_dxdw_kernel<DX_ONLY, true><<<grid, kThreads, 0, st>>>(x, w); break;
+      case DX_FIRST * 2: bwd_dxdw_kernel<DX_FIRST, false><<<grid, kThreads, 0, st>>>(x, w); break;
+      case DX_FIRST * 2 + 1: bwd_dxdw_kernel<DX_FIRST, true><<<grid, kThreads, 0, st>>>(x, w); break;
+      case DX_MID * 2: bwd_dxdw_kernel<DX_MID, false><<<grid, kThreads, 0, st>>>(x, w); break;
+      case DX_MID * 2 + 1: bwd_dxdw_kernel<DX_MID, true><<<grid, kThreads, 0, st>>>(x, w); break;
+      case DX_LAST * 2: bwd_dxdw_kernel<DX_LAST, false><<<grid, kThreads, 0, st>>>(x, w); break;
+      default: bwd_dxdw_kernel<DX_LAST, true><<<grid, kThreads, 0, st>>>(x, w); break;
+    }
+  });
+}
+
+// Whether a chunk's dH and dW tiles go into one launch (bwd_dxdw_kernel):
+// only with direct dW stores, when the dH tiles' K length (per split) equals
+// dW's (the token blocks) so that the combined grid stays balanced, and when
+// one grid needs fewer rounds of CUs than the two. FLCE_DXDW=0 never
+// combines, FLCE_DXDW=1 always does with direct dW stores (tests and tuning
+// only).
+bool combine_dxdw(const Plan& p, int nk, int64_t ndx, int64_t ndw) {
+  if (p.dw_splits != 1) return false;
+  const char* e = std::getenv("FLCE_DXDW");
+  if (e != nullptr && e[0] == '0') return false;
+  if (e != nullptr && e[0] == '1') return true;
+  const int kper = (int)ceil_div(nk, p.dx_splits);
+  if (kper != p.nkb) return false;
+  return ceil_div(ndx, kNumCUs) + ceil_div(ndw, kNumCUs) > ceil_div(ndx + ndw, kNumCUs);
 }
 
 // grad_hidden rows of compacted rows [r0, r0 + rows) from the K-split dH
@@ -711,9 +744,7 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
                            : (p.nchunks == 1 ? DX_ONLY
                                              : (c == 0 ? DX_FIRST
                                                        : (c == p.nchunks - 1 ? DX_LAST : DX_MID)));
-    FLCE_TRY(launch_dx(x, mode, f32, p.TB * p.HT * p.dx_splits, st));
-    if (split && c == p.nchunks - 1)
-      FLCE_TRY(launch_dx_finalize(acc, p.dx_splits, N, H, idx, nvalid, 0, grad_hidden, f32, st));
+    const int gx = p.TB * p.HT * p.dx_splits;
 
     DwArgs w{};
     w.xtb = xtb;
@@ -737,14 +768,21 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
     w.gw = grad_weight;
     w.part = part;
     const int gw = p.HT * vtc * p.dw_splits;
-    FLCE_TRY(launch(K_BWD_DW, st, [&] {
-      if (p.dw_splits > 1)
-        bwd_dw_kernel<DW_SPLIT, false><<<gw, kThreads, 0, st>>>(w);
-      else if (f32)
-        bwd_dw_kernel<DW_DIRECT, true><<<gw, kThreads, 0, st>>>(w);
-      else
-        bwd_dw_kernel<DW_DIRECT, false><<<gw, kThreads, 0, st>>>(w);
-    }));
+    if (combine_dxdw(p, x.nk, gx, gw)) {
+      FLCE_TRY(launch_dxdw(x, w, mode, f32, gx + gw, st));
+    } else {
+      FLCE_TRY(launch_dx(x, mode, f32, gx, st));
+      FLCE_TRY(launch(K_BWD_DW, st, [&] {
+        if (p.dw_splits > 1)
+          bwd_dw_kernel<DW_SPLIT, false><<<gw, kThreads, 0, st>>>(w);
+        else if (f32)
+          bwd_dw_kernel<DW_DIRECT, true><<<gw, kThreads, 0, st>>>(w);
+        else
+          bwd_dw_kernel<DW_DIRECT, false><<<gw, kThreads, 0, st>>>(w);
+      }));
+    }
+    if (split && c == p.nchunks - 1)
+      FLCE_TRY(launch_dx_finalize(acc, p.dx_splits, N, H, idx, nvalid, 0, grad_hidden, f32, st));
     if (p.dw_splits > 1) {
       const int64_t n = H * vc;
       const int blocks = (int)(ceil_div(n, 256) < 8192 ? ceil_div(n, 256) : 8192);

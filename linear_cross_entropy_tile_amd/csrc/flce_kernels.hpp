@@ -1108,18 +1108,23 @@ struct DxArgs {
 // the output), DX_FIRST (store fp32), DX_MID (add into fp32), DX_LAST (add and
 // write the output). F32OUT: the output is fp32, else bf16. Out-of-range rows
 // and columns fall outside the buffer resources.
+// Token tiles of a dH launch that hold compacted tokens; the tiles are
+// numbered over them only (dx_tiles() of them in all).
+__device__ __forceinline__ int dx_token_tiles(const DxArgs& a) {
+  const int left = (*a.nvalid - a.r0 + kTile - 1) / kTile;
+  return left < a.TB ? (left > 0 ? left : 0) : a.TB;
+}
+__device__ __forceinline__ int dx_tiles(const DxArgs& a) {
+  return dx_token_tiles(a) * a.HT * a.splits;
+}
+
+// Tile L (logical, < dx_tiles(a)) of the dH contraction.
 template <int MODE, bool F32OUT>
-__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                               amdgpu_waves_per_eu(2, 2)))
-bwd_dx_kernel(DxArgs a) {
-  FLCE_DECLARE_STAGES(sa, sb);
-  // Tiles numbered over the token tiles that hold compacted tokens only.
+__device__ __forceinline__ void dx_tile(const DxArgs& a, int L, char* const (&sa)[kStages],
+                                        char* const (&sb)[kStages]) {
   const int nval = *a.nvalid - a.r0;  // valid rows from this launch's row 0
-  const int left = (nval + kTile - 1) / kTile;
-  const int tbv = left < a.TB ? (left > 0 ? left : 0) : a.TB;
+  const int tbv = dx_token_tiles(a);
   const int per_split = tbv * a.HT;
-  if ((int)blockIdx.x >= per_split * a.splits) return;
-  const int L = xcd_remap(blockIdx.x, per_split * a.splits);
   const int sp = L / per_split;
   int tb, ht;
   group_map(L - sp * per_split, tbv, a.HT, a.group, tb, ht);
@@ -1183,6 +1188,16 @@ bwd_dx_kernel(DxArgs a) {
       __builtin_amdgcn_sched_barrier(0);  // one 32 x 32 block at a time
     }
   }
+}
+
+template <int MODE, bool F32OUT>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                               amdgpu_waves_per_eu(2, 2)))
+bwd_dx_kernel(DxArgs a) {
+  FLCE_DECLARE_STAGES(sa, sb);
+  const int total = dx_tiles(a);
+  if ((int)blockIdx.x >= total) return;
+  dx_tile<MODE, F32OUT>(a, xcd_remap(blockIdx.x, total), sa, sb);
 }
 
 // With K-split dH: grad_hidden row idx[r] = sum over splits of acc[s][r],
@@ -1300,19 +1315,13 @@ __device__ __forceinline__ void dw_store_tile(const Acc& acc, const DwArgs& a, i
   }
 }
 
+// Tile L (logical, < HT * VTc * splits) of the dW contraction:
 // C[h][v] = sum_t hidden[t][h] D[t][v] over the split's (or chunk's) tokens.
+// `last` (DW_CHUNK): the chunk holds the last valid token.
 template <int MODE, bool F32OUT>
-__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                               amdgpu_waves_per_eu(2, 2)))
-bwd_dw_kernel(DwArgs a) {
-  FLCE_DECLARE_STAGES(sa, sb);
+__device__ __forceinline__ void dw_tile(const DwArgs& a, int L, bool last,
+                                        char* const (&sa)[kStages], char* const (&sb)[kStages]) {
   const int n = *a.nvalid;
-  bool last = true;
-  if constexpr (MODE == DW_CHUNK) {
-    if (!a.first && n <= a.r0) return;  // no valid token in this chunk
-    last = n <= a.r0 + a.rows;          // the chunk holds the last valid token
-  }
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int per = a.HT * a.VTc;
   const int sp = L / per;
   int ht, vt;
@@ -1346,6 +1355,40 @@ bwd_dw_kernel(DwArgs a) {
     else
       dw_store_tile<DWS_MID, F32OUT>(acc, a, h0, vl0, sp, wm, wn, lane);
   }
+}
+
+template <int MODE, bool F32OUT>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                               amdgpu_waves_per_eu(2, 2)))
+bwd_dw_kernel(DwArgs a) {
+  FLCE_DECLARE_STAGES(sa, sb);
+  bool last = true;
+  if constexpr (MODE == DW_CHUNK) {
+    const int n = *a.nvalid;
+    if (!a.first && n <= a.r0) return;  // no valid token in this chunk
+    last = n <= a.r0 + a.rows;          // the chunk holds the last valid token
+  }
+  dw_tile<MODE, F32OUT>(a, xcd_remap(blockIdx.x, gridDim.x), last, sa, sb);
+}
+
+// dH and dW of one vocabulary chunk in a single launch (dW stored directly):
+// the dH tiles take logical ids [0, dx_tiles), the dW tiles the rest, so
+// with equal K lengths the two tile sets fill the GPU as one grid (e.g. two
+// grids of 4.5 rounds of CUs each become one of 9 rounds). The XCD-aware
+// numbering gives each XCD a contiguous range of the combined ids.
+template <int DXMODE, bool F32OUT>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                               amdgpu_waves_per_eu(2, 2)))
+bwd_dxdw_kernel(DxArgs x, DwArgs w) {
+  FLCE_DECLARE_STAGES(sa, sb);
+  const int ndx = dx_tiles(x);
+  const int total = ndx + w.HT * w.VTc * w.splits;
+  if ((int)blockIdx.x >= total) return;
+  const int L = xcd_remap(blockIdx.x, total);
+  if (L < ndx)
+    dx_tile<DXMODE, F32OUT>(x, L, sa, sb);
+  else
+    dw_tile<DW_DIRECT, F32OUT>(w, L - ndx, true, sa, sb);
 }
 
 // Sums the split partials in split order and writes dW for the chunk (bf16,
