@@ -22,8 +22,11 @@ Prints one JSON line. Besides the throughput it reports:
   cpu_baseline  the float64 CPU oracle timed on a bounded token sample;
   mfma_sustained  the bf16 MFMA rate the device sustains in the kernels' wave
                 tile with no memory traffic, on pseudo-random and on zero
-                operands (flce_probe_mfma_rate); roofline.frac_of_sustained is
-                the roofline kernel's rate against the random-operand figure;
+                operands, and with the tile's LDS fragment reads and its
+                L2 -> LDS DMA added (flce_probe_mfma_rate modes 0-3);
+                roofline.frac_of_sustained is the roofline kernel's rate
+                against the random-operand figure, frac_of_lds_dma_probe
+                against the figure with the tile's data movement;
   memory        peak device memory of one step vs the fp32 logits that a
                 materialising implementation needs;
   torch_ref     (optional) a materialising torch implementation of the same
@@ -393,20 +396,26 @@ def main():
         out["bwd_ms"], _ = timed(bwd_only, args.steps, 1)
     # Context measurements below never keep the line from being printed.
     try:
-        probe_ws = torch.empty(256 * 512 * 4, dtype=torch.uint8, device=dev)
-        probe = lambda zero, steps: flce.flce_probe_mfma_rate(zero, steps, probe_ws.data_ptr(),
+        probe_ws = torch.empty(256 * 512 * 4 + (2 << 20), dtype=torch.uint8, device=dev)
+        probe = lambda mode, steps: flce.flce_probe_mfma_rate(mode, steps, probe_ws.data_ptr(),
                                                               probe_ws.numel(), stream)
-        probe(False, 20000)  # warm-up: let the clock settle under this load
+        probe(flce.PROBE_REGISTERS, 20000)  # warm-up: let the clock settle under this load
         sustained = {
-            "random_tflops": probe(False, 120000),
-            "zero_tflops": probe(True, 120000),
-            "what": "register-only 4 x 2 v_mfma_f32_32x32x16_bf16 wave tile, 2 waves per SIMD, "
-                    "one block per CU, operands uniform in [-2, 2) or zero",
+            "random_tflops": probe(flce.PROBE_REGISTERS, 120000),
+            "zero_tflops": probe(flce.PROBE_ZEROS, 120000),
+            "lds_tflops": probe(flce.PROBE_LDS, 120000),
+            "lds_dma_tflops": probe(flce.PROBE_LDS_DMA, 120000),
+            "what": "4 x 2 v_mfma_f32_32x32x16_bf16 wave tile, 2 waves per SIMD, one block per "
+                    "CU: operands in registers, uniform in [-2, 2) (random) or zero; random "
+                    "with the fragments read from LDS (lds); and with the 32 KiB-per-K-block "
+                    "global->LDS DMA of a 256 x 256 tile from L2 added (lds_dma)",
         }
         out["mfma_sustained"] = sustained
         if out["roofline"]["achieved"]:
             out["roofline"]["frac_of_sustained"] = (out["roofline"]["achieved"]
                                                     / sustained["random_tflops"])
+            out["roofline"]["frac_of_lds_dma_probe"] = (out["roofline"]["achieved"]
+                                                        / sustained["lds_dma_tflops"])
     except Exception as exc:
         out["mfma_sustained"] = {"error": str(exc)[:200]}
     if args.path == "recompute" and args.alt_fused:

@@ -347,17 +347,25 @@ int flce_profile_kinds(void);
 flce_status_t flce_profile_read(int kind, const char** name, int64_t* launches, double* total_ms);
 
 /* Measurement hook, for context in benchmarks: the bf16 MFMA rate (TFLOP/s,
- * in *tflops) that this device sustains in the GEMM kernels' wave tile with no
- * memory traffic at all: one 512-thread block per CU (two waves per SIMD), each
- * wave running `steps` (4 <= steps <= 2^24, rounded down to a multiple of 4)
- * 16-wide K steps of 4 x 2 v_mfma_f32_32x32x16_bf16 on operands held in
- * registers, pseudo-random bf16 in [-2, 2) (zero_operands = 0) or zeros (1).
+ * in *tflops) that this device sustains in the GEMM kernels' wave tile: one
+ * 512-thread block per CU (two waves per SIMD), each wave running `steps`
+ * (4 <= steps <= 2^24, rounded down to a multiple of 4) 16-wide K steps of
+ * 4 x 2 v_mfma_f32_32x32x16_bf16, with the GEMM kernels' data movement added
+ * by `mode`:
+ *   0  operands held in registers, pseudo-random bf16 in [-2, 2);
+ *   1  the same with zero operands;
+ *   2  mode 0 with each step's six operand fragments read from LDS
+ *      (ds_read_b128);
+ *   3  mode 2 plus the global -> LDS DMA of a 256 x 256 block tile (32 KiB per
+ *      block per 32-deep K block) from a 2 MiB window that stays in L2.
  * The published dense peak assumes a clock that the matrix cores hold on
- * zero operands but not under the power they draw on varying data.
- * workspace: device, at least 256 * 512 * 4 bytes (scratch for the results).
- * Synchronises `stream`. */
-flce_status_t flce_probe_mfma_rate(int zero_operands, int64_t steps, double* tflops,
-                                   void* workspace, size_t workspace_bytes, void* stream);
+ * zero operands but not under the power they draw on varying data; modes 2
+ * and 3 show what the LDS and L2 traffic of the tile costs on top.
+ * workspace: device, 16-byte aligned, at least 256 * 512 * 4 bytes (results)
+ * plus 2 MiB for mode 3 (the DMA window, filled here). Synchronises `stream`.
+ * FLCE_ERR_BAD_OPTION for another mode. */
+flce_status_t flce_probe_mfma_rate(int mode, int64_t steps, double* tflops, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

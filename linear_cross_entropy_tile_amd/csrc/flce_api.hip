@@ -1275,13 +1275,23 @@ const char* flce_status_string(flce_status_t s) {
 
 int flce_version(void) { return 211; }
 
-flce_status_t flce_probe_mfma_rate(int zero_operands, int64_t steps, double* tflops,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+flce_status_t flce_probe_mfma_rate(int mode, int64_t steps, double* tflops, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
   if (tflops == nullptr || workspace == nullptr) return FLCE_ERR_NULL_POINTER;
+  if (mode < 0 || mode > 3) return FLCE_ERR_BAD_OPTION;
   if (steps < 4 || steps > ((int64_t)1 << 24)) return FLCE_ERR_BAD_SHAPE;
   const int blocks = kNumCUs;
-  if (workspace_bytes < (size_t)blocks * kThreads * 4) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  const size_t out_bytes = (size_t)blocks * kThreads * 4;
+  const size_t win_bytes = (size_t)2 << 20;  // the DMA source window of mode 3
+  if (workspace_bytes < out_bytes + (mode == 3 ? win_bytes : 0)) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(workspace)) return FLCE_ERR_MISALIGNED;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  float* out = static_cast<float*>(workspace);
+  uint16_t* win = reinterpret_cast<uint16_t*>(wsp(workspace, out_bytes));
+  if (mode == 3) {
+    probe_fill_kernel<<<1024, 256, 0, st>>>(win, (int64_t)(win_bytes / 2));
+    if (hipGetLastError() != hipSuccess) return FLCE_ERR_HIP;
+  }
   const int n = (int)(steps / 4 * 4);
   hipEvent_t a = nullptr, b = nullptr;
   if (hipEventCreate(&a) != hipSuccess) return FLCE_ERR_HIP;
@@ -1292,8 +1302,12 @@ flce_status_t flce_probe_mfma_rate(int zero_operands, int64_t steps, double* tfl
   float ms = 0.f;
   bool ok = hipEventRecord(a, st) == hipSuccess;
   if (ok) {
-    mfma_probe_kernel<<<blocks, kThreads, 0, st>>>(n, zero_operands != 0,
-                                                   static_cast<float*>(workspace));
+    switch (mode) {
+      case 0: mfma_probe_kernel<0><<<blocks, kThreads, 0, st>>>(n, 0, out, win); break;
+      case 1: mfma_probe_kernel<0><<<blocks, kThreads, 0, st>>>(n, 1, out, win); break;
+      case 2: mfma_probe_kernel<2><<<blocks, kThreads, 0, st>>>(n, 0, out, win); break;
+      default: mfma_probe_kernel<3><<<blocks, kThreads, 0, st>>>(n, 0, out, win); break;
+    }
     ok = hipGetLastError() == hipSuccess && hipEventRecord(b, st) == hipSuccess &&
          hipEventSynchronize(b) == hipSuccess && hipEventElapsedTime(&ms, a, b) == hipSuccess;
   }

@@ -1438,14 +1438,28 @@ __device__ __forceinline__ bf16x8_t probe_frag(uint32_t c, bool zero) {
   return __builtin_bit_cast(bf16x8_t, w);
 }
 
-// Register-only throughput of the GEMM kernels' wave tile: `steps` 16-wide K
-// steps of 4 x 2 v_mfma_f32_32x32x16_bf16 per wave (two waves per SIMD, as in
-// the GEMM kernels), cycling through four operand sets held in registers; no
-// memory traffic in the loop. The accumulators are summed into out (one float
-// per thread) so that nothing is elided.
+// Throughput of the GEMM kernels' wave tile (`steps` 16-wide K steps of
+// 4 x 2 v_mfma_f32_32x32x16_bf16 per wave, two waves per SIMD, one block per
+// CU) with the GEMM kernels' data movement added piece by piece (the
+// template argument is the mode; mode 1 runs the mode-0 code with `zero`):
+//   mode 0  operands in registers, pseudo-random, four sets cycled;
+//   mode 1  the same with zero operands (a run-time flag, so the compiler
+//           cannot fold the products);
+//   mode 2  mode 0 with every step's six operand fragments read from LDS
+//           (ds_read_b128, as the blocked operands are), 32 KiB of random data;
+//   mode 3  mode 2 plus the global -> LDS DMA of a 256 x 256 block tile,
+//           32 KiB per block per 32-deep K block (1 KiB pieces), from a 2 MiB
+//           window of `src` that all blocks share, so it stays in L2.
+// No result depends on the loaded data; the accumulators are summed into
+// out (one float per thread) so that nothing is elided.
+template <int MODE>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(2, 2)))
-mfma_probe_kernel(int steps, int zero, float* __restrict__ out) {
+mfma_probe_kernel(int steps, int zero, float* __restrict__ out, const uint16_t* __restrict__ src) {
+  constexpr bool kLds = MODE >= 2;
+  __shared__ __attribute__((aligned(1024))) char fr[kLds ? kBlockBytes * 2 : 16];
+  __shared__ __attribute__((aligned(1024))) char dm[MODE == 3 ? kBlockBytes * 2 : 16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint32_t id = blockIdx.x * kThreads + threadIdx.x;
   bf16x8_t a[4][4], b[4][2];
 #pragma unroll
@@ -1454,6 +1468,13 @@ mfma_probe_kernel(int steps, int zero, float* __restrict__ out) {
     for (int i = 0; i < 4; ++i) a[s][i] = probe_frag(id * 24u + (uint32_t)(s * 6 + i), zero != 0);
 #pragma unroll
     for (int j = 0; j < 2; ++j) b[s][j] = probe_frag(id * 24u + (uint32_t)(s * 6 + 4 + j), zero != 0);
+  }
+  if constexpr (kLds) {
+    // 64 bytes of random fragments per thread.
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<bf16x8_t*>(fr + threadIdx.x * 64 + q * 16) = probe_frag(id * 4u + q + 7u, false);
+    __syncthreads();
   }
   Acc acc;
 #pragma unroll
@@ -1464,13 +1485,41 @@ mfma_probe_kernel(int steps, int zero, float* __restrict__ out) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   for (int t = 0; t < steps; t += 4) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < 4; ++s) {
+      if constexpr (MODE == 3) {
+        if ((s & 1) == 0) {
+          // One 32-deep K block every two steps: 4 KiB per wave in 1 KiB pieces.
+          const uint32_t kb = (uint32_t)((t + s) >> 1) & 63u;  // 64 x 32 KiB = 2 MiB window
+          const __amdgpu_buffer_rsrc_t rs =
+              make_rsrc(src + (size_t)kb * (2 * kBlockElems), 2 * kBlockBytes);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (lds_void_t*)(dm + (w * 4 + q) * 1024), 16,
+                (uint32_t)((w * 4 + q) * 1024 + lane * 16), 0, 0, 0);
+          wait_vmcnt<8>();
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s][i], b[s][j], acc[i][j], 0, 0, 0);
+      if constexpr (kLds) {
+        // Next use of this operand set: six fragments from LDS (distinct
+        // 1 KiB rows per instruction, 16 consecutive bytes per lane).
+        const int o = (((t + s) * 6) & 31) * 1024 + lane * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a[s][i] = *reinterpret_cast<const bf16x8_t*>(fr + ((o + i * 1024) & (2 * kBlockBytes - 1)));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          b[s][j] =
+              *reinterpret_cast<const bf16x8_t*>(fr + ((o + (4 + j) * 1024) & (2 * kBlockBytes - 1)));
+      }
+    }
   }
+  if constexpr (MODE == 3) wait_vmcnt<0>();
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -1479,6 +1528,14 @@ mfma_probe_kernel(int steps, int zero, float* __restrict__ out) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sum += acc[i][j][r];
   out[id] = sum;
+}
+
+// Fills n 16-bit values with pseudo-random bf16 bit patterns in [-2, 2).
+__global__ void __launch_bounds__(256) probe_fill_kernel(uint16_t* __restrict__ p, int64_t n) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const uint32_t x = probe_hash((uint32_t)e * 2654435761u + 12345u);
+    p[e] = (uint16_t)(bf16_bits((float)(x >> 8) * (4.f / 16777216.f) - 2.f));
+  }
 }
 
 // Writes zeros (used for empty inputs; a kernel rather than a memset so the

@@ -266,12 +266,15 @@ def flce_profile_read(kind: int):
     return name.value.decode(), n.value, ms.value
 
 
-def flce_probe_mfma_rate(zero_operands: bool, steps: int, workspace, workspace_bytes,
-                         stream) -> float:
-    """Sustained bf16 MFMA TFLOP/s of the GEMM wave tile with no memory traffic
-    (synchronises the stream)."""
+PROBE_REGISTERS, PROBE_ZEROS, PROBE_LDS, PROBE_LDS_DMA = 0, 1, 2, 3
+
+
+def flce_probe_mfma_rate(mode, steps: int, workspace, workspace_bytes, stream) -> float:
+    """Sustained bf16 MFMA TFLOP/s of the GEMM wave tile (synchronises the
+    stream). mode: PROBE_REGISTERS (or False), PROBE_ZEROS (or True),
+    PROBE_LDS, PROBE_LDS_DMA; see include/flce.h."""
     t = ctypes.c_double(0.0)
-    _check(lib().flce_probe_mfma_rate(1 if zero_operands else 0, steps, ctypes.byref(t), workspace,
+    _check(lib().flce_probe_mfma_rate(int(mode), steps, ctypes.byref(t), workspace,
                                       workspace_bytes, stream), "flce_probe_mfma_rate")
     return t.value
 
