@@ -221,3 +221,37 @@ def test_fused_mostly_ignored_chunks():
             e = G.rel_l2(out[what].float().cpu().numpy(), ref)
             assert e <= G.GRAD_REL_L2, f"{what} rel L2 {e:.2e}"
     assert torch.equal(outs[0]["lse"], outs[1]["lse"])
+
+
+def test_fused_full_size_class_weights():
+    """The fused call on the Gemma2-shaped head with the seeded class weights
+    of the stored variant gemma2_softcap_weighted: weighted means and sampled
+    gradient rows / columns against those stored oracle values."""
+    name = "gemma2_softcap_weighted"
+    path = os.path.join(HERE, "golden", f"{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    import sys
+    sys.path.insert(0, os.path.join(HERE, "golden"))
+    import make_golden
+    ref = np.load(path)
+    wl = W.WORKLOADS[make_golden.WEIGHTED[name][0]]
+    print(f"[fused full] {name} N={wl.N} H={wl.H} V={wl.V}", flush=True)
+    x = W.make_inputs(wl)
+    t = G.upload(x)
+    cw = torch.from_numpy(make_golden.class_weights(name)).to(G.dev())
+    out = flce.forward_backward(t["hidden"], t["weight"], t["labels"], t["grad_logprob"],
+                                t["grad_entropy"], ignore_index=wl.ignore_index,
+                                softcap=wl.softcap, reduction=wl.reduction, class_weight=cw)
+    torch.cuda.synchronize()
+    for k in ("lse", "logprob", "entropy", "logprob_mean", "entropy_mean"):
+        e = G.stat_err(out[k].cpu().numpy(), ref[k])
+        assert e <= 1.0, f"{name} {k}: error {e:.3f} x tolerance"
+    rows = torch.from_numpy(ref["rows"]).to(G.dev())
+    cols = torch.from_numpy(ref["cols"]).to(G.dev())
+    e = G.rel_l2(out["grad_hidden"].index_select(0, rows).float().cpu().numpy(),
+                 ref["dhidden_rows"])
+    assert e <= G.GRAD_REL_L2, f"{name} grad_hidden rows rel L2 {e:.2e}"
+    e = G.rel_l2(out["grad_weight"].index_select(1, cols).float().cpu().numpy(),
+                 ref["dweight_cols"])
+    assert e <= G.GRAD_REL_L2, f"{name} grad_weight cols rel L2 {e:.2e}"
