@@ -12,7 +12,11 @@
  *     and logprob = z_y - lse with the logits z recomputed here in double
  *     from the same bf16 inputs;
  *   - the invalid-label count of flce_get_status, and host-side argument
- *     errors (misaligned pointer, bad reduction, too small a workspace).
+ *     errors (misaligned pointer, bad reduction, too small a workspace);
+ *   - class weights through flce_forward_ex (the options struct built in C):
+ *     with 0/1 weights the weighted mean of logprob equals the plain mean over
+ *     the tokens of weight 1, computed here from the per-token outputs of the
+ *     same call; class weights under reduction NONE are refused.
  *
  * Prints "flce_c_check ok" and returns 0 on success, 1 on the first failure.
  */
@@ -173,10 +177,68 @@ static int run(int zero_weight) {
   return 0;
 }
 
+static int run_class_weights(void) {
+  static uint16_t hh[N * H], hw[H * V];
+  static int64_t hy[N];
+  static float hcw[V], hlp[N], hred[4];
+  for (int i = 0; i < N * H; ++i) hh[i] = bf16(urand());
+  for (int i = 0; i < H * V; ++i) hw[i] = bf16(0.25f * urand());
+  for (int j = 0; j < V; ++j) hcw[j] = (j % 3 == 0) ? 0.f : 1.f;
+  for (int i = 0; i < N; ++i) {
+    lcg = lcg * 1664525u + 1013904223u;
+    hy[i] = (int64_t)((lcg >> 8) % V);
+  }
+  hy[11] = -100;
+  void *dh, *dw, *ws;
+  int64_t* dy;
+  float *dcw, *dlse, *dlp, *dent, *dred;
+  size_t fb = 0;
+  FLCK(flce_workspace_size(N, H, V, FLCE_REDUCTION_MEAN, &fb, NULL));
+  HIPCK(hipMalloc(&dh, sizeof hh));
+  HIPCK(hipMalloc(&dw, sizeof hw));
+  HIPCK(hipMalloc((void**)&dy, sizeof hy));
+  HIPCK(hipMalloc((void**)&dcw, sizeof hcw));
+  HIPCK(hipMalloc((void**)&dlse, sizeof hlp));
+  HIPCK(hipMalloc((void**)&dlp, sizeof hlp));
+  HIPCK(hipMalloc((void**)&dent, sizeof hlp));
+  HIPCK(hipMalloc((void**)&dred, sizeof hred));
+  HIPCK(hipMalloc(&ws, fb));
+  HIPCK(hipMemcpy(dh, hh, sizeof hh, hipMemcpyHostToDevice));
+  HIPCK(hipMemcpy(dw, hw, sizeof hw, hipMemcpyHostToDevice));
+  HIPCK(hipMemcpy(dy, hy, sizeof hy, hipMemcpyHostToDevice));
+  HIPCK(hipMemcpy(dcw, hcw, sizeof hcw, hipMemcpyHostToDevice));
+  hipStream_t st;
+  HIPCK(hipStreamCreate(&st));
+  flce_options_t opt = {.ignore_index = -100, .softcap = 0.f, .reduction = FLCE_REDUCTION_NONE,
+                        .z_loss_scale = 0.f, .grad_dtype = FLCE_GRAD_BF16, .class_weight = dcw};
+  CHECK(flce_forward_ex(dh, dw, dy, N, H, V, &opt, dlse, dlp, dent, NULL, NULL, NULL, ws, fb, st) ==
+            FLCE_ERR_BAD_OPTION, "class weights under reduction none");
+  opt.reduction = FLCE_REDUCTION_MEAN;
+  FLCK(flce_forward_ex(dh, dw, dy, N, H, V, &opt, dlse, dlp, dent, NULL, NULL, dred, ws, fb, st));
+  HIPCK(hipStreamSynchronize(st));
+  HIPCK(hipMemcpy(hlp, dlp, sizeof hlp, hipMemcpyDeviceToHost));
+  HIPCK(hipMemcpy(hred, dred, sizeof hred, hipMemcpyDeviceToHost));
+  double sum = 0.0;
+  int count = 0;
+  for (int i = 0; i < N; ++i)
+    if (hy[i] >= 0 && hcw[hy[i]] != 0.f) {
+      sum += hlp[i];
+      ++count;
+    }
+  const double want = count ? sum / count : 0.0;
+  CHECK(count > 0 && fabs(hred[0] - want) <= 1e-5 * (1.0 + fabs(want)),
+        "weighted logprob mean %g, mean over weight-1 tokens %g", hred[0], want);
+  hipFree(dh); hipFree(dw); hipFree(dy); hipFree(dcw); hipFree(dlse); hipFree(dlp);
+  hipFree(dent); hipFree(dred); hipFree(ws);
+  hipStreamDestroy(st);
+  return 0;
+}
+
 int main(void) {
   printf("libflce version %d\n", flce_version());
   if (run(1)) return 1;
   if (run(0)) return 1;
+  if (run_class_weights()) return 1;
   printf("flce_c_check ok\n");
   return 0;
 }
