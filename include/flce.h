@@ -300,7 +300,9 @@ flce_status_t flce_backward_shard(const void* hidden, const void* weight_shard,
  * rounding of the kept logits (bf16 of z' - m), not bit for bit.
  *
  * chunk_tokens: tokens per chunk Nc (rounded up to 256); 0 picks 8192, or all
- * tokens when N <= 8192 + H (then chunking would not save memory). V <= 2^21.
+ * tokens when N <= 8192 + H (then chunking would not save memory; the chunk
+ * images then hold every logit of the call, 4 bytes each: pass a smaller
+ * chunk_tokens to bound them). V <= 2^21.
  * Workspace bytes for this shape, options and chunk_tokens (host only): */
 flce_status_t flce_fused_workspace_size(int64_t N, int64_t H, int64_t V, const flce_options_t* opt,
                                         int64_t chunk_tokens, size_t* bytes);
