@@ -64,8 +64,12 @@
  *     flce_get_status and flce_profile_read, which say so.
  *   - Matrices are dense and row-major. bf16 means IEEE bfloat16 bits (uint16).
  *   - Alignment: hidden, weight, grad_hidden, grad_weight and the workspace
- *     must be 16-byte aligned, and H and V must be multiples of 8
- *     (FLCE_ERR_MISALIGNED otherwise). N, H and V need no other multiple.
+ *     must be 16-byte aligned, and H must be a multiple of 8
+ *     (FLCE_ERR_MISALIGNED otherwise). V may take any value; when it is not a
+ *     multiple of 8 the weight is read from a copy with 16-byte aligned rows
+ *     and dW is formed in a buffer of that row stride and copied out (both in
+ *     the workspace; flce_workspace_size counts them). flce_forward_backward
+ *     alone needs V a multiple of 8. N, H and V need no other multiple.
  *   - Argument errors are detected on the host before anything is enqueued;
  *     then nothing is launched and no output is touched. A failed launch
  *     returns FLCE_ERR_HIP. No C++ exception crosses this interface.

@@ -50,10 +50,16 @@ struct Plan {
   int dw_splits;       // split over tokens of the dW contraction
   int dw_kper;         // K blocks per dW split
   int group;           // tile rows per XCD patch of the block -> tile map
+  // A vocabulary that is not a multiple of 8: the weight is copied with rows
+  // of V8 = V rounded up to 8 (zero columns past V), and dW is formed in a
+  // buffer of the same row stride and copied out.
+  bool padw;
+  int64_t V8;
   // forward workspace
-  size_t f_idx, f_labc, f_part, f_zlab, f_bsum, f_xb, f_total;
+  size_t f_idx, f_labc, f_part, f_zlab, f_bsum, f_xb, f_wp, f_total;
   // backward workspace
-  size_t b_lab, b_idx, b_coef, b_wb, b_xb, b_xtb, b_dtv, b_dvt, b_acc, b_part, b_total;
+  size_t b_lab, b_idx, b_coef, b_wb, b_xb, b_xtb, b_dtv, b_dvt, b_acc, b_part, b_wp, b_gwp,
+      b_total;
 };
 
 size_t env_size(const char* name, size_t dflt) {
@@ -73,6 +79,8 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   p.VT = (int)ceil_div(V, kTile);
   p.HT = (int)ceil_div(H, kTile);
   p.hkb = (int)ceil_div(H, kBK);
+  p.V8 = ceil_div(V, 8) * 8;
+  p.padw = p.V8 != V;
   p.nkb = p.TB * (kTile / kBK);
   // The vocabulary is processed in chunks of Vc columns: the weight images
   // are built per chunk, and the backward's two bf16 images of the logit
@@ -137,6 +145,8 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
   off = align_up(off + (reduction != FLCE_REDUCTION_NONE ? 32 * (size_t)ceil_div(N, kCombineTokens) : 0));
   p.f_xb = off;
   off = align_up(off + blk * (size_t)p.TB * (size_t)p.hkb);
+  p.f_wp = off;
+  off = align_up(off + (p.padw ? 2 * (size_t)H * (size_t)p.V8 : 0));
   p.f_total = off;
 
   off = kHeaderBytes;
@@ -161,6 +171,11 @@ Plan make_plan(int64_t N, int64_t H, int64_t V, int reduction) {
                             ? 4 * (size_t)p.dx_splits * (size_t)N * (size_t)H : 0));
   p.b_part = off;
   off = align_up(off + (p.dw_splits > 1 ? 4 * (size_t)p.dw_splits * (size_t)H * (size_t)p.Vc : 0));
+  // Padded weight copy and padded dW (room for fp32 gradients).
+  p.b_wp = off;
+  off = align_up(off + (p.padw ? 2 * (size_t)H * (size_t)p.V8 : 0));
+  p.b_gwp = off;
+  off = align_up(off + (p.padw ? 4 * (size_t)H * (size_t)p.V8 : 0));
   p.b_total = off;
   return p;
 }
@@ -251,10 +266,11 @@ FusedPlan make_fused_plan(int64_t N, int64_t H, int64_t V, const flce_options_t&
   return f;
 }
 
-flce_status_t check_shape(int64_t N, int64_t H, int64_t V) {
+// H must be a multiple of 8; so must V for the fused call (any_v false).
+flce_status_t check_shape(int64_t N, int64_t H, int64_t V, bool any_v = true) {
   if (N < 0 || H < 1 || V < 1) return FLCE_ERR_BAD_SHAPE;
   if (N > kMaxN || H > kMaxH || V > kMaxV) return FLCE_ERR_BAD_SHAPE;
-  if (H % 8 != 0 || V % 8 != 0) return FLCE_ERR_MISALIGNED;
+  if (H % 8 != 0 || (!any_v && V % 8 != 0)) return FLCE_ERR_MISALIGNED;
   return FLCE_OK;
 }
 
@@ -378,6 +394,30 @@ flce_status_t pack_cols(int kind, const void* src, int64_t R, int64_t K, int64_t
   return launch(kind, st, [&] {
     pack_cols_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(src), R, K, ld, nkb,
                                            gather, count, dst);
+  });
+}
+
+// dst [rows, ldd] = src [rows, cols] with zero columns past cols.
+flce_status_t pad_cols(const void* src, int64_t rows, int64_t cols, int64_t ldd, void* dst,
+                       hipStream_t st) {
+  const int64_t n = rows * ldd;
+  const int blocks = (int)(ceil_div(n, 256) < 16384 ? ceil_div(n, 256) : 16384);
+  return launch(K_FILL, st, [&] {
+    pad_cols_kernel<<<blocks, 256, 0, st>>>(static_cast<const uint16_t*>(src), rows, cols, ldd,
+                                            static_cast<uint16_t*>(dst));
+  });
+}
+
+// dst [rows, cols] = the first cols columns of src [rows, lds] (2- or 4-byte elements).
+flce_status_t unpad_cols(const void* src, int64_t rows, int64_t lds, int64_t cols, void* dst,
+                         bool f32, hipStream_t st) {
+  const int64_t n = rows * cols;
+  const int blocks = (int)(ceil_div(n, 256) < 16384 ? ceil_div(n, 256) : 16384);
+  return launch(K_FILL, st, [&] {
+    if (f32)
+      unpad_cols_kernel<4><<<blocks, 256, 0, st>>>(src, rows, lds, cols, dst);
+    else
+      unpad_cols_kernel<2><<<blocks, 256, 0, st>>>(src, rows, lds, cols, dst);
   });
 }
 
@@ -559,8 +599,17 @@ flce_status_t forward_impl(const void* hidden, const void* weight, const int64_t
     uint16_t* xb = reinterpret_cast<uint16_t*>(wsp(workspace, p.f_xb));
     // Only the valid tokens, compacted in token order, enter the contractions.
     FLCE_TRY(pack_rows(K_PACK_HIDDEN, hidden, N, H, H, p.hkb, idx, nvalid, xb, st));
+    // A vocabulary that is not a multiple of 8 is read from a copy whose rows
+    // are 16-byte aligned (zero columns past V, masked like any tile tail).
+    const void* wrd = weight;
+    if (p.padw) {
+      void* wp = wsp(workspace, p.f_wp);
+      FLCE_TRY(pad_cols(weight, H, V, p.V8, wp, st));
+      wrd = wp;
+    }
     FwdTileArgs a{};
-    a.weight = static_cast<const uint16_t*>(weight);
+    a.weight = static_cast<const uint16_t*>(wrd);
+    a.ldw = p.V8;
     a.xb = xb;
     a.lab = labc;
     a.nvalid = nvalid;
@@ -685,15 +734,27 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
   FLCE_TRY(pack_cols(K_PACK_HIDDEN, hidden, H, N, H, p.nkb, idx, nvalid, xtb, st));
   const float softcap = o.softcap;
   const bool capped = softcap > 0.f;
+  // A vocabulary that is not a multiple of 8: the weight is read from a copy
+  // with 16-byte aligned rows of V8 columns (zero past V) and dW is formed in
+  // a buffer of the same row stride, copied out at the end.
+  const uint16_t* wrd = static_cast<const uint16_t*>(weight);
+  void* gw_out = grad_weight;
+  if (p.padw) {
+    uint16_t* wp = reinterpret_cast<uint16_t*>(wsp(workspace, p.b_wp));
+    FLCE_TRY(pad_cols(weight, H, V, p.V8, wp, st));
+    wrd = wp;
+    gw_out = wsp(workspace, p.b_gwp);
+  }
   for (int c = 0; c < p.nchunks; ++c) {
     const int64_t v0 = (int64_t)c * p.Vc;
     const int64_t vc = V - v0 < p.Vc ? V - v0 : p.Vc;
+    const int64_t vc8 = p.V8 - v0 < p.Vc ? p.V8 - v0 : p.Vc;  // columns of the (padded) copy
     const int vtc = (int)ceil_div(vc, kTile);
-    const uint16_t* wchunk = static_cast<const uint16_t*>(weight) + v0;
-    FLCE_TRY(pack_rows(K_PACK_WEIGHT, wchunk, H, vc, V, p.kbv, nullptr, nullptr, wb, st));
+    FLCE_TRY(pack_rows(K_PACK_WEIGHT, wrd + v0, H, vc8, p.V8, p.kbv, nullptr, nullptr, wb, st));
 
     DlogitsArgs d{};
-    d.weight = static_cast<const uint16_t*>(weight);
+    d.weight = wrd;
+    d.ldw = p.V8;
     d.xb = xb;
     d.coef = coef;
     d.lab = lab32;
@@ -765,7 +826,8 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
     w.splits = p.dw_splits;
     w.group = p.group;
     w.kper = p.dw_kper;
-    w.gw = grad_weight;
+    w.gw = gw_out;
+    w.ldo = p.V8;
     w.part = part;
     const int gw = p.HT * vtc * p.dw_splits;
     if (combine_dxdw(p, x.nk, gx, gw)) {
@@ -788,14 +850,15 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
       const int blocks = (int)(ceil_div(n, 256) < 8192 ? ceil_div(n, 256) : 8192);
       FLCE_TRY(launch(K_DW_REDUCE, st, [&] {
         if (f32)
-          dw_reduce_kernel<true><<<blocks, 256, 0, st>>>(part, p.dw_splits, H, vc, p.Vc, V, v0,
-                                                         grad_weight);
+          dw_reduce_kernel<true><<<blocks, 256, 0, st>>>(part, p.dw_splits, H, vc, p.Vc, p.V8,
+                                                         v0, gw_out);
         else
-          dw_reduce_kernel<false><<<blocks, 256, 0, st>>>(part, p.dw_splits, H, vc, p.Vc, V, v0,
-                                                          grad_weight);
+          dw_reduce_kernel<false><<<blocks, 256, 0, st>>>(part, p.dw_splits, H, vc, p.Vc, p.V8,
+                                                          v0, gw_out);
       }));
     }
   }
+  if (p.padw) FLCE_TRY(unpad_cols(gw_out, H, p.V8, V, grad_weight, f32, st));
   return FLCE_OK;
 }
 
@@ -889,6 +952,7 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
 
       FwdTileArgs a{};
       a.weight = static_cast<const uint16_t*>(weight);
+      a.ldw = V;  // V is a multiple of 8 here
       a.xb = xb;
       a.lab = labc;
       a.nvalid = nvalid;
@@ -1015,6 +1079,7 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
       w.kper = w.kbn;
       w.ldp = 0;
       w.gw = grad_weight;
+      w.ldo = V;
       w.part = nullptr;
       w.accw = dwacc;
       w.rows = rows;
@@ -1105,7 +1170,7 @@ flce_status_t flce_backward_ex(const void* hidden, const void* weight, const int
 
 flce_status_t flce_fused_workspace_size(int64_t N, int64_t H, int64_t V, const flce_options_t* opt,
                                         int64_t chunk_tokens, size_t* bytes) {
-  FLCE_TRY(check_shape(N, H, V));
+  FLCE_TRY(check_shape(N, H, V, false));
   FLCE_TRY(check_options(opt));
   if (V > kMaxVF32 || chunk_tokens < 0) return FLCE_ERR_BAD_SHAPE;
   if (bytes) *bytes = make_fused_plan(N, H, V, *opt, chunk_tokens).total;
@@ -1120,7 +1185,7 @@ flce_status_t flce_forward_backward(const void* hidden, const void* weight, cons
                                     float* entropy, float* uniform_ce, float* z_loss,
                                     float* reduced, void* grad_hidden, void* grad_weight,
                                     void* workspace, size_t workspace_bytes, void* stream) {
-  FLCE_TRY(check_shape(N, H, V));
+  FLCE_TRY(check_shape(N, H, V, false));
   FLCE_TRY(check_options(opt));
   return fused_impl(hidden, weight, labels, N, H, V, *opt, chunk_tokens, grad_logprob,
                     grad_entropy, grad_uniform_ce, grad_z_loss, lse, logprob, entropy, uniform_ce,
@@ -1263,7 +1328,8 @@ const char* flce_status_string(flce_status_t s) {
     case FLCE_ERR_NULL_POINTER: return "a required pointer is NULL";
     case FLCE_ERR_BAD_SHAPE: return "bad shape (need N >= 0, H >= 1, V >= 1 within limits)";
     case FLCE_ERR_BAD_REDUCTION: return "reduction must be NONE (0), MEAN (1) or SUM (2)";
-    case FLCE_ERR_MISALIGNED: return "pointers must be 16-byte aligned and H, V multiples of 8";
+    case FLCE_ERR_MISALIGNED:
+      return "pointers must be 16-byte aligned, H a multiple of 8 (and V for the fused call)";
     case FLCE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than flce_workspace_size";
     case FLCE_ERR_BAD_SOFTCAP: return "softcap must be finite";
     case FLCE_ERR_HIP: return "HIP runtime error or failed kernel launch";

@@ -33,6 +33,7 @@
 #pragma once
 
 #include "flce_gemm.hpp"
+#include <type_traits>
 
 namespace flce {
 
@@ -250,7 +251,9 @@ __global__ void __launch_bounds__(256) pack_cols_kernel(const uint16_t* __restri
 // ---- forward: fused logit tiles + online row statistics ---------------------
 
 struct FwdTileArgs {
-  const uint16_t* weight;  // [H,V]
+  const uint16_t* weight;  // [H,V], rows ldw apart
+  int64_t ldw;             // row stride of weight (V, or V rounded up to 8 for a padded copy
+                           // whose extra columns are zero)
   const uint16_t* xb;      // blocked hidden: strips of 256 tokens, K = H
   const int32_t* lab;      // [N] compacted label codes (label logit captured when >= 0)
   const int32_t* nvalid;   // device: number n of compacted tokens
@@ -388,7 +391,7 @@ __device__ __forceinline__ void fwd_tile_body(const FwdTileArgs& a) {
   {
     MainloopRowA ml;
     RowA A;
-    A.init(a.weight, a.V, a.V, (int64_t)vt * kTile, 0, a.H);
+    A.init(a.weight, a.ldw, a.ldw, (int64_t)vt * kTile, 0, a.H);
     ml.run(sa, sb, A, Strip{a.xb + (int64_t)tb * a.hkb * kBlockElems, a.hkb}, 0, a.hkb, acc);
   }
 
@@ -813,7 +816,8 @@ __global__ void __launch_bounds__(256) zero_ignored_rows_kernel(const int64_t* _
 // ---- backward: recompute logits, form the logit gradient ----------------------
 
 struct DlogitsArgs {
-  const uint16_t* weight;  // [H,V]
+  const uint16_t* weight;  // [H,V], rows ldw apart (see FwdTileArgs)
+  int64_t ldw;
   const uint16_t* xb;      // blocked hidden
   const DzToken* coef;     // [N] compacted tokens
   const int32_t* lab;      // [N] compacted label offsets in the slice (-1: none)
@@ -962,7 +966,7 @@ bwd_dlogits_kernel(DlogitsArgs a) {
   {
     MainloopRowA ml;
     RowA A;
-    A.init(a.weight, a.V, a.V, vg0, 0, a.H);
+    A.init(a.weight, a.ldw, a.ldw, vg0, 0, a.H);
     ml.run(sa, sb, A, Strip{a.xb + (int64_t)tb * a.hkb * kBlockElems, a.hkb}, 0, a.hkb, acc);
   }
 
@@ -1254,7 +1258,9 @@ struct DwArgs {
   int group;
   int kper;                // K blocks per split
   int64_t ldp;             // row stride of the split partials
-  void* gw;                // [H,V] output, bf16 or fp32 (F32OUT)
+  void* gw;                // [H,V] output, bf16 or fp32 (F32OUT), rows ldo apart
+  int64_t ldo;             // row stride of gw and accw (V, or V rounded up to 8 when the
+                           // output goes to a padded buffer)
   float* part;             // [splits][H][ldp] fp32 (DW_SPLIT)
   float* accw;             // [H,V] fp32 accumulator over chunks (DW_CHUNK; grad_weight
                            // itself when F32OUT)
@@ -1272,7 +1278,7 @@ __device__ __forceinline__ void dw_store_tile(const Acc& acc, const DwArgs& a, i
     base = ((int64_t)sp * a.H + h0) * ld + vl0;
     span = (a.H - h0) * ld - vl0;
   } else {
-    ld = a.V;
+    ld = a.ldo;
     base = h0 * ld + a.v0 + vl0;
     span = (a.H - h0) * ld - (a.v0 + vl0);
   }
@@ -1284,7 +1290,9 @@ __device__ __forceinline__ void dw_store_tile(const Acc& acc, const DwArgs& a, i
       fdst != nullptr ? make_rsrc(fdst + base, span * 4)
                       : make_rsrc(static_cast<char*>(a.gw) + base * kOut, span * kOut);
   const __amdgpu_buffer_rsrc_t racc = kRead ? make_rsrc(a.accw + base, span * 4) : rs;
-  // Quad transposes as in bwd_dx_kernel; vc is a multiple of 8.
+  // Quad transposes as in bwd_dx_kernel. A quad at vq < vc may reach past vc
+  // (vc not a multiple of 4) only into a padded output, whose row stride ldo
+  // is vc rounded up to 8 and whose extra columns are never read back.
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int vq = acc_col(wn, j, lane) & ~3;
@@ -1396,16 +1404,16 @@ bwd_dxdw_kernel(DxArgs x, DwArgs w) {
 template <bool F32OUT>
 __global__ void __launch_bounds__(256) dw_reduce_kernel(const float* __restrict__ part, int splits,
                                                         int64_t H, int64_t vc, int64_t ldd,
-                                                        int64_t V, int64_t v0, void* gw) {
+                                                        int64_t ldo, int64_t v0, void* gw) {
   const int64_t n = H * vc;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
     const int64_t h = e / vc, v = e % vc;
     float s = 0.f;
     for (int k = 0; k < splits; ++k) s += part[((int64_t)k * H + h) * ldd + v];
     if constexpr (F32OUT)
-      static_cast<float*>(gw)[h * V + v0 + v] = s;
+      static_cast<float*>(gw)[h * ldo + v0 + v] = s;
     else
-      static_cast<uint16_t*>(gw)[h * V + v0 + v] = (uint16_t)(pack_bf16x2(s, 0.f) & 0xFFFFu);
+      static_cast<uint16_t*>(gw)[h * ldo + v0 + v] = (uint16_t)(pack_bf16x2(s, 0.f) & 0xFFFFu);
   }
 }
 
@@ -1535,6 +1543,35 @@ __global__ void __launch_bounds__(256) probe_fill_kernel(uint16_t* __restrict__ 
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
     const uint32_t x = probe_hash((uint32_t)e * 2654435761u + 12345u);
     p[e] = (uint16_t)(bf16_bits((float)(x >> 8) * (4.f / 16777216.f) - 2.f));
+  }
+}
+
+// dst [rows, ldd] = src [rows, cols] (16-bit elements) with columns cols..ldd-1
+// zero: a weight whose row length is not a multiple of 8, re-laid out so that
+// every row starts 16-byte aligned. One element per thread, grid-stride.
+__global__ void __launch_bounds__(256) pad_cols_kernel(const uint16_t* __restrict__ src,
+                                                       int64_t rows, int64_t cols, int64_t ldd,
+                                                       uint16_t* __restrict__ dst) {
+  const int64_t n = rows * ldd;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / ldd, c = e - r * ldd;
+    dst[e] = c < cols ? src[r * cols + c] : (uint16_t)0;
+  }
+}
+
+// dst [rows, cols] = the first cols columns of src [rows, lds]; elements of
+// ELEM bytes (2: bf16, 4: fp32).
+template <int ELEM>
+__global__ void __launch_bounds__(256) unpad_cols_kernel(const void* __restrict__ src, int64_t rows,
+                                                         int64_t lds, int64_t cols,
+                                                         void* __restrict__ dst) {
+  typedef typename std::conditional<ELEM == 4, uint32_t, uint16_t>::type T;
+  const T* s = static_cast<const T*>(src);
+  T* d = static_cast<T*>(dst);
+  const int64_t n = rows * cols;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / cols, c = e - r * cols;
+    d[e] = s[r * lds + c];
   }
 }
 

@@ -96,6 +96,13 @@ WORKLOADS = {
     "dw_split": Workload("dw_split", 4096, 256, 2048, seed=205, weight_std=0.1,
                          ignore="fraction", ignore_fraction=0.05,
                          grad_logprob=("normal",), grad_entropy=("normal",)),
+    # Vocabularies that are not a multiple of 8 (odd; 2 mod 8 with a split dW).
+    "odd_vocab": Workload("odd_vocab", 300, 128, 1001, seed=209, weight_std=0.1,
+                          ignore="fraction", ignore_fraction=0.1,
+                          grad_logprob=("normal",), grad_entropy=("normal",)),
+    "odd_vocab_dw_split": Workload("odd_vocab_dw_split", 2048, 64, 1002, seed=210,
+                                   weight_std=0.15, ignore="fraction", ignore_fraction=0.05,
+                                   grad_logprob=("normal",), grad_entropy=("normal",)),
     # The library's size limits, one extreme at a time (weight std 1/sqrt(H)
     # keeps the logits of order 1).
     "max_vocab": Workload("max_vocab", 64, 64, (1 << 22) - 256, seed=206, weight_std=0.125,

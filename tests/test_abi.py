@@ -80,7 +80,7 @@ def _bwd(**kw):
     (dict(H=(1 << 20) + 8), 2),
     (dict(V=(1 << 22) + 8), 2),
     (dict(red=3), 3), (dict(red=-1), 3),
-    (dict(H=12), 4), (dict(V=1001), 4), (dict(hidden=A + 2), 4), (dict(weight=A + 8), 4),
+    (dict(H=12), 4), (dict(hidden=A + 2), 4), (dict(weight=A + 8), 4),
     (dict(ws=A + 4), 4),
     (dict(wsb=16), 5),
     (dict(cap=float("nan")), 6), (dict(cap=float("inf")), 6),
@@ -94,7 +94,7 @@ def test_forward_rejects(kw, code):
     (dict(ent=None), 1), (dict(ws=None), 1),
     (dict(N=-3), 2), (dict(H=-8), 2),
     (dict(red=7), 3),
-    (dict(gh=A + 2), 4), (dict(gw=A + 2), 4), (dict(V=12), 4),
+    (dict(gh=A + 2), 4), (dict(gw=A + 2), 4), (dict(H=12), 4),
     (dict(wsb=100), 5),
     (dict(cap=float("-inf")), 6),
 ])
@@ -162,7 +162,7 @@ def _bwd_ex(opt=None, **kw):
     (dict(grad_dtype=3), {}, 9),
     (dict(class_weight=A), {}, 9),                          # class weights under "none"
     (dict(reduction=2, class_weight=A + 2), dict(red=A), 4),  # class weights not 4-byte aligned
-    (dict(), dict(N=-2), 2), (dict(), dict(V=12), 4), (dict(), dict(wsb=8), 5),
+    (dict(), dict(N=-2), 2), (dict(), dict(H=12), 4), (dict(), dict(wsb=8), 5),
 ])
 def test_forward_ex_rejects(okw, kw, code):
     assert _fwd_ex(_opt(**okw) if okw is not None else None, **kw) == code
@@ -188,6 +188,17 @@ def test_options_layout():
     assert flce.FlceOptions.class_weight.offset == 24
 
 
+def test_workspace_size_any_vocabulary():
+    # A vocabulary that is not a multiple of 8 adds the padded weight copy
+    # (forward and backward) and the padded dW buffer (backward, fp32 room).
+    H = 64
+    f0, b0 = flce.flce_workspace_size(300, H, 1000, 0)
+    f1, b1 = flce.flce_workspace_size(300, H, 1001, 0)
+    assert f1 >= f0 + 2 * H * 1008 and b1 >= b0 + 6 * H * 1008
+    with pytest.raises(flce.FlceError):
+        flce.flce_fused_workspace_size(300, H, 1001, _opt())
+
+
 def test_workspace_size_sum():
     f0, b0 = flce.flce_workspace_size(4096, 4096, 32000, 0)
     f2, b2 = flce.flce_workspace_size(4096, 4096, 32000, 2)
@@ -206,7 +217,7 @@ def _fwd_shard(opt, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(v0=-8), 2), (dict(v0=12), 2), (dict(VT=4), 2),    # slice outside [0, V_total)
-    (dict(state=None), 1), (dict(zl=None), 1), (dict(state=A + 4), 4), (dict(Vs=12), 4),
+    (dict(state=None), 1), (dict(zl=None), 1), (dict(state=A + 4), 4), (dict(H=12), 4),
 ])
 def test_forward_shard_rejects(kw, code):
     assert _fwd_shard(_opt(), **kw) == code
@@ -244,6 +255,7 @@ def _fused(opt=None, **kw):
     (dict(z_loss_scale=-1.0), {}, 9), (dict(grad_dtype=2), {}, 9),
     (dict(), dict(N=-1), 2), (dict(), dict(V=(1 << 21) + 8), 2),  # V <= 2^21
     (dict(), dict(chunk=-256), 2), (dict(), dict(H=12), 4),
+    (dict(), dict(V=12), 4),                                  # the fused call: V % 8 == 0
     (dict(), dict(lse=None), 1), (dict(), dict(gw=None), 1), (dict(), dict(ws=None), 1),
     (dict(), dict(gh=A + 8), 4), (dict(), dict(wsb=8), 5),
 ])
