@@ -68,8 +68,8 @@
  *     (FLCE_ERR_MISALIGNED otherwise). V may take any value; when it is not a
  *     multiple of 8 the weight is read from a copy with 16-byte aligned rows
  *     and dW is formed in a buffer of that row stride and copied out (both in
- *     the workspace; flce_workspace_size counts them). flce_forward_backward
- *     alone needs V a multiple of 8. N, H and V need no other multiple.
+ *     the workspace; flce_workspace_size and flce_fused_workspace_size count
+ *     them). N, H and V need no other multiple.
  *   - Argument errors are detected on the host before anything is enqueued;
  *     then nothing is launched and no output is touched. A failed launch
  *     returns FLCE_ERR_HIP. No C++ exception crosses this interface.

@@ -207,7 +207,8 @@ struct FusedPlan {
   int dx_splits;       // K splits of dH per chunk
   int kbv;             // VT * 8: K blocks of a vocabulary-long strip
   bool dw_acc;         // a separate fp32 dW accumulator
-  size_t idx, labc, zlab, part, bsum, coef, xb, xtb, wb, dtv, dvt, mref, dxacc, dwacc, total;
+  size_t idx, labc, zlab, part, bsum, coef, xb, xtb, wb, dtv, dvt, mref, dxacc, dwacc, wp, gwp,
+      total;
 };
 
 FusedPlan make_fused_plan(int64_t N, int64_t H, int64_t V, const flce_options_t& o,
@@ -261,16 +262,20 @@ FusedPlan make_fused_plan(int64_t N, int64_t H, int64_t V, const flce_options_t&
   take(f.dvt, blk * (size_t)p.VT * (size_t)tbc * (kTile / kBK));
   take(f.mref, 4 * 2 * (size_t)p.VT * crow);
   take(f.dxacc, f.dx_splits > 1 ? 4 * (size_t)f.dx_splits * crow * (size_t)H : 0);
-  take(f.dwacc, f.dw_acc ? 4 * (size_t)H * (size_t)V : 0);
+  take(f.dwacc, f.dw_acc ? 4 * (size_t)H * (size_t)p.V8 : 0);
+  // A vocabulary that is not a multiple of 8: padded weight copy and padded
+  // dW (fp32 room), as on the recompute path.
+  take(f.wp, p.padw ? 2 * (size_t)H * (size_t)p.V8 : 0);
+  take(f.gwp, p.padw ? 4 * (size_t)H * (size_t)p.V8 : 0);
   f.total = off;
   return f;
 }
 
-// H must be a multiple of 8; so must V for the fused call (any_v false).
-flce_status_t check_shape(int64_t N, int64_t H, int64_t V, bool any_v = true) {
+// H must be a multiple of 8; V may take any value (see Plan::padw).
+flce_status_t check_shape(int64_t N, int64_t H, int64_t V) {
   if (N < 0 || H < 1 || V < 1) return FLCE_ERR_BAD_SHAPE;
   if (N > kMaxN || H > kMaxH || V > kMaxV) return FLCE_ERR_BAD_SHAPE;
-  if (H % 8 != 0 || (!any_v && V % 8 != 0)) return FLCE_ERR_MISALIGNED;
+  if (H % 8 != 0) return FLCE_ERR_MISALIGNED;
   return FLCE_OK;
 }
 
@@ -909,7 +914,11 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
   uint16_t* dvt = reinterpret_cast<uint16_t*>(wsp(workspace, f.dvt));
   float* mref = reinterpret_cast<float*>(wsp(workspace, f.mref));
   float* dxacc = reinterpret_cast<float*>(wsp(workspace, f.dxacc));
-  float* dwacc = f32 ? static_cast<float*>(grad_weight)
+  // dW goes to grad_weight, or with a vocabulary that is not a multiple of 8
+  // to a padded buffer copied out at the end (the weight is then read from a
+  // padded copy).
+  void* gw_out = p.padw ? static_cast<void*>(wsp(workspace, f.gwp)) : grad_weight;
+  float* dwacc = f32 ? static_cast<float*>(gw_out)
                      : reinterpret_cast<float*>(wsp(workspace, f.dwacc));
 
   FwdPrepArgs pr{};
@@ -942,7 +951,13 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
     // weight (H rows, K = vocabulary) for dH.
     FLCE_TRY(pack_rows(K_PACK_HIDDEN, hidden, N, H, H, p.hkb, idx, nvalid, xb, st));
     FLCE_TRY(pack_cols(K_PACK_HIDDEN, hidden, H, N, H, p.nkb, idx, nvalid, xtb, st));
-    FLCE_TRY(pack_rows(K_PACK_WEIGHT, weight, H, V, V, f.kbv, nullptr, nullptr, wb, st));
+    const uint16_t* wrd = static_cast<const uint16_t*>(weight);
+    if (p.padw) {
+      uint16_t* wp = reinterpret_cast<uint16_t*>(wsp(workspace, f.wp));
+      FLCE_TRY(pad_cols(weight, H, V, p.V8, wp, st));
+      wrd = wp;
+    }
+    FLCE_TRY(pack_rows(K_PACK_WEIGHT, wrd, H, p.V8, p.V8, f.kbv, nullptr, nullptr, wb, st));
     const int64_t mld = (int64_t)f.TBc * kTile;
     for (int c = 0; c < f.nchunks; ++c) {
       const int tb0 = c * f.TBc;
@@ -951,8 +966,8 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
       const int64_t rows = (int64_t)tbc * kTile;
 
       FwdTileArgs a{};
-      a.weight = static_cast<const uint16_t*>(weight);
-      a.ldw = V;  // V is a multiple of 8 here
+      a.weight = wrd;
+      a.ldw = p.V8;
       a.xb = xb;
       a.lab = labc;
       a.nvalid = nvalid;
@@ -1078,8 +1093,8 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
       w.group = p.group;
       w.kper = w.kbn;
       w.ldp = 0;
-      w.gw = grad_weight;
-      w.ldo = V;
+      w.gw = gw_out;
+      w.ldo = p.V8;
       w.part = nullptr;
       w.accw = dwacc;
       w.rows = rows;
@@ -1095,6 +1110,7 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
           bwd_dw_kernel<DW_CHUNK, false><<<gw, kThreads, 0, st>>>(w);
       }));
     }
+    if (p.padw) FLCE_TRY(unpad_cols(gw_out, H, p.V8, V, grad_weight, f32, st));
   }
   if (reduce) {
     float* const red[4] = {reduced, reduced + 1, reduced + 2, reduced + 3};
@@ -1170,7 +1186,7 @@ flce_status_t flce_backward_ex(const void* hidden, const void* weight, const int
 
 flce_status_t flce_fused_workspace_size(int64_t N, int64_t H, int64_t V, const flce_options_t* opt,
                                         int64_t chunk_tokens, size_t* bytes) {
-  FLCE_TRY(check_shape(N, H, V, false));
+  FLCE_TRY(check_shape(N, H, V));
   FLCE_TRY(check_options(opt));
   if (V > kMaxVF32 || chunk_tokens < 0) return FLCE_ERR_BAD_SHAPE;
   if (bytes) *bytes = make_fused_plan(N, H, V, *opt, chunk_tokens).total;
@@ -1185,7 +1201,7 @@ flce_status_t flce_forward_backward(const void* hidden, const void* weight, cons
                                     float* entropy, float* uniform_ce, float* z_loss,
                                     float* reduced, void* grad_hidden, void* grad_weight,
                                     void* workspace, size_t workspace_bytes, void* stream) {
-  FLCE_TRY(check_shape(N, H, V, false));
+  FLCE_TRY(check_shape(N, H, V));
   FLCE_TRY(check_options(opt));
   return fused_impl(hidden, weight, labels, N, H, V, *opt, chunk_tokens, grad_logprob,
                     grad_entropy, grad_uniform_ce, grad_z_loss, lse, logprob, entropy, uniform_ce,
@@ -1329,7 +1345,7 @@ const char* flce_status_string(flce_status_t s) {
     case FLCE_ERR_BAD_SHAPE: return "bad shape (need N >= 0, H >= 1, V >= 1 within limits)";
     case FLCE_ERR_BAD_REDUCTION: return "reduction must be NONE (0), MEAN (1) or SUM (2)";
     case FLCE_ERR_MISALIGNED:
-      return "pointers must be 16-byte aligned, H a multiple of 8 (and V for the fused call)";
+      return "pointers must be 16-byte aligned and H a multiple of 8";
     case FLCE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than flce_workspace_size";
     case FLCE_ERR_BAD_SOFTCAP: return "softcap must be finite";
     case FLCE_ERR_HIP: return "HIP runtime error or failed kernel launch";

@@ -3,8 +3,8 @@ read from a padded copy with 16-byte aligned rows and dW is formed in a
 padded buffer, both in the workspace) against the float64 oracle on the same
 seeded bf16 inputs: forward statistics and reductions, both gradients in bf16
 and fp32, the cap, several vocabulary chunks with an odd last one, the
-token-split dW, class weights and odd vocabulary slices. The fused call
-refuses such a vocabulary.
+token-split dW, class weights, odd vocabulary slices and the fused call
+(one chunk and several, bf16 and fp32).
 
 Tolerances as everywhere: statistics within 2e-3 absolute or 1e-3
 relative, gradients within 1e-2 relative L2.
@@ -158,9 +158,25 @@ def test_odd_vocab_slices():
     assert G.rel_l2(torch.cat(gws, dim=1).cpu().numpy(), dw) <= G.GRAD_REL_L2
 
 
-def test_fused_refuses_odd_vocab():
+@pytest.mark.parametrize("chunk,gdt", [(0, "bf16"), (256, "bf16"), (256, "f32")])
+def test_odd_vocab_fused(chunk, gdt):
+    """The fused call with V = 1001: one chunk, and 256-token chunks whose dW
+    accumulates in fp32 across chunks (in a padded buffer)."""
     wl = W.WORKLOADS["odd_vocab"]
-    t = G.upload(W.make_inputs(wl))
-    with pytest.raises(flce.FlceError):
-        flce.forward_backward(t["hidden"], t["weight"], t["labels"], t["grad_logprob"],
-                              t["grad_entropy"])
+    x = W.make_inputs(wl)
+    print(f"[odd V fused] chunk={chunk} {gdt}", flush=True)
+    t = G.upload(x)
+    res = flce.forward_backward(t["hidden"], t["weight"], t["labels"], t["grad_logprob"],
+                                t["grad_entropy"], ignore_index=wl.ignore_index, softcap=4.0,
+                                grad_dtype=gdt, chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    assert res["grad_weight"].shape == (wl.H, wl.V)
+    hf = W.bf16_bits_to_f32(x["hidden"])
+    wf = W.bf16_bits_to_f32(x["weight"])
+    fw = oracle.forward(hf, wf, x["labels"], ignore_index=wl.ignore_index, softcap_c=4.0)
+    dh, dw = oracle.backward(hf, wf, x["labels"], ignore_index=wl.ignore_index, softcap_c=4.0,
+                             grad_logprob=x["grad_logprob"], grad_entropy=x["grad_entropy"])
+    for k in ("lse", "logprob", "entropy"):
+        assert G.stat_err(res[k].cpu().numpy(), fw[k]) <= 1.0, k
+    assert G.rel_l2(res["grad_hidden"].float().cpu().numpy(), dh) <= G.GRAD_REL_L2
+    assert G.rel_l2(res["grad_weight"].float().cpu().numpy(), dw) <= G.GRAD_REL_L2
