@@ -5,7 +5,11 @@
 // tile C[m][n] = sum_k A[m][k] * B[n][k], fp32 accumulators. Wave w computes
 // rows [128*(w&1), +128) x cols [64*(w>>1), +64) with
 // v_mfma_f32_32x32x16_bf16 (4 x 2 blocks of 32 x 32, 128 accumulators per
-// lane), so two waves share each SIMD and hide each other's stalls.
+// lane). Two K-loop schedules share the stages and loaders below: a ping-pong
+// one (the two waves of a SIMD alternate between MFMAs and memory work, so
+// the matrix unit is fed while the other wave waits) for contractions whose
+// operands are both blocked, and an interleaved one for the logit tiles, whose
+// transposing LDS reads are too slow to fit in a ping-pong half period.
 //
 // Operand layout ("blocked"). Every GEMM operand is first arranged in HBM as
 // strips of 256 rows; a strip is a sequence of K blocks of 32 values, and a
@@ -29,10 +33,9 @@
 // ds_read_b64_tr_b16. This spares a transposed copy of the weight; the slower
 // LDS reads only touch one of the two operands.
 //
-// Four LDS stages (16 KiB per operand each, 128 KiB in all) keep three K
-// blocks in flight while one is consumed; every stage is a separate
-// __shared__ array so the compiler can tell a stage being read from the ones
-// being filled.
+// Four LDS stages (16 KiB per operand each, 128 KiB in all) keep two to three
+// K blocks in flight while one is consumed; every stage is a separate
+// __shared__ array.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -150,30 +153,53 @@ __device__ __forceinline__ void block_barrier() {
 
 // ---- global -> LDS DMA of one block -------------------------------------------------
 
+// Wave-uniform index of the calling wave (an SGPR value, so LDS addresses
+// derived from it need no VGPR).
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// One 1 KiB global -> LDS DMA instruction (buffer_load_dwordx4 ... lds): lane
+// l moves the 16 bytes at voff + soff (+16 l is in voff) of resource rs to
+// LDS byte lds + 16 l. It is issued from inline assembly so that the
+// compiler, which cannot tell the LDS stages apart through M0, does not make
+// fragment reads of one stage wait for the DMA of another: every wait on these
+// loads is an explicit s_waitcnt vmcnt in the main loop below. The
+// instruction writes no register, so nothing the compiler allocates is left
+// pending.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, const char* lds, uint32_t voff,
+                                          uint32_t soff) {
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "{m0}"((uint32_t)(uintptr_t)(const lds_void_t*)lds), "v"(voff), "s"(rs), "s"(soff)
+      : "memory");
+}
+
 // Wave w copies pieces [w * kDmaBlocks, +kDmaBlocks) of 1 KiB; lane l moves
-// bytes [16 l, +16) of each piece. Block indices at or past the strip's end
-// are sent to an out-of-range offset (no memory access; zeros land in LDS), so
-// every step issues the same number of loads.
+// bytes [16 l, +16) of each piece. The resource is rebased to the block and
+// has size 0 for block indices at or past the strip's end (no memory access;
+// zeros land in LDS), so every step issues the same number of loads; the
+// piece index rides in the scalar offset, so one VGPR serves every piece.
 struct Dma {
-  __amdgpu_buffer_rsrc_t rs;
+  const uint16_t* ptr;
   uint32_t off;
+  int wofs;
   int nkb;
   __device__ __forceinline__ void init(const Strip& s) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    rs = make_rsrc(s.ptr, (int64_t)s.nkb * kBlockBytes);
-    off = (uint32_t)(w * kDmaBlocks * 1024 + lane * 16);
+    const int lane = threadIdx.x & 63;
+    ptr = s.ptr;
+    wofs = wave_id() * kDmaBlocks * 1024;
+    off = (uint32_t)(wofs + lane * 16);
     nkb = s.nkb;
   }
   __device__ __forceinline__ void issue(char* dst, int kb) const {
-    const int w = threadIdx.x >> 6;
     const bool ok = kb < nkb;
-    const uint32_t base = off + (uint32_t)kb * (uint32_t)kBlockBytes;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(ptr + (int64_t)(ok ? kb : 0) * kBlockElems, ok ? kBlockBytes : 0);
 #pragma unroll
-    for (int q = 0; q < kDmaBlocks; ++q) {
-      const uint32_t v = ok ? base + q * 1024 : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void_t*)(dst + (w * kDmaBlocks + q) * 1024), 16, v, 0, 0, 0);
-    }
+    for (int q = 0; q < kDmaBlocks; ++q) lds_dma16(rs, dst + wofs + q * 1024, off, q * 1024);
   }
 };
 
@@ -210,7 +236,7 @@ struct RowA {
   uint32_t off[kDmaBlocks];
   __device__ __forceinline__ void init(const uint16_t* p, int64_t ld_, int64_t rows, int64_t r0,
                                        int64_t kb, int64_t ke) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = wave_id();
     ptr = p;
     ld = ld_;
     kbeg = kb;
@@ -224,17 +250,12 @@ struct RowA {
     }
   }
   __device__ __forceinline__ void issue(char* dst, int kt, int nk) const {
-    const int w = threadIdx.x >> 6;
+    const int w = wave_id();
     const int64_t k0 = kbeg + (int64_t)kt * kBK;
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(ptr + k0 * ld, kt < nk ? (kend - k0) * ld * 2 : 0);
 #pragma unroll
-    for (int q = 0; q < kDmaBlocks; ++q) {
-      uint32_t v = off[q];
-      opaque(v);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void_t*)(dst + (w * kDmaBlocks + q) * 1024), 16, v, 0, 0, 0);
-    }
+    for (int q = 0; q < kDmaBlocks; ++q) lds_dma16(rs, dst + (w * kDmaBlocks + q) * 1024, off[q], 0);
   }
 };
 
@@ -317,6 +338,7 @@ typedef f32x16_t Acc[4][2];
 
 // ---- the pipelined K loop ------------------------------------------------------
 
+
 // Instruction-class masks of __builtin_amdgcn_sched_group_barrier.
 enum : int { SG_MFMA = 0x8, SG_VMEM_RD = 0x20, SG_DS_RD = 0x100 };
 
@@ -339,10 +361,15 @@ __device__ __forceinline__ void interleave_reads() {
   sg_mfma_then_reads<NR, 7>();
 }
 
-// ASrc: BlockedA or RowA (already initialised by the caller); AFrag: the
-// matching fragment reader, FragSrc<4> or FragRow<4>.
+// Interleaved schedule: both waves of a SIMD run the same phase of every K
+// block, with the fragment reads of the next 16-wide substep spread over the
+// MFMAs of the current one and one block barrier per K block. Used where the
+// A operand is row-contiguous: its transposing LDS reads take longer than the
+// MFMAs of a half period, so the ping-pong schedule below would leave the
+// matrix units waiting on them. ASrc: BlockedA or RowA (already initialised by
+// the caller); AFrag: the matching fragment reader, FragSrc<4> or FragRow<4>.
 template <class ASrc, class AFrag>
-struct MainloopT {
+struct MainloopIL {
   struct Frags {
     bf16x8_t a[4], b[2];
   };
@@ -436,8 +463,154 @@ struct MainloopT {
   }
 };
 
-typedef MainloopT<BlockedA, FragSrc<4>> Mainloop;     // both operands blocked
-typedef MainloopT<RowA, FragRow<4>> MainloopRowA;     // A row-contiguous, B blocked
+
+// Ping-pong schedule. The hardware puts wave w of a block on SIMD w % 4, so
+// waves 0-3 (the leader group) and 4-7 (the follower group) share each SIMD
+// one to one. The two groups run half a K block apart: in every half period
+// one group issues the 16 MFMAs of a whole 32-deep K block back to back from
+// registers, at raised priority, while the other reads the next block's
+// fragments from LDS and issues its part of the global -> LDS DMA; a block
+// barrier ends each half period. The matrix unit of each SIMD is thus fed by
+// one wave while the other waits on LDS, DMA and the barrier, instead of both
+// waves draining it at a common barrier.
+//   half period 2k:    leader M(k)          follower DMA(k+3), R(k)
+//   half period 2k+1:  leader DMA(k+3), R(k+1)   follower M(k)
+// M = MFMAs, R = fragment reads; block b lives in stage b % 4. The DMA of
+// block k+3 overwrites the stage of block k-1, which both groups finished
+// reading (waited on before their barriers) by the end of half period 2k-1.
+// Before the barrier that ends half period 2k every wave has its own pieces of
+// block k+1 in LDS: the leader has issued blocks up to k+2 (one may stay in
+// flight), the follower up to k+3 (two may).
+template <class ASrc, class AFrag>
+struct MainloopPP {
+  struct Frags {
+    bf16x8_t a[2][4], b[2][2];  // both 16-wide substeps of one K block
+  };
+  AFrag fa;
+  FragSrc<2> fb;
+  ASrc da;
+  Dma db;
+  int b_kb0;
+
+  // DMA instructions per block and wave.
+  static constexpr int kDma = 2 * kDmaBlocks;
+
+  template <int S>
+  __device__ __forceinline__ void issue(char* const (&sa)[kStages], char* const (&sb)[kStages], int kt,
+                                        int nk) const {
+    da.issue(sa[S], kt, nk);
+    db.issue(sb[S], kt < nk ? b_kb0 + kt : db.nkb);
+  }
+  template <int S>
+  __device__ __forceinline__ void read(char* const (&sa)[kStages], char* const (&sb)[kStages],
+                                       Frags& f) const {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      fa.read(sa[S], kk, f.a[kk]);
+      fb.read(sb[S], kk, f.b[kk]);
+    }
+  }
+  __device__ __forceinline__ static void math(const Frags& f, Acc& acc) {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
+  }
+  // Keeps the scheduler from moving instructions across a phase boundary.
+  __device__ __forceinline__ static void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+  // Leader, block k in stage S.
+  template <int S>
+  __device__ __forceinline__ void lead(char* const (&sa)[kStages], char* const (&sb)[kStages], Frags& f,
+                                       Acc& acc, int k, int nk) const {
+    math(f, acc);
+    fence();
+    wait_vmcnt<kDma * (kStages - 3)>();
+    block_barrier();
+    fence();
+    issue<(S + kStages - 1) % kStages>(sa, sb, k + kStages - 1, nk);
+    if (k + 1 < nk) read<(S + 1) % kStages>(sa, sb, f);
+    wait_lgkmcnt0();
+    block_barrier();
+    fence();
+  }
+  // Follower, block k in stage S.
+  template <int S>
+  __device__ __forceinline__ void follow(char* const (&sa)[kStages], char* const (&sb)[kStages],
+                                         Frags& f, Acc& acc, int k, int nk) const {
+    issue<(S + kStages - 1) % kStages>(sa, sb, k + kStages - 1, nk);
+    read<S>(sa, sb, f);
+    wait_lgkmcnt0();
+    wait_vmcnt<kDma * (kStages - 2)>();
+    block_barrier();
+    fence();
+    math(f, acc);
+    fence();
+    block_barrier();
+    fence();
+  }
+
+  // C tile = A x strip B over nk K blocks (B's from bkb0). Leaves every DMA
+  // drained and the block synchronised, so callers may reuse the stage arrays
+  // afterwards. Every wave passes the same number of barriers.
+  __device__ __forceinline__ void run(char* const (&sa)[kStages], char* const (&sb)[kStages],
+                                      const ASrc& A, const Strip& B, int bkb0, int nk, Acc& acc) {
+    static_assert(kStages == 4, "the schedule above assumes four stages");
+    const int wave = wave_id();
+    const int wm = wave & 1, wn = wave >> 1;
+    const bool leader = wave < 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    if (nk <= 0) return;
+    da = A;
+    db.init(B);
+    b_kb0 = bkb0;
+    fa.init(wm * 128);
+    fb.init(wn * 64);
+    issue<0>(sa, sb, 0, nk);
+    issue<1>(sa, sb, 1, nk);
+    issue<2>(sa, sb, 2, nk);
+    wait_vmcnt<kDma * (kStages - 2)>();
+    block_barrier();
+    Frags f;
+    if (leader) {
+      read<0>(sa, sb, f);
+      wait_lgkmcnt0();
+    }
+    block_barrier();
+    fence();
+    if (leader) {
+      for (int kt = 0; kt < nk; kt += kStages) {
+        lead<0>(sa, sb, f, acc, kt, nk);
+        if (kt + 1 < nk) lead<1>(sa, sb, f, acc, kt + 1, nk);
+        if (kt + 2 < nk) lead<2>(sa, sb, f, acc, kt + 2, nk);
+        if (kt + 3 < nk) lead<3>(sa, sb, f, acc, kt + 3, nk);
+      }
+    } else {
+      for (int kt = 0; kt < nk; kt += kStages) {
+        follow<0>(sa, sb, f, acc, kt, nk);
+        if (kt + 1 < nk) follow<1>(sa, sb, f, acc, kt + 1, nk);
+        if (kt + 2 < nk) follow<2>(sa, sb, f, acc, kt + 2, nk);
+        if (kt + 3 < nk) follow<3>(sa, sb, f, acc, kt + 3, nk);
+      }
+    }
+    wait_vmcnt<0>();
+    block_barrier();
+  }
+};
+
+typedef MainloopPP<BlockedA, FragSrc<4>> Mainloop;     // both operands blocked
+typedef MainloopIL<RowA, FragRow<4>> MainloopRowA;     // A row-contiguous, B blocked
 
 // Blocked A operand descriptor for Mainloop::run.
 __device__ __forceinline__ BlockedA blocked_a(const Strip& s, int kb0) {
