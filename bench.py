@@ -9,8 +9,10 @@ labels, reduction none, per-token upstream gradients).
 
 --path fused times flce_forward_backward instead (the gradient formed from
 logits kept during the forward, for upstream gradients known in advance; no
-recompute GEMM). With the default path the fused one is also timed on the
-same inputs and reported under alt_paths.fused (--alt-fused 0 skips it).
+recompute GEMM) with its default token chunks (kept-logit images within
+1 GiB). With the default path the fused one is also timed on the same inputs
+and reported under alt_paths.fused, and with every logit of the batch kept in
+one chunk under alt_paths.fused_one_chunk (--alt-fused 0 skips both).
 
 Prints one JSON line. Besides the throughput it reports:
   roofline      the dominant kernel's algorithmic TFLOP/s (flops per launch /
@@ -32,13 +34,15 @@ Prints one JSON line. Besides the throughput it reports:
   torch_ref     (optional) a materialising torch implementation of the same
                 forward + backward on the same GPU, for context.
 
-roofline.traffic is the dominant kernel's HBM bytes per launch as measured
-by rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads
-for a plain device copy of known size in the same run), taken from
-profiles/traffic_<workload>.txt; it is null when that file is missing or was
-taken on kernel sources other than the ones built now (a SHA-256 over the
-library's sources is stored with the counters). --copy-calibration-mib runs
-that plain copy once before warmup, for the counter runs.
+roofline.traffic is the dominant kernel's fabric bytes per launch: what its
+L2 caches fetched from and wrote to the memory fabric (MALL hits and HBM
+alike; the counters do not separate them), from the rocprofv3 counters
+FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain device
+copy of known size in the same run, taken from profiles/traffic_<workload>.txt;
+it is null when that file is missing or was taken on kernel sources other
+than the ones built now (a SHA-256 over the library's sources is stored with
+the counters). --copy-calibration-mib runs that plain copy once before warmup,
+for the counter runs.
 """
 from __future__ import annotations
 
@@ -111,8 +115,13 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+TRAFFIC_WHAT = ("fabric bytes per launch (L2 fetches + writes to MALL or HBM, rocprofv3 "
+                "FETCH_SIZE + WRITE_SIZE scaled by a device-copy calibration)")
+
+
 def counted_traffic(workload: str, path: str = "recompute"):
-    """Per-kernel HBM bytes per launch from profiles/traffic_<workload>.txt
+    """Per-kernel fabric bytes (L2 misses to MALL or HBM, and L2 write-backs)
+    per launch from profiles/traffic_<workload>.txt
     (traffic_<workload>_fused.txt for the fused path), or None when absent or
     taken on other sources. Lines of that file:
       source_sha256 <hex>
@@ -298,20 +307,26 @@ def main():
     entm = torch.empty(1, **f32)
     gh = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
     gw = torch.empty((H, V), dtype=torch.bfloat16, device=dev)
-    wsf = torch.empty(fbytes, dtype=torch.uint8, device=dev)
-    wsb = torch.empty(bbytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
     P = {k: v.data_ptr() for k, v in t.items()}
+    # The recompute path's workspaces, allocated on first use and released
+    # before the fused path is measured (each path's peak counts its own).
+    rws = {}
+
+    def rws_ptr(key, nbytes):
+        if key not in rws:
+            rws[key] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        return rws[key].data_ptr()
 
     def fwd_only():
         flce.flce_forward(P["hidden"], P["weight"], P["labels"], N, H, V, wl.ignore_index,
                           wl.softcap, red, lse.data_ptr(), lp.data_ptr(), ent.data_ptr(),
-                          lpm.data_ptr(), entm.data_ptr(), wsf.data_ptr(), fbytes, stream)
+                          lpm.data_ptr(), entm.data_ptr(), rws_ptr("f", fbytes), fbytes, stream)
 
     def bwd_only():
         flce.flce_backward(P["hidden"], P["weight"], P["labels"], N, H, V, wl.ignore_index,
                            wl.softcap, red, lse.data_ptr(), ent.data_ptr(), P["grad_logprob"],
-                           P["grad_entropy"], gh.data_ptr(), gw.data_ptr(), wsb.data_ptr(),
+                           P["grad_entropy"], gh.data_ptr(), gw.data_ptr(), rws_ptr("b", bbytes),
                            bbytes, stream)
 
     def step_recompute():
@@ -322,16 +337,25 @@ def main():
     reduced = torch.empty(4, **f32)
     fused_ws = {}
 
-    def step_fused():
-        if "buf" not in fused_ws:
-            fused_ws["bytes"] = flce.flce_fused_workspace_size(N, H, V, opt, 0)
-            fused_ws["buf"] = torch.empty(fused_ws["bytes"], dtype=torch.uint8, device=dev)
-        flce.flce_forward_backward(P["hidden"], P["weight"], P["labels"], N, H, V, opt, 0,
-                                   P["grad_logprob"], P["grad_entropy"], None, None,
-                                   lse.data_ptr(), lp.data_ptr(), ent.data_ptr(), None, None,
-                                   reduced.data_ptr(), gh.data_ptr(), gw.data_ptr(),
-                                   fused_ws["buf"].data_ptr(), fused_ws["bytes"], stream)
+    def make_step_fused(chunk_tokens):
+        """flce_forward_backward with `chunk_tokens` (0: the library's
+        default); its workspace is allocated on the first call and freed
+        before another chunking allocates its own."""
+        def step_fused():
+            if fused_ws.get("chunk") != chunk_tokens:
+                fused_ws.clear()
+                torch.cuda.empty_cache()
+                fused_ws["chunk"] = chunk_tokens
+                fused_ws["bytes"] = flce.flce_fused_workspace_size(N, H, V, opt, chunk_tokens)
+                fused_ws["buf"] = torch.empty(fused_ws["bytes"], dtype=torch.uint8, device=dev)
+            flce.flce_forward_backward(P["hidden"], P["weight"], P["labels"], N, H, V, opt,
+                                       chunk_tokens, P["grad_logprob"], P["grad_entropy"], None,
+                                       None, lse.data_ptr(), lp.data_ptr(), ent.data_ptr(), None,
+                                       None, reduced.data_ptr(), gh.data_ptr(), gw.data_ptr(),
+                                       fused_ws["buf"].data_ptr(), fused_ws["bytes"], stream)
+        return step_fused
 
+    step_fused = make_step_fused(0)
     step = step_fused if args.path == "fused" else step_recompute
 
     if args.copy_calibration_mib > 0:
@@ -378,7 +402,7 @@ def main():
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": dk.get("tflops"),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": dk.get("mfma_frac"),
-                     "traffic": (traffic or {}).get(dom)},
+                     "traffic": (traffic or {}).get(dom), "traffic_what": TRAFFIC_WHAT},
         "step_tflops": step_tflops,
         "step_mfma_frac": step_tflops / PEAK_BF16_TFLOPS,
         "kernels": kernels,
@@ -419,23 +443,38 @@ def main():
     except Exception as exc:
         out["mfma_sustained"] = {"error": str(exc)[:200]}
     if args.path == "recompute" and args.alt_fused:
-        try:
-            print("[bench] fused path (gradient in the forward)", flush=True)
-            fpeak = peak_of(step_fused)
-            fms, ftable = timed(step_fused, args.steps, args.warmup)
-            fk = kernel_rows(ftable, args.steps, n_valid, H, V)
-            fdom = max((k for k in fk if "tflops" in fk[k]), key=lambda k: fk[k]["ms_per_step"])
-            out["alt_paths"] = {"fused": {
-                "value": N / (fms * 1e-3), "unit": "tokens/s", "ms_per_step": fms,
-                "executed_tflops": 6.0 * n_valid * H * V / (fms * 1e-3) / 1e12,
-                "peak_bytes": fpeak, "workspace_bytes": fused_ws["bytes"],
-                "roofline": {"kernel": fdom, "bound": "mfma", "achieved": fk[fdom]["tflops"],
-                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                             "frac": fk[fdom]["mfma_frac"],
-                             "traffic": (counted_traffic(wl.name, "fused") or {}).get(fdom)},
-                "kernels": fk}}
-        except Exception as exc:
-            out["alt_paths"] = {"fused": {"error": str(exc)[:200]}}
+        rws.clear()
+        torch.cuda.empty_cache()
+        out["alt_paths"] = {}
+        vt = -(-V // 256) * 256
+        for key, chunk in (("fused", 0), ("fused_one_chunk", N)):
+            try:
+                print(f"[bench] fused path (gradient in the forward), {key}", flush=True)
+                sf = make_step_fused(chunk)
+                fpeak = peak_of(sf)
+                fms, ftable = timed(sf, args.steps, args.warmup)
+                fk = kernel_rows(ftable, args.steps, n_valid, H, V)
+                fdom = max((k for k in fk if "tflops" in fk[k]),
+                           key=lambda k: fk[k]["ms_per_step"])
+                ntok = fk["fused_tile"]["launches_per_step"] if "fused_tile" in fk else None
+                out["alt_paths"][key] = {
+                    "value": N / (fms * 1e-3), "unit": "tokens/s", "ms_per_step": fms,
+                    "executed_tflops": 6.0 * n_valid * H * V / (fms * 1e-3) / 1e12,
+                    "chunk_tokens": chunk if chunk else "default",
+                    "token_chunks_run": ntok,
+                    "peak_bytes": fpeak, "workspace_bytes": fused_ws["bytes"],
+                    "kept_logit_image_bytes": 4 * vt * 256 * (
+                        -(-chunk // 256) if chunk
+                        else min(-(-N // 256), max(1, (1 << 30) // (4 * 256 * vt)))),
+                    "roofline": {"kernel": fdom, "bound": "mfma",
+                                 "achieved": fk[fdom]["tflops"], "peak": PEAK_BF16_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": fk[fdom]["mfma_frac"],
+                                 "traffic": ((counted_traffic(wl.name, "fused") or {}).get(fdom)
+                                             if key == "fused" else None)},
+                    "kernels": fk}
+            except Exception as exc:
+                out["alt_paths"][key] = {"error": str(exc)[:200]}
+        fused_ws.clear()
     if args.torch_ref:
         try:
             print("[bench] torch materialising reference", flush=True)

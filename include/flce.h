@@ -95,7 +95,8 @@ typedef enum {
   FLCE_ERR_BAD_SOFTCAP = 6,       /* softcap is NaN or infinite */
   FLCE_ERR_HIP = 7,               /* a HIP runtime call or kernel launch failed */
   FLCE_ERR_INVALID_LABEL = 8,     /* reported only by flce_get_status */
-  FLCE_ERR_BAD_OPTION = 9         /* z_loss_scale negative or not finite, unknown grad_dtype */
+  FLCE_ERR_BAD_OPTION = 9         /* z_loss_scale negative or not finite, unknown grad_dtype,
+                                   * class_weight under NONE, entropy_per_token not 0 or 1 */
 } flce_status_t;
 
 enum { FLCE_REDUCTION_NONE = 0, FLCE_REDUCTION_MEAN = 1, FLCE_REDUCTION_SUM = 2 };
@@ -119,7 +120,12 @@ enum { FLCE_GRAD_BF16 = 0, FLCE_GRAD_F32 = 1 };
 flce_status_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int reduction,
                                   size_t* fwd_bytes, size_t* bwd_bytes);
 
-/* Forward.
+/* Forward. The call shape of the API example of verl pull request #462
+ * (section "API": hidden [num_tokens, hidden_size], weight [hidden_size,
+ * vocab_size], integer labels, a reduction argument, two outputs), with the
+ * outputs of its section "Equivalent compute logic" (per-token entropy and the
+ * label log-probability, the negated cross-entropy) and the cap of
+ * Liger-Kernel issue #127 (proposal: applied after the head matmul).
  *   hidden   device bf16 [N,H]        weight  device bf16 [H,V]
  *   labels   device int64 [N]         ignore_index: label value that marks a skipped token
  *   softcap  c > 0 caps logits as c*tanh(z/c); c <= 0 disables the cap
@@ -141,6 +147,11 @@ flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t
 /* Backward: writes grad_hidden = dL/dhidden (device bf16 [N,H]) and
  * grad_weight = dL/dweight (device bf16 [H,V]) for
  *   L = sum_i gbar_i logprob_i + ebar_i entropy_i.
+ * Liger-Kernel pull request #435 ("Why we pass gradient to output.backward()")
+ * fixes the convention: an unreduced output takes one upstream gradient per
+ * element, a reduced one a scalar; the review thread of Liger-Kernel pull
+ * request #551 fixes the mean's divisor (the non-ignored tokens) and issue #127
+ * (discussion) the cap's chain rule into both gradients.
  * hidden, weight, labels, N, H, V, ignore_index, softcap and reduction must be
  * those of the matching flce_forward; lse and entropy are its outputs.
  *   reduction NONE: grad_logprob, grad_entropy are device fp32 [N]
@@ -162,8 +173,9 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Options of the extended entry points. class_weight was added in version
- * 211 (flce_version); the struct grew from 24 to 32 bytes, so callers built
- * against an older header must be rebuilt. */
+ * 211 (flce_version), entropy_per_token in version 212; the struct grew from
+ * 24 to 32 and then to 40 bytes, so callers built against an older header must
+ * be rebuilt. A zero-initialised tail keeps the earlier behaviour. */
 typedef struct flce_options {
   int64_t ignore_index;  /* label value that marks a skipped token */
   float softcap;         /* c > 0: z' = c*tanh(z/c); c <= 0: no cap; must be finite */
@@ -173,6 +185,15 @@ typedef struct flce_options {
   const float* class_weight; /* NULL, or device fp32 [V] (the whole vocabulary; 4-byte
                               * aligned, finite values): target weights of the MEAN and
                               * SUM reductions, see below; FLCE_ERR_BAD_OPTION under NONE */
+  int entropy_per_token; /* 0: the entropy follows `reduction` like the other outputs;
+                          * 1: under MEAN or SUM the entropy is taken per token while the
+                          * other outputs are reduced, so the backward's grad_entropy is
+                          * device fp32 [N] (ebar_i = grad_entropy[i], no class weight) and
+                          * the other upstream gradients stay [1]; the verl pull request
+                          * #462 "Equivalent compute logic" returns entropy per token beside
+                          * a reduced logprob. Any other value: FLCE_ERR_BAD_OPTION. The
+                          * forward writes the per-token entropy under every reduction
+                          * (reduced[1] is still the entropy's reduction). */
 } flce_options_t;
 
 /* Target (class) weights. The Liger-Kernel PR #551 review ("[Verl] Add
@@ -303,10 +324,12 @@ flce_status_t flce_backward_shard(const void* hidden, const void* weight_shard,
  * The results agree with flce_forward_ex followed by flce_backward_ex to the
  * rounding of the kept logits (bf16 of z' - m), not bit for bit.
  *
- * chunk_tokens: tokens per chunk Nc (rounded up to 256); 0 picks 8192, or all
- * tokens when N <= 8192 + H (then chunking would not save memory; the chunk
- * images then hold every logit of the call, 4 bytes each: pass a smaller
- * chunk_tokens to bound them). V <= 2^21.
+ * chunk_tokens: tokens per chunk Nc (rounded up to 256); 0 picks the largest
+ * multiple of 256 whose chunk images fit in 1 GiB (the budget of the
+ * backward's logit-gradient images; at least 256 tokens), e.g. 2048 tokens at
+ * V = 128256. A larger chunk saves passes over the fp32 dW accumulator at the
+ * price of memory; chunk_tokens >= N keeps every logit of the call (4 bytes
+ * each) in one chunk. V <= 2^21.
  * Workspace bytes for this shape, options and chunk_tokens (host only): */
 flce_status_t flce_fused_workspace_size(int64_t N, int64_t H, int64_t V, const flce_options_t* opt,
                                         int64_t chunk_tokens, size_t* bytes);

@@ -196,9 +196,10 @@ size_t merge_bytes(int64_t N) {
 // the logit gradient is formed from them in both blocked layouts, so the
 // chunk images take 4 * 256 TBc * 256 VT bytes; with several chunks dW is
 // accumulated over them in fp32 (H * V * 4 bytes, or in grad_weight itself
-// when it is fp32). By default a chunk holds 8192 tokens, or all of them when
-// that costs no more memory than chunking (N <= 8192 + H, counted in blocks).
-constexpr int kFusedChunkBlocks = 32;
+// when it is fp32). By default a chunk is the largest number of token blocks
+// whose images fit in kFusedImageBudget (the recompute path's budget for its
+// logit-gradient images), at least one block.
+constexpr size_t kFusedImageBudget = (size_t)1 << 30;
 
 struct FusedPlan {
   Plan b;              // TB, VT, HT, hkb, nkb, group of the shape
@@ -218,10 +219,13 @@ FusedPlan make_fused_plan(int64_t N, int64_t H, int64_t V, const flce_options_t&
   const Plan& p = f.b;
   const int TB = p.TB;
   int tbc;
-  if (chunk_tokens > 0)
+  if (chunk_tokens > 0) {
     tbc = (int)ceil_div(chunk_tokens, kTile);
-  else
-    tbc = TB <= kFusedChunkBlocks + p.HT ? TB : kFusedChunkBlocks;
+  } else {
+    const size_t per_block = 4 * (size_t)kTile * (size_t)kTile * (size_t)(p.VT > 0 ? p.VT : 1);
+    const size_t fit = kFusedImageBudget / per_block;
+    tbc = fit > (size_t)TB ? TB : (int)fit;
+  }
   if (tbc > TB) tbc = TB;
   if (tbc < 1) tbc = 1;
   f.TBc = tbc;
@@ -539,6 +543,7 @@ flce_status_t check_options(const flce_options_t* o) {
   // Class weights only enter the mean and sum reductions.
   if (o->class_weight != nullptr && o->reduction == FLCE_REDUCTION_NONE) return FLCE_ERR_BAD_OPTION;
   if (((uintptr_t)o->class_weight & 3u) != 0) return FLCE_ERR_MISALIGNED;
+  if (o->entropy_per_token != 0 && o->entropy_per_token != 1) return FLCE_ERR_BAD_OPTION;
   return FLCE_OK;
 }
 
@@ -726,6 +731,7 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
   pa.idx = idx;
   pa.header = header;
   pa.cw = reduction != FLCE_REDUCTION_NONE ? o.class_weight : nullptr;
+  pa.ent_tok = o.entropy_per_token;
   FLCE_TRY(launch(K_BWD_PREP, st, [&] { bwd_prep_kernel<<<1, 1024, 0, st>>>(pa); }));
   // Rows of ignored tokens are never written by the compacted contractions.
   FLCE_TRY(launch_zero_ignored(labels, N, V_total, o.ignore_index, grad_hidden,
@@ -1017,6 +1023,7 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
       cb.guce = grad_uniform_ce;
       cb.gzl = grad_z_loss;
       cb.reduction = reduction;
+      cb.ent_tok = o.entropy_per_token;
       cb.header = header;
       cb.labels = labels;
       cb.cw = cw;
@@ -1350,12 +1357,14 @@ const char* flce_status_string(flce_status_t s) {
     case FLCE_ERR_BAD_SOFTCAP: return "softcap must be finite";
     case FLCE_ERR_HIP: return "HIP runtime error or failed kernel launch";
     case FLCE_ERR_INVALID_LABEL: return "labels outside [0, V) that are not ignore_index";
-    case FLCE_ERR_BAD_OPTION: return "z_loss_scale must be finite and >= 0; grad_dtype BF16 or F32";
+    case FLCE_ERR_BAD_OPTION:
+      return "z_loss_scale must be finite and >= 0; grad_dtype BF16 or F32; class_weight needs "
+             "MEAN or SUM; entropy_per_token 0 or 1";
   }
   return "unknown status";
 }
 
-int flce_version(void) { return 211; }
+int flce_version(void) { return 212; }
 
 flce_status_t flce_probe_mfma_rate(int mode, int64_t steps, double* tflops, void* workspace,
                                    size_t workspace_bytes, void* stream) {

@@ -563,6 +563,7 @@ struct CombineArgs {
   DzToken* coef;
   const float *glp, *gent, *guce, *gzl;
   int reduction;
+  int ent_tok;             // 1: gent is per token [N] under mean / sum too
   const int32_t* header;
   // Optional class weights [V]: token t's block sums and (fused path) its
   // scalar gradients carry cw[labels[t]]; the mean divides by the weight sum
@@ -581,10 +582,11 @@ __device__ __forceinline__ DzToken token_coef(const CombineArgs& a, int64_t t, f
   const bool scalar = a.reduction != 0;
   const float div = a.reduction == 1 ? mean_divisor_inv(a.header, a.cw != nullptr) : 1.f;
   const float om = scalar ? token_weight(a.cw, a.labels, t) * div : 1.f;
-  auto grad = [&](const float* g) {
-    return g == nullptr ? 0.f : (scalar ? g[0] * om : g[t]);
+  auto grad = [&](const float* g, bool sc) {
+    return g == nullptr ? 0.f : (sc ? g[0] * om : g[t]);
   };
-  const float g = grad(a.glp), ge = grad(a.gent), gu = grad(a.guce), gz = grad(a.gzl);
+  const float g = grad(a.glp, scalar), ge = grad(a.gent, scalar && a.ent_tok == 0),
+              gu = grad(a.guce, scalar), gz = grad(a.gzl, scalar);
   const float S = l - e;
   DzToken c;
   c.lse = l;
@@ -724,6 +726,7 @@ struct PrepArgs {
   int32_t* lab32;
   int32_t* header;
   const float* cw;             // optional class weights [V] (mean, sum)
+  int ent_tok;                 // 1: gent is per token [N] under mean / sum too
 };
 
 // One block of 1024: compacts the valid tokens (in token order) and writes
@@ -751,10 +754,12 @@ __global__ void __launch_bounds__(1024) bwd_prep_kernel(PrepArgs a) {
   // weights: token t takes the share cw[y_t] / sum of the weights); those of
   // a sum apply as they are (times cw[y_t]).
   const bool scalar = a.reduction != 0;
+  const bool escalar = scalar && a.ent_tok == 0;  // the entropy gradient is a scalar too
   const double dv = a.cw != nullptr ? ws : (double)nv;
   const float div = a.reduction == 1 ? (dv != 0.0 ? (float)(1.0 / dv) : 0.f) : 1.f;
   auto scal = [&](const float* g) { return (scalar && g != nullptr) ? g[0] * div : 0.f; };
-  const float g0 = scal(a.glp), e0 = scal(a.gent), u0 = scal(a.guce), z0 = scal(a.gzl);
+  const float g0 = scal(a.glp), u0 = scal(a.guce), z0 = scal(a.gzl);
+  const float e0 = (escalar && a.gent != nullptr) ? a.gent[0] * div : 0.f;
   const float invV = 1.f / (float)a.V;
   int base = 0;
   for (int64_t c0 = 0; c0 < a.N; c0 += 1024) {
@@ -767,10 +772,11 @@ __global__ void __launch_bounds__(1024) bwd_prep_kernel(PrepArgs a) {
     const int r = base + chunk_rank(valid, sh, total);
     if (valid) {
       const float om = (scalar && a.cw != nullptr) ? a.cw[a.labels[t]] : 1.f;
-      auto per = [&](const float* g, float s0) {
-        return scalar ? s0 * om : (g != nullptr ? g[t] : 0.f);
+      auto per = [&](const float* g, float s0, bool sc) {
+        return sc ? s0 * om : (g != nullptr ? g[t] : 0.f);
       };
-      const float g = per(a.glp, g0), e = per(a.gent, e0), u = per(a.guce, u0), z = per(a.gzl, z0);
+      const float g = per(a.glp, g0, scalar), e = per(a.gent, e0, escalar),
+                  u = per(a.guce, u0, scalar), z = per(a.gzl, z0, scalar);
       const float l = a.lse[t];
       const float S = l - a.entropy[t];
       DzToken c;

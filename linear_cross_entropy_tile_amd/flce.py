@@ -29,7 +29,7 @@ __all__ = [
     "flce_backward_ex", "flce_fused_workspace_size", "flce_forward_backward", "flce_get_status",
     "flce_status_string", "flce_version", "flce_profile_enable", "flce_profile_reset",
     "flce_profile_kinds", "flce_profile_read", "profile_table", "flce_probe_mfma_rate",
-    "forward", "backward", "forward_backward", "workspace_bytes",
+    "forward", "backward", "forward_backward", "workspace_bytes", "check_shapes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflce.so")
@@ -55,7 +55,8 @@ class FlceOptions(ctypes.Structure):
     """flce_options_t."""
     _fields_ = [("ignore_index", ctypes.c_int64), ("softcap", ctypes.c_float),
                 ("reduction", ctypes.c_int), ("z_loss_scale", ctypes.c_float),
-                ("grad_dtype", ctypes.c_int), ("class_weight", ctypes.c_void_p)]
+                ("grad_dtype", ctypes.c_int), ("class_weight", ctypes.c_void_p),
+                ("entropy_per_token", ctypes.c_int)]
 
 # Every exported symbol with its (restype, argtypes).
 _P = ctypes.c_void_p
@@ -310,6 +311,26 @@ def _require(t, dtype, ndim, name):
         raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
 
 
+def check_shapes(hidden, weight, labels, *per_token) -> None:
+    """Raises ValueError unless hidden [N,H], weight [H,V], labels [N] and
+    each (name, tensor) pair of ``per_token`` ([N] each; None skipped) agree
+    in size: the kernels read them by those extents."""
+    N, H = hidden.shape
+    if weight.dim() != 2 or weight.shape[0] != H or labels.shape[0] != N:
+        raise ValueError("shape mismatch among hidden [N,H], weight [H,V], labels [N]")
+    for name, t in per_token:
+        if t is not None and (t.dim() != 1 or t.shape[0] != N):
+            raise ValueError(f"{name} must have N = {N} elements")
+
+
+def _entropy_per_token(reduction: str, entropy_reduction) -> int:
+    if entropy_reduction is None or entropy_reduction == reduction:
+        return 0
+    if entropy_reduction != "none":
+        raise ValueError("entropy_reduction must be None, 'none' or the reduction itself")
+    return 1
+
+
 def workspace_bytes(N: int, H: int, V: int, reduction: str = "none"):
     return flce_workspace_size(N, H, V, _REDUCTIONS[reduction])
 
@@ -344,10 +365,9 @@ def forward(hidden, weight, labels, ignore_index: int = -100, softcap: float = 0
     _require(hidden, torch.bfloat16, 2, "hidden")
     _require(weight, torch.bfloat16, 2, "weight")
     _require(labels, torch.int64, 1, "labels")
+    check_shapes(hidden, weight, labels)
     N, H = hidden.shape
     V = weight.shape[1]
-    if weight.shape[0] != H or labels.shape[0] != N:
-        raise ValueError("shape mismatch among hidden [N,H], weight [H,V], labels [N]")
     red = _REDUCTIONS[reduction]
     fbytes, _ = flce_workspace_size(N, H, V, red)
     if workspace is None or workspace.numel() < fbytes:
@@ -389,16 +409,30 @@ def forward(hidden, weight, labels, ignore_index: int = -100, softcap: float = 0
     return out
 
 
+def _check_grads(grads, N, red, reduction, ept):
+    torch = _torch()
+    for g, name in grads:
+        if g is not None:
+            _require(g, torch.float32, 1, name)
+            want = N if (red == FLCE_REDUCTION_NONE or (ept and name == "grad_entropy")) else 1
+            if g.shape[0] != want:
+                raise ValueError(f"{name} must have {want} element(s) under '{reduction}'")
+
+
 def backward(hidden, weight, labels, lse, entropy, grad_logprob=None, grad_entropy=None,
              ignore_index: int = -100, softcap: float = 0.0, reduction: str = "none",
              grad_uniform_ce=None, grad_z_loss=None, z_loss_scale: float = 0.0,
-             grad_dtype: str = "bf16", class_weight=None, workspace=None):
+             grad_dtype: str = "bf16", class_weight=None, entropy_reduction=None,
+             workspace=None):
     """(grad_hidden [N,H], grad_weight [H,V]), bf16 or fp32 (``grad_dtype``).
 
     Upstream gradients: fp32 [N] under "none", fp32 [1] under "mean" and
-    "sum", or None for zero; class_weight as for ``forward``. Without the
-    auxiliary gradients, z-loss, "sum", class weights and fp32 outputs this
-    calls flce_backward, else flce_backward_ex.
+    "sum", or None for zero; with ``entropy_reduction="none"`` under "mean" /
+    "sum" the entropy's gradient is per token [N] (the entropy taken
+    unreduced beside the reduced logprob; options field entropy_per_token).
+    class_weight as for ``forward``. Without the auxiliary gradients, z-loss,
+    "sum", class weights, a per-token entropy and fp32 outputs this calls
+    flce_backward, else flce_backward_ex.
     """
     torch = _torch()
     _require(hidden, torch.bfloat16, 2, "hidden")
@@ -406,18 +440,15 @@ def backward(hidden, weight, labels, lse, entropy, grad_logprob=None, grad_entro
     _require(labels, torch.int64, 1, "labels")
     _require(lse, torch.float32, 1, "lse")
     _require(entropy, torch.float32, 1, "entropy")
+    check_shapes(hidden, weight, labels, ("lse", lse), ("entropy", entropy))
     N, H = hidden.shape
     V = weight.shape[1]
     red = _REDUCTIONS[reduction]
     gdt = _GRAD_DTYPES[grad_dtype]
-    want = N if red == FLCE_REDUCTION_NONE else 1
+    ept = _entropy_per_token(reduction, entropy_reduction)
     grads = ((grad_logprob, "grad_logprob"), (grad_entropy, "grad_entropy"),
              (grad_uniform_ce, "grad_uniform_ce"), (grad_z_loss, "grad_z_loss"))
-    for g, name in grads:
-        if g is not None:
-            _require(g, torch.float32, 1, name)
-            if g.shape[0] != want:
-                raise ValueError(f"{name} must have {want} element(s) under '{reduction}'")
+    _check_grads(grads, N, red, reduction, ept)
     _, bbytes = flce_workspace_size(N, H, V, red)
     if workspace is None or workspace.numel() < bbytes:
         workspace = torch.empty(max(bbytes, 256), dtype=torch.uint8, device=hidden.device)
@@ -426,7 +457,8 @@ def backward(hidden, weight, labels, lse, entropy, grad_logprob=None, grad_entro
     gw = torch.empty((H, V), dtype=odt, device=hidden.device)
     _check_class_weight(class_weight, V)
     extended = (grad_uniform_ce is not None or grad_z_loss is not None or z_loss_scale != 0.0
-                or red == FLCE_REDUCTION_SUM or gdt != FLCE_GRAD_BF16 or class_weight is not None)
+                or red == FLCE_REDUCTION_SUM or gdt != FLCE_GRAD_BF16 or class_weight is not None
+                or ept)
     if not extended:
         flce_backward(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), N, H, V,
                       int(ignore_index), float(softcap), red, lse.data_ptr(), entropy.data_ptr(),
@@ -434,7 +466,7 @@ def backward(hidden, weight, labels, lse, entropy, grad_logprob=None, grad_entro
                       workspace.data_ptr(), workspace.numel(), _stream())
         return gh, gw
     opt = FlceOptions(int(ignore_index), float(softcap), red, float(z_loss_scale), gdt,
-                      _ptr(class_weight))
+                      _ptr(class_weight), ept)
     flce_backward_ex(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), N, H, V, opt,
                      lse.data_ptr(), entropy.data_ptr(), _ptr(grad_logprob), _ptr(grad_entropy),
                      _ptr(grad_uniform_ce), _ptr(grad_z_loss), gh.data_ptr(), gw.data_ptr(),
@@ -446,33 +478,29 @@ def forward_backward(hidden, weight, labels, grad_logprob=None, grad_entropy=Non
                      ignore_index: int = -100, softcap: float = 0.0, reduction: str = "none",
                      grad_uniform_ce=None, grad_z_loss=None, z_loss_scale: float = 0.0,
                      grad_dtype: str = "bf16", aux: bool = False, chunk_tokens: int = 0,
-                     class_weight=None, workspace=None) -> dict:
+                     class_weight=None, entropy_reduction=None, workspace=None) -> dict:
     """The fused forward + backward (flce_forward_backward): the outputs of
     ``forward`` and, under "grad_hidden" / "grad_weight", the gradients of
     ``backward`` for upstream gradients known before the call (fp32 [N] under
-    "none", [1] under "mean" and "sum", None for zero).
+    "none", [1] under "mean" and "sum", None for zero; entropy_reduction as
+    for ``backward``).
     """
     torch = _torch()
     _require(hidden, torch.bfloat16, 2, "hidden")
     _require(weight, torch.bfloat16, 2, "weight")
     _require(labels, torch.int64, 1, "labels")
+    check_shapes(hidden, weight, labels)
     N, H = hidden.shape
     V = weight.shape[1]
-    if weight.shape[0] != H or labels.shape[0] != N:
-        raise ValueError("shape mismatch among hidden [N,H], weight [H,V], labels [N]")
     red = _REDUCTIONS[reduction]
     gdt = _GRAD_DTYPES[grad_dtype]
-    want = N if red == FLCE_REDUCTION_NONE else 1
+    ept = _entropy_per_token(reduction, entropy_reduction)
     grads = ((grad_logprob, "grad_logprob"), (grad_entropy, "grad_entropy"),
              (grad_uniform_ce, "grad_uniform_ce"), (grad_z_loss, "grad_z_loss"))
-    for g, name in grads:
-        if g is not None:
-            _require(g, torch.float32, 1, name)
-            if g.shape[0] != want:
-                raise ValueError(f"{name} must have {want} element(s) under '{reduction}'")
+    _check_grads(grads, N, red, reduction, ept)
     _check_class_weight(class_weight, V)
     opt = FlceOptions(int(ignore_index), float(softcap), red, float(z_loss_scale), gdt,
-                      _ptr(class_weight))
+                      _ptr(class_weight), ept)
     nbytes = flce_fused_workspace_size(N, H, V, opt, int(chunk_tokens))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=hidden.device)

@@ -23,7 +23,7 @@ class LinearCrossEntropy(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, hidden, weight, labels, reduction="mean", ignore_index=-100, softcap=0.0,
-                class_weight=None):
+                class_weight=None, entropy_reduction=None):
         out = flce.forward(hidden, weight, labels, ignore_index=ignore_index, softcap=softcap,
                            reduction=reduction, class_weight=class_weight)
         ctx.save_for_backward(hidden, weight, labels, out["lse"], out["entropy"])
@@ -31,33 +31,40 @@ class LinearCrossEntropy(torch.autograd.Function):
         ctx.reduction = reduction
         ctx.ignore_index = ignore_index
         ctx.softcap = softcap
-        if reduction == "none":
-            return out["logprob"], out["entropy"]
-        return (out[f"logprob_{reduction}"].reshape(()), out[f"entropy_{reduction}"].reshape(()))
+        ctx.entropy_tokens = reduction == "none" or entropy_reduction == "none"
+        ctx.entropy_reduction = entropy_reduction
+        lp = out["logprob"] if reduction == "none" else out[f"logprob_{reduction}"].reshape(())
+        ent = out["entropy"] if ctx.entropy_tokens else out[f"entropy_{reduction}"].reshape(())
+        return lp, ent
 
     @staticmethod
     def backward(ctx, grad_logprob, grad_entropy):
         hidden, weight, labels, lse, entropy = ctx.saved_tensors
-        n = hidden.shape[0] if ctx.reduction == "none" else 1
+        n = hidden.shape[0]
 
-        def prep(g):
-            return None if g is None else g.float().reshape(n).contiguous()
+        def prep(g, size):
+            return None if g is None else g.float().reshape(size).contiguous()
 
-        gh, gw = flce.backward(hidden, weight, labels, lse, entropy, prep(grad_logprob),
-                               prep(grad_entropy), ignore_index=ctx.ignore_index,
-                               softcap=ctx.softcap, reduction=ctx.reduction,
-                               class_weight=ctx.class_weight)
-        return gh, gw, None, None, None, None, None
+        gh, gw = flce.backward(hidden, weight, labels, lse, entropy,
+                               prep(grad_logprob, n if ctx.reduction == "none" else 1),
+                               prep(grad_entropy, n if ctx.entropy_tokens else 1),
+                               ignore_index=ctx.ignore_index, softcap=ctx.softcap,
+                               reduction=ctx.reduction, class_weight=ctx.class_weight,
+                               entropy_reduction=ctx.entropy_reduction)
+        return gh, gw, None, None, None, None, None, None
 
 
 def linear_cross_entropy(hidden, weight, labels, reduction="mean", ignore_index=-100,
-                         softcap=0.0, class_weight=None):
+                         softcap=0.0, class_weight=None, entropy_reduction=None):
     """(logprob, entropy) for hidden bf16 [N,H], weight bf16 [H,V], labels
     int64 [N]: per token ([N] fp32) under reduction "none", else the mean over
     the non-ignored tokens ("mean") or their sum ("sum"), 0-d fp32 tensors.
+    ``entropy_reduction="none"`` returns the entropy per token ([N], 0 at
+    ignored tokens) beside the reduced logprob, the output shapes of the verl
+    pull request #462 "Equivalent compute logic"; None reduces both alike.
     class_weight (fp32 [V], "mean" / "sum" only) weights token t by
-    class_weight[labels[t]] in both reductions; the mean then divides by the
+    class_weight[labels[t]] in the reductions; the mean then divides by the
     weight sum of the non-ignored tokens. Differentiable with respect to
     hidden and weight (gradients in bf16)."""
     return LinearCrossEntropy.apply(hidden, weight, labels, reduction, ignore_index, softcap,
-                                    class_weight)
+                                    class_weight, entropy_reduction)

@@ -125,10 +125,10 @@ def test_profile_hooks_host_only():
 
 def _opt(**kw):
     o = dict(ignore_index=-100, softcap=0.0, reduction=0, z_loss_scale=0.0, grad_dtype=0,
-             class_weight=None)
+             class_weight=None, entropy_per_token=0)
     o.update(kw)
     return flce.FlceOptions(o["ignore_index"], o["softcap"], o["reduction"], o["z_loss_scale"],
-                            o["grad_dtype"], o["class_weight"])
+                            o["grad_dtype"], o["class_weight"], o["entropy_per_token"])
 
 
 def _fwd_ex(opt=None, **kw):
@@ -174,6 +174,7 @@ def test_forward_ex_rejects(okw, kw, code):
     (dict(z_loss_scale=float("nan")), {}, 9), (dict(grad_dtype=-1), {}, 9),
     (dict(grad_dtype=1), dict(V=(1 << 21) + 8), 2),           # fp32 gradients: V <= 2^21
     (dict(class_weight=A), {}, 9), (dict(reduction=1, class_weight=A + 1), {}, 4),
+    (dict(reduction=1, entropy_per_token=2), {}, 9), (dict(entropy_per_token=-1), {}, 9),
     (dict(), dict(gw=None), 1), (dict(), dict(gh=A + 4), 4), (dict(), dict(wsb=8), 5),
 ])
 def test_backward_ex_rejects(okw, kw, code):
@@ -181,11 +182,45 @@ def test_backward_ex_rejects(okw, kw, code):
 
 
 def test_options_layout():
-    # flce_options_t: int64, float, int, float, int, pointer -> 32 bytes with
-    # natural alignment (4 bytes of padding before the pointer).
-    assert ctypes.sizeof(flce.FlceOptions) == 32
+    # flce_options_t: int64, float, int, float, int, pointer, int -> 40 bytes
+    # with natural alignment (4 bytes of padding before the pointer and at
+    # the end).
+    assert ctypes.sizeof(flce.FlceOptions) == 40
     assert flce.FlceOptions.reduction.offset == 12 and flce.FlceOptions.grad_dtype.offset == 20
     assert flce.FlceOptions.class_weight.offset == 24
+    assert flce.FlceOptions.entropy_per_token.offset == 32
+    assert flce.flce_version() == 212
+
+
+def test_binding_shape_checks():
+    """The torch wrappers refuse tensors whose extents disagree before any
+    launch (the kernels read every tensor by N, H and V): hidden [N,H],
+    weight [H,V], labels [N], and the saved lse / entropy [N]."""
+    import torch
+    h = torch.zeros(6, 8)
+    w = torch.zeros(8, 5)
+    y = torch.zeros(6, dtype=torch.int64)
+    v = torch.zeros(6)
+    flce.check_shapes(h, w, y, ("lse", v), ("entropy", v))
+    with pytest.raises(ValueError):
+        flce.check_shapes(h, torch.zeros(7, 5), y)
+    with pytest.raises(ValueError):
+        flce.check_shapes(h, w, torch.zeros(5, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        flce.check_shapes(h, w, y, ("lse", torch.zeros(5)))
+    with pytest.raises(ValueError):
+        flce.check_shapes(h, w, y, ("lse", v), ("entropy", torch.zeros(7)))
+    with pytest.raises(ValueError):
+        flce.check_shapes(h, torch.zeros(8), y)
+
+
+def test_entropy_reduction_argument():
+    assert flce._entropy_per_token("mean", None) == 0
+    assert flce._entropy_per_token("mean", "mean") == 0
+    assert flce._entropy_per_token("none", "none") == 0
+    assert flce._entropy_per_token("sum", "none") == 1
+    with pytest.raises(ValueError):
+        flce._entropy_per_token("none", "mean")
 
 
 def test_workspace_size_any_vocabulary():
@@ -266,7 +301,7 @@ def test_forward_backward_rejects(okw, kw, code):
 
 def test_fused_workspace_size():
     o = _opt()
-    one = flce.flce_fused_workspace_size(8192, 4096, 128256, o, 0)
+    one = flce.flce_fused_workspace_size(8192, 4096, 128256, o, 8192)
     four = flce.flce_fused_workspace_size(8192, 4096, 128256, o, 2048)
     vt = -(-128256 // 256) * 256
     # One chunk: both bf16 images of all 8192 x vt logits, the re-laid-out
@@ -277,11 +312,21 @@ def test_fused_workspace_size():
     assert four < one
     # fp32 gradients accumulate dW in grad_weight itself.
     assert flce.flce_fused_workspace_size(8192, 4096, 128256, _opt(grad_dtype=1), 2048) < four
-    # The default keeps all tokens in one chunk when N <= 8192 + H, else
-    # takes chunks of 8192.
-    assert flce.flce_fused_workspace_size(8192, 4096, 128256, o, 8192) == one
+    # The default chunk is the largest whose two bf16 images fit in 1 GiB:
+    # 2048 tokens at V = 128256 (4 * 2048 * 128256 bytes), 8192 at V = 32000
+    # (one chunk for N = 4096), and at least 256 tokens.
+    assert flce.flce_fused_workspace_size(8192, 4096, 128256, o, 0) == four
     assert (flce.flce_fused_workspace_size(32768, 4096, 128256, o, 0)
-            == flce.flce_fused_workspace_size(32768, 4096, 128256, o, 8192))
+            == flce.flce_fused_workspace_size(32768, 4096, 128256, o, 2048))
+    assert (flce.flce_fused_workspace_size(4096, 4096, 32000, o, 0)
+            == flce.flce_fused_workspace_size(4096, 4096, 32000, o, 4096))
+    assert (flce.flce_fused_workspace_size(4096, 64, (1 << 21), o, 0)
+            == flce.flce_fused_workspace_size(4096, 64, (1 << 21), o, 256))
+    for N, V in ((8192, 128256), (8192, 256000), (32768, 152064), (4096, 32000)):
+        vt = -(-V // 256) * 256
+        d = flce.flce_fused_workspace_size(N, 4096, V, o, 0)
+        images = d - flce.flce_fused_workspace_size(N, 4096, V, o, 256) + 4 * 256 * vt
+        assert images <= (1 << 30) + 4 * 256 * vt
     with pytest.raises(flce.FlceError):
         flce.flce_fused_workspace_size(8, 8, (1 << 21) + 8, o, 0)
 

@@ -119,6 +119,34 @@ def test_vocab_permutation():
     assert G.rel_l2(b["grad_hidden"], a["grad_hidden"]) <= 1e-3
 
 
+@pytest.mark.parametrize("path", ["recompute", "fused"])
+def test_duplicate_rows(path):
+    """Metamorphic: a token repeated elsewhere in the batch (same hidden row,
+    label and upstream gradients) gets the same per-token outputs and the same
+    grad_hidden row, bit for bit (every token is computed by the same
+    arithmetic whatever its position; duplicates far apart land in different
+    token tiles and, under compaction, at shifted positions)."""
+    wl, x = _inputs("dw_split")
+    rng = np.random.default_rng(11)
+    src = rng.choice(wl.N, 24, replace=False)
+    dst = rng.choice(np.setdiff1d(np.arange(wl.N), src), 24, replace=False)
+    xd = dict(x)
+    for k in ("hidden", "labels", "grad_logprob", "grad_entropy"):
+        xd[k] = x[k].copy()
+        xd[k][dst] = x[k][src]
+    t = G.upload(xd)
+    if path == "recompute":
+        got = G.run(wl, t)
+    else:
+        res = flce.forward_backward(t["hidden"], t["weight"], t["labels"], t["grad_logprob"],
+                                    t["grad_entropy"], ignore_index=wl.ignore_index)
+        torch.cuda.synchronize()
+        got = {k: res[k].float().cpu().numpy()
+               for k in ("lse", "logprob", "entropy", "grad_hidden")}
+    for k in ("lse", "logprob", "entropy", "grad_hidden"):
+        assert np.array_equal(got[k][dst], got[k][src]), k
+
+
 def test_invalid_labels_counted():
     """Labels outside [0, V) that are not ignore_index count in the status
     word and are treated as ignored."""
