@@ -95,8 +95,10 @@ typedef enum {
   FLCE_ERR_BAD_SOFTCAP = 6,       /* softcap is NaN or infinite */
   FLCE_ERR_HIP = 7,               /* a HIP runtime call or kernel launch failed */
   FLCE_ERR_INVALID_LABEL = 8,     /* reported only by flce_get_status */
-  FLCE_ERR_BAD_OPTION = 9         /* z_loss_scale negative or not finite, unknown grad_dtype,
+  FLCE_ERR_BAD_OPTION = 9,        /* z_loss_scale negative or not finite, unknown grad_dtype,
                                    * class_weight under NONE, entropy_per_token not 0 or 1 */
+  FLCE_ERR_TOO_LARGE = 10         /* flce_forward_noalloc: the shape needs more scratch than
+                                   * FLCE_NOALLOC_SCRATCH_BYTES */
 } flce_status_t;
 
 enum { FLCE_REDUCTION_NONE = 0, FLCE_REDUCTION_MEAN = 1, FLCE_REDUCTION_SUM = 2 };
@@ -171,6 +173,30 @@ flce_status_t flce_backward(const void* hidden, const void* weight, const int64_
                             const float* grad_logprob, const float* grad_entropy,
                             void* grad_hidden, void* grad_weight,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Forward without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). Arguments, outputs and errors as flce_forward, minus
+ * the workspace: the call runs in a scratch array of FLCE_NOALLOC_SCRATCH_BYTES
+ * that the library holds in every device it runs on until the process ends
+ * (its address is looked up once per device, on the first call with that
+ * device current; `stream` must belong to the current device). Shapes whose
+ * forward workspace (flce_workspace_size) exceeds that size are refused with
+ * FLCE_ERR_TOO_LARGE before anything is enqueued (about N * (16 ceil(V/256) +
+ * 2 H) bytes must fit, e.g. N = 2048 at H = 4096, V = 128256; a vocabulary
+ * that is not a multiple of 8 adds 2 H V). The call allocates nothing,
+ * enqueues kernels only, and writes every scratch byte it reads before
+ * reading it. All calls on one device share that device's array: calls that
+ * overlap in time on one device (two streams, two threads) race and give
+ * wrong results; serialise them. The invalid-label count of these calls is
+ * not reported (flce_get_status needs a workspace); such labels are treated
+ * as ignored as in flce_forward. */
+#define FLCE_NOALLOC_SCRATCH_BYTES (64u << 20)
+flce_status_t flce_forward_noalloc(const void* hidden, const void* weight, const int64_t* labels,
+                                   int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                                   float softcap, int reduction,
+                                   float* lse, float* logprob, float* entropy,
+                                   float* logprob_mean, float* entropy_mean, void* stream);
 
 /* Options of the extended entry points. class_weight was added in version
  * 211 (flce_version), entropy_per_token in version 212; the struct grew from

@@ -1146,6 +1146,57 @@ flce_status_t flce_forward(const void* hidden, const void* weight, const int64_t
                       nullptr, red, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The no-allocation forward's scratch: one array per device that the library
+// runs on, held until the process ends. In host code `noalloc_scratch` names
+// a host-side stand-in, not device memory: only the per-device address that
+// hipGetSymbolAddress returns is ever handed to kernels.
+constexpr size_t kNoallocScratchBytes = (size_t)FLCE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char noalloc_scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex noalloc_mu;
+void* noalloc_ptr[kMaxDevices] = {};
+
+// The current device's copy of the scratch array (looked up once per device,
+// with that device current).
+flce_status_t noalloc_scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FLCE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(noalloc_mu);
+  if (noalloc_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch)) != hipSuccess || p == nullptr)
+      return FLCE_ERR_HIP;
+    noalloc_ptr[dev] = p;
+  }
+  *out = noalloc_ptr[dev];
+  return FLCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+flce_status_t flce_forward_noalloc(const void* hidden, const void* weight, const int64_t* labels,
+                                   int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                                   float softcap, int reduction, float* lse, float* logprob,
+                                   float* entropy, float* logprob_mean, float* entropy_mean,
+                                   void* stream) {
+  FLCE_TRY(check_shape(N, H, V));
+  const flce_options_t o{ignore_index, softcap, reduction, 0.f, FLCE_GRAD_BF16, nullptr};
+  FLCE_TRY(check_options(&o));
+  if (make_plan(N, H, V, reduction).f_total > kNoallocScratchBytes) return FLCE_ERR_TOO_LARGE;
+  void* scratch = nullptr;
+  FLCE_TRY(noalloc_scratch_ptr(&scratch));
+  return flce_forward(hidden, weight, labels, N, H, V, ignore_index, softcap, reduction, lse,
+                      logprob, entropy, logprob_mean, entropy_mean, scratch,
+                      kNoallocScratchBytes, stream);
+}
+
 flce_status_t flce_forward_ex(const void* hidden, const void* weight, const int64_t* labels,
                               int64_t N, int64_t H, int64_t V, const flce_options_t* opt,
                               float* lse, float* logprob, float* entropy, float* uniform_ce,
@@ -1360,6 +1411,9 @@ const char* flce_status_string(flce_status_t s) {
     case FLCE_ERR_BAD_OPTION:
       return "z_loss_scale must be finite and >= 0; grad_dtype BF16 or F32; class_weight needs "
              "MEAN or SUM; entropy_per_token 0 or 1";
+    case FLCE_ERR_TOO_LARGE:
+      return "the call needs more scratch than flce_forward_noalloc's static buffer "
+             "(FLCE_NOALLOC_SCRATCH_BYTES) holds; use flce_forward with a workspace";
   }
   return "unknown status";
 }

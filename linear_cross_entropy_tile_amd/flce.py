@@ -27,6 +27,7 @@ __all__ = [
     "FLCE_GRAD_BF16", "FLCE_GRAD_F32", "FlceOptions",
     "flce_workspace_size", "flce_forward", "flce_backward", "flce_forward_ex",
     "flce_backward_ex", "flce_fused_workspace_size", "flce_forward_backward", "flce_get_status",
+    "flce_forward_noalloc", "FLCE_NOALLOC_SCRATCH_BYTES",
     "flce_status_string", "flce_version", "flce_profile_enable", "flce_profile_reset",
     "flce_profile_kinds", "flce_profile_read", "profile_table", "flce_probe_mfma_rate",
     "forward", "backward", "forward_backward", "workspace_bytes", "check_shapes",
@@ -47,8 +48,9 @@ STATUS_NAMES = {
     0: "FLCE_OK", 1: "FLCE_ERR_NULL_POINTER", 2: "FLCE_ERR_BAD_SHAPE",
     3: "FLCE_ERR_BAD_REDUCTION", 4: "FLCE_ERR_MISALIGNED",
     5: "FLCE_ERR_WORKSPACE_TOO_SMALL", 6: "FLCE_ERR_BAD_SOFTCAP", 7: "FLCE_ERR_HIP",
-    8: "FLCE_ERR_INVALID_LABEL", 9: "FLCE_ERR_BAD_OPTION",
+    8: "FLCE_ERR_INVALID_LABEL", 9: "FLCE_ERR_BAD_OPTION", 10: "FLCE_ERR_TOO_LARGE",
 }
+FLCE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class FlceOptions(ctypes.Structure):
@@ -70,6 +72,8 @@ _SIG = {
     "flce_backward": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
                                      ctypes.c_int, _P, _P, _P, _P, _P, _P, _P,
                                      ctypes.c_size_t, _P]),
+    "flce_forward_noalloc": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
+                                            ctypes.c_int, _P, _P, _P, _P, _P, _P]),
     "flce_forward_ex": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, ctypes.POINTER(FlceOptions),
                                        _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "flce_backward_ex": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, ctypes.POINTER(FlceOptions),
@@ -153,6 +157,13 @@ def flce_forward(hidden, weight, labels, N, H, V, ignore_index, softcap, reducti
     _check(lib().flce_forward(hidden, weight, labels, N, H, V, ignore_index, softcap, reduction,
                               lse, logprob, entropy, logprob_mean, entropy_mean, workspace,
                               workspace_bytes, stream), "flce_forward")
+
+
+def flce_forward_noalloc(hidden, weight, labels, N, H, V, ignore_index, softcap, reduction,
+                         lse, logprob, entropy, logprob_mean, entropy_mean, stream):
+    _check(lib().flce_forward_noalloc(hidden, weight, labels, N, H, V, ignore_index, softcap,
+                                      reduction, lse, logprob, entropy, logprob_mean,
+                                      entropy_mean, stream), "flce_forward_noalloc")
 
 
 def flce_backward(hidden, weight, labels, N, H, V, ignore_index, softcap, reduction,

@@ -42,7 +42,7 @@ def test_exports_match_header():
 
 
 def test_status_strings():
-    for code in range(10):
+    for code in range(11):
         assert flce.flce_status_string(code)
     assert "unknown" in flce.flce_status_string(99)
 
@@ -100,6 +100,28 @@ def test_forward_rejects(kw, code):
 ])
 def test_backward_rejects(kw, code):
     assert _bwd(**kw) == code
+
+
+def _fwd_noalloc(**kw):
+    args = dict(hidden=A, weight=A, labels=A, N=4, H=8, V=8, ii=-100, cap=0.0, red=0,
+                lse=A, lp=A, ent=A, lpm=None, entm=None, st=None)
+    args.update(kw)
+    return flce.lib().flce_forward_noalloc(args["hidden"], args["weight"], args["labels"],
+                                           args["N"], args["H"], args["V"], args["ii"],
+                                           args["cap"], args["red"], args["lse"], args["lp"],
+                                           args["ent"], args["lpm"], args["entm"], args["st"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), 2), (dict(H=12), 4), (dict(red=7), 3), (dict(cap=float("inf")), 6),
+    # forward workspace beyond the static scratch: 16 * N * ceil(V/256) + 2 N H bytes
+    (dict(N=8192, H=4096, V=128256), 10), (dict(N=1 << 20, H=64, V=512), 10),
+    (dict(N=4096, H=4096, V=128256 + 1), 10),   # the padded weight copy alone is 1 GB
+])
+def test_forward_noalloc_rejects(kw, code):
+    """The static-scratch forward refuses bad arguments and shapes that do not
+    fit its scratch on the host, before it looks up the device array."""
+    assert _fwd_noalloc(**kw) == code
 
 
 def test_workspace_size():
