@@ -10,6 +10,8 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libflce.so")
 SOURCES = [os.path.join(PKG, "csrc", "flce_api.hip")]
 HEADERS = [os.path.join(ROOT, "include", "flce.h"),
+           os.path.join(PKG, "csrc", "flce_layout.hpp"),
+           os.path.join(PKG, "csrc", "flce_plan.hpp"),
            os.path.join(PKG, "csrc", "flce_gemm.hpp"),
            os.path.join(PKG, "csrc", "flce_kernels.hpp")]
 

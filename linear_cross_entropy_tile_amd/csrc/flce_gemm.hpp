@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "flce_layout.hpp"
+
 namespace flce {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -52,13 +54,9 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int kTile = 256;                          // M and N extent of a block tile; strip height
-constexpr int kBK = 32;                             // K values per block / LDS stage
 constexpr int kStages = 4;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBlockBytes = kTile * kBK * 2;        // 16 KiB: one K block of one strip
-constexpr int kBlockElems = kBlockBytes / 2;
 constexpr int kDmaBlocks = kBlockBytes / 1024 / kWaves;  // 1 KiB DMA pieces per wave per block
 
 // Byte offset of element (r, k) inside a block (r < 256, k < 32).

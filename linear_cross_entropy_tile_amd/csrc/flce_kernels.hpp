@@ -515,18 +515,8 @@ __device__ __forceinline__ float mean_divisor_inv(const int32_t* header, bool we
   return d != 0.0 ? (float)(1.0 / d) : 0.f;
 }
 
-// Per-token constants of the logit gradient (see bwd_dlogits_kernel):
-//   dz'_v = gbar [v == y] + k0 - p_v (ebar z'_v + cs),
-//   cs = gbar - ebar S - gu - 2 lam gz lse,  k0 = -gu / V,
-// from the upstream gradients gbar (logprob), ebar (entropy), gu
-// (uniform_ce) and gz (z_loss). Ignored tokens: lse = 1e30 (every p
-// underflows to 0) and zeros.
-struct DzToken {
-  float lse, ebar, cs, gbar;
-  float k0, pad0, pad1, pad2;
-};
-
-constexpr int kCombineTokens = 64;   // tokens per combine block (one per lane)
+// DzToken (the per-token constants of the logit gradient) and kCombineTokens:
+// flce_layout.hpp.
 constexpr int kCombineWaves = 16;    // vocabulary-tile groups per combine block
 
 // Block of 1024 threads for 64 tokens: wave w merges the partial states of
