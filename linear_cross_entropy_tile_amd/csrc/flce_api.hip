@@ -472,10 +472,9 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
   for (int c = 0; c < p.nchunks; ++c) {
     const int64_t v0 = (int64_t)c * p.Vc;
     const int64_t vc = V - v0 < p.Vc ? V - v0 : p.Vc;
-    const int64_t vc8 = p.V8 - v0 < p.Vc ? p.V8 - v0 : p.Vc;  // columns of the (padded) copy
     const int vtc = (int)ceil_div(vc, kTile);
-    FLCE_TRY(pack_rows(K_PACK_WEIGHT, wrd + v0, H, vc8, p.V8, p.kbv, nullptr, nullptr, wb, st));
 
+    // bwd_dlogits also writes the chunk's weight image for dH (wimg).
     DlogitsArgs d{};
     d.weight = wrd;
     d.ldw = p.V8;
@@ -498,6 +497,7 @@ flce_status_t backward_impl(const void* hidden, const void* weight, const int64_
     d.inv_cap = capped ? 1.f / softcap : 0.f;
     d.dtv = dtv;
     d.dvt = dvt;
+    d.wimg = wb;
     FLCE_TRY(launch(K_BWD_DLOGITS, st, [&] {
       if (capped)
         bwd_dlogits_kernel<true><<<vtc * p.TB, kThreads, 0, st>>>(d);
@@ -676,7 +676,7 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
       FLCE_TRY(pad_cols(weight, H, V, p.V8, wp, st));
       wrd = wp;
     }
-    FLCE_TRY(pack_rows(K_PACK_WEIGHT, wrd, H, p.V8, p.V8, f.kbv, nullptr, nullptr, wb, st));
+    // The weight image for dH (wb) is written by the first chunk's logit tiles.
     const int64_t mld = (int64_t)f.TBc * kTile;
     for (int c = 0; c < f.nchunks; ++c) {
       const int tb0 = c * f.TBc;
@@ -706,6 +706,7 @@ flce_status_t fused_impl(const void* hidden, const void* weight, const int64_t* 
       a.kbv = f.kbv;
       a.mref = mref;
       a.mld = mld;
+      a.wimg = c == 0 ? wb : nullptr;
       FLCE_TRY(launch(K_FUSED_TILE, st, [&] {
         if (capped)
           fused_tile_kernel<true><<<tbc * p.VT, kThreads, 0, st>>>(a);

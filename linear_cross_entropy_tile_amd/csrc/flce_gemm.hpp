@@ -124,6 +124,9 @@ __device__ __forceinline__ f32x4_t buf_load_f32x4(__amdgpu_buffer_rsrc_t r, uint
 __device__ __forceinline__ void buf_store_f32x4(f32x4_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, voff, 0, 0);
 }
+__device__ __forceinline__ void buf_store_u32x4(u32x4_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 0);
+}
 
 // Keeps the compiler from hoisting work that depends on `x` out of a loop.
 template <class T>
@@ -366,6 +369,11 @@ __device__ __forceinline__ void interleave_reads() {
 // MFMAs of a half period, so the ping-pong schedule below would leave the
 // matrix units waiting on them. ASrc: BlockedA or RowA (already initialised by
 // the caller); AFrag: the matching fragment reader, FragSrc<4> or FragRow<4>.
+// A per-stage callback of the interleaved loop that does nothing.
+struct NoStageHook {
+  __device__ __forceinline__ void operator()(const char*, int) const {}
+};
+
 template <class ASrc, class AFrag>
 struct MainloopIL {
   struct Frags {
@@ -404,13 +412,18 @@ struct MainloopIL {
   // awaited and the block synchronises (the next stage is now complete in
   // LDS); the next block's sub-step 0 fragments are read while this block's
   // sub-step 1 MFMAs run (they only need registers).
-  template <int S>
+  // `hook(stage, k)` sees the complete A stage of K block k (kiss - 3) once;
+  // its LDS reads finish before the block barrier below, so before any wave
+  // refills that stage.
+  template <int S, class Hook>
   __device__ __forceinline__ void step(char* const (&sa)[kStages], char* const (&sb)[kStages],
-                                       Frags (&f)[2], Acc& acc, int kiss, int nk) {
+                                       Frags (&f)[2], Acc& acc, int kiss, int nk,
+                                       const Hook& hook) {
     constexpr int SI = (S + kStages - 1) % kStages;
     constexpr int SN = (S + 1) % kStages;
     issue(sa[SI], sb[SI], kiss, nk);
     frags(sa[S], sb[S], 1, f[1]);
+    hook(sa[S], kiss - (kStages - 1));
     mma(f[0], acc);
     // DMA issue first, then the fragment reads spread over the MFMAs, so the
     // LDS sees a steady stream rather than a burst per wave.
@@ -429,6 +442,12 @@ struct MainloopIL {
   // afterwards.
   __device__ __forceinline__ void run(char* const (&sa)[kStages], char* const (&sb)[kStages],
                                       const ASrc& A, const Strip& B, int bkb0, int nk, Acc& acc) {
+    run(sa, sb, A, B, bkb0, nk, acc, NoStageHook{});
+  }
+  template <class Hook>
+  __device__ __forceinline__ void run(char* const (&sa)[kStages], char* const (&sb)[kStages],
+                                      const ASrc& A, const Strip& B, int bkb0, int nk, Acc& acc,
+                                      const Hook& hook) {
     const int wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
 #pragma unroll
@@ -451,10 +470,10 @@ struct MainloopIL {
     frags(sa[0], sb[0], 0, f[0]);
     for (int kt = 0; kt < nk; kt += kStages) {
       const int k3 = kt + kStages - 1;
-      step<0>(sa, sb, f, acc, k3, nk);
-      if (kt + 1 < nk) step<1>(sa, sb, f, acc, k3 + 1, nk);
-      if (kt + 2 < nk) step<2>(sa, sb, f, acc, k3 + 2, nk);
-      if (kt + 3 < nk) step<3>(sa, sb, f, acc, k3 + 3, nk);
+      step<0>(sa, sb, f, acc, k3, nk, hook);
+      if (kt + 1 < nk) step<1>(sa, sb, f, acc, k3 + 1, nk, hook);
+      if (kt + 2 < nk) step<2>(sa, sb, f, acc, k3 + 2, nk, hook);
+      if (kt + 3 < nk) step<3>(sa, sb, f, acc, k3 + 3, nk, hook);
     }
     wait_vmcnt<0>();
     block_barrier();

@@ -273,6 +273,9 @@ struct FwdTileArgs {
   int kbv;
   float* mref;
   int64_t mld;
+  // STORE only, or null: the blocked weight as the dH operand (strips of 256
+  // hidden rows, K = vocabulary, kbv blocks each), written by this launch.
+  uint16_t* wimg;
 };
 
 // Copies a tile's eight 16 KiB blocks from the stage arrays (block b in sa[b]
@@ -362,6 +365,42 @@ __device__ __forceinline__ void column_stats(const Acc& acc, int j, float cap, f
   u = (up[0] + up[1]) + (up[2] + up[3]);
 }
 
+// The dH contraction reads the weight as its B operand in the blocked layout
+// (strips of 256 hidden rows, K = vocabulary). A logit-tile block streams the
+// same bytes through its A stages: the stage of K block k holds hidden rows
+// 32k .. 32k+31 of the tile's 256 vocabulary columns, i.e. rows
+// 32 (k % 8) .. +31 of strip k / 8 in the tile's 8 vocabulary blocks
+// kb0 .. kb0+7. One block per vocabulary tile (image_writer) copies every
+// stage into that image, so the image costs no pass over the weight of its
+// own. Rows past H in the last strip are left as they are: they only reach dH
+// columns past H, which are never stored.
+struct WeightImageHook {
+  uint16_t* img;  // block 0 of strip 0
+  int kbv;        // K blocks per strip
+  int kb0;        // the tile's first vocabulary block
+  __device__ __forceinline__ void operator()(const char* st, int k) const {
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(img + (int64_t)(k >> 3) * kbv * kBlockElems, (int64_t)kbv * kBlockBytes);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = (int)threadIdx.x + kThreads * i;  // 16-byte piece of the stage
+      const int kr = p >> 5, j = (p >> 2) & 7, c = p & 3;
+      // RowA stage layout: K row kr takes 512 bytes; its 16-byte slot s holds
+      // columns 32 ((s >> 2) ^ (kr & 3)) + 8 (s & 3) .. +7.
+      const u32x4_t v =
+          *reinterpret_cast<const u32x4_t*>(st + kr * 512 + ((((j ^ (kr & 3)) << 2) + c) << 4));
+      const int r = 32 * (k & 7) + kr;
+      buf_store_u32x4(v, rs, (uint32_t)((kb0 + j) * kBlockBytes + r * 64 + ((c ^ ((r >> 2) & 3)) << 4)));
+    }
+  }
+};
+
+// Whether tile (tb, vt) writes the weight image: the tile of token block
+// vt % tbv, so that the writers spread over token blocks and thus over XCDs.
+__device__ __forceinline__ bool image_writer(int tb, int vt, int tbv) {
+  return tb == vt % tbv;
+}
+
 // Block (tb, vt): tokens [256 tb, +256) against vocabulary [256 vt, +256).
 // The MFMA tile is z^T: rows = vocabulary (A = the [H,V] weight read
 // row-contiguous), cols = tokens (B = hidden strip), so each lane's 64
@@ -392,7 +431,17 @@ __device__ __forceinline__ void fwd_tile_body(const FwdTileArgs& a) {
     MainloopRowA ml;
     RowA A;
     A.init(a.weight, a.ldw, a.ldw, (int64_t)vt * kTile, 0, a.H);
-    ml.run(sa, sb, A, Strip{a.xb + (int64_t)tb * a.hkb * kBlockElems, a.hkb}, 0, a.hkb, acc);
+    const Strip B{a.xb + (int64_t)tb * a.hkb * kBlockElems, a.hkb};
+    bool wrote = false;
+    if constexpr (STORE) {
+      // As in bwd_dlogits_kernel: one tile per vocabulary tile writes the
+      // weight image for dH.
+      if (a.wimg != nullptr && image_writer(tbl, vt, tbv)) {
+        ml.run(sa, sb, A, B, 0, a.hkb, acc, WeightImageHook{a.wimg, a.kbv, 8 * vt});
+        wrote = true;
+      }
+    }
+    if (!wrote) ml.run(sa, sb, A, B, 0, a.hkb, acc);
   }
 
   const int vb = vt * kTile + wm * 128;  // first vocabulary row of this wave
@@ -828,6 +877,8 @@ struct DlogitsArgs {
   float cap, cap_k, inv_cap;
   uint16_t* dtv;           // blocked D, strips of 256 tokens, K = chunk vocabulary
   uint16_t* dvt;           // blocked D^T, strips of 256 chunk vocabulary rows, K = tokens
+  uint16_t* wimg;          // blocked weight chunk as the dH operand (strips of 256 hidden
+                           // rows, K = chunk vocabulary, kbv blocks each), written here; or null
 };
 
 // Per-token constants of the logit gradient.
@@ -963,7 +1014,13 @@ bwd_dlogits_kernel(DlogitsArgs a) {
     MainloopRowA ml;
     RowA A;
     A.init(a.weight, a.ldw, a.ldw, vg0, 0, a.H);
-    ml.run(sa, sb, A, Strip{a.xb + (int64_t)tb * a.hkb * kBlockElems, a.hkb}, 0, a.hkb, acc);
+    const Strip B{a.xb + (int64_t)tb * a.hkb * kBlockElems, a.hkb};
+    // One tile per vocabulary tile also writes its weight columns into the
+    // dH operand image.
+    if (a.wimg != nullptr && image_writer(tb, vt, tbv))
+      ml.run(sa, sb, A, B, 0, a.hkb, acc, WeightImageHook{a.wimg, a.kbv, 8 * vt});
+    else
+      ml.run(sa, sb, A, B, 0, a.hkb, acc);
   }
 
   // Each tile owns 8 consecutive K blocks in each image: dtv strip tb, blocks
