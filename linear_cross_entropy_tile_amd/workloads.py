@@ -19,7 +19,7 @@ import math
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "f32_to_bf16_bits",
-           "bf16_bits_to_f32", "sample_indices", "make_class_weights"]
+           "bf16_bits_to_f32", "sample_indices", "make_class_weights", "projection_matrix"]
 
 
 @dataclass(frozen=True)
@@ -235,3 +235,11 @@ def make_class_weights(V: int, seed: int, zero_fraction: float = 0.0) -> np.ndar
     if k:
         cw[rng.permutation(V)[:k]] = 0.0
     return cw
+
+
+def projection_matrix(dim: int, k: int, seed: int) -> np.ndarray:
+    """Seeded float32 [dim, k] with independent N(0, 1) entries: the random
+    directions onto which gradients are projected to compare every row and
+    column of them at full size."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    return rng.standard_normal((dim, k)).astype(np.float32)

@@ -1,18 +1,25 @@
 """Writes the stored expected values of the full-size parity tests.
 
 For each full-size workload this runs the float64 CPU oracle (and nothing
-else) on the seeded inputs and stores, in tests/golden/<workload>.npz:
+else: oracle.forward and oracle.backward, whose results the oracle pins fix)
+on the seeded inputs and stores, in tests/golden/<workload>.npz:
 
   lse, logprob, entropy   [N]   every token's statistics
   logprob_mean, entropy_mean    (reduction "mean" only; class-weighted for
                                  the "_weighted" variant)
   rows, dhidden_rows      sampled rows of dHidden      [len(rows), H]
   cols, dweight_cols      sampled columns of dWeight   [H, len(cols)]
+  dhidden_proj            dHidden @ R_h                [N, K_PROJ]
+  dweight_proj            R_w^T @ dWeight              [K_PROJ, V]
 
-Stored as float32 (the tolerances are 1e-3 relative and looser). The oracle
-materialises each block of 128 rows against the full vocabulary once and
-derives the statistics, the sampled dHidden rows and the contribution to the
-sampled dWeight columns from that block.
+R_h and R_w are seeded Gaussian [H, K_PROJ] matrices (workloads.
+projection_matrix with the seeds of ``projection_seeds``): the projections
+carry every row of dHidden and every column of dWeight, so the GPU test checks
+all of them, not a sample. The "_weighted" variant stores the sampled rows and
+columns only (its contractions are those of the plain workload).
+
+Stored as float32 (the tolerances are 1e-3 relative and looser). The full
+float64 dWeight is held in memory: up to 6.2 GB for the RL-rollout head.
 
 Run:  python tests/golden/make_golden.py [workload ...]
 """
@@ -37,12 +44,23 @@ FULL = ["llama3_head", "gemma2_softcap", "rl_rollout", "gemma2_softcap_weighted"
 WEIGHTED = {"gemma2_softcap_weighted": ("gemma2_softcap", 4242, 0.05)}
 N_ROWS = 16
 N_COLS = 16
+K_PROJ = 8
 
 
 def sample(wl):
     rows = W.sample_indices(wl.N, N_ROWS, wl.seed + 1000)
     cols = W.sample_indices(wl.V, N_COLS, wl.seed + 2000)
     return rows, cols
+
+
+def projection_seeds(wl):
+    """Seeds of R_h and R_w for a workload."""
+    return wl.seed + 3000, wl.seed + 4000
+
+
+def projections(wl):
+    sh, sw = projection_seeds(wl)
+    return W.projection_matrix(wl.H, K_PROJ, sh), W.projection_matrix(wl.H, K_PROJ, sw)
 
 
 def class_weights(name: str):
@@ -53,49 +71,36 @@ def class_weights(name: str):
     return W.make_class_weights(W.WORKLOADS[base].V, seed, zf)
 
 
-def golden(name: str, block: int = 128) -> str:
-    wl = W.WORKLOADS[WEIGHTED[name][0] if name in WEIGHTED else name]
-    cw = class_weights(name)
-    t0 = time.time()
-    x = W.make_inputs(wl)
+def expected(wl, x, cw=None, project=True) -> dict:
+    """The stored arrays for workload `wl` on inputs `x`, from oracle.forward
+    and oracle.backward."""
     h = W.bf16_bits_to_f32(x["hidden"])
-    w = W.bf16_bits_to_f32(x["weight"]).astype(np.float64)
-    labels, valid = O._valid_mask(x["labels"], wl.V, wl.ignore_index)
-    gb, eb = O._token_grads(labels, valid, wl.reduction, cw, x["grad_logprob"],
-                            x["grad_entropy"])
+    w = W.bf16_bits_to_f32(x["weight"])
+    fw = O.forward(h, w, x["labels"], ignore_index=wl.ignore_index, softcap_c=wl.softcap,
+                   reduction=wl.reduction, class_weight=cw)
+    dh, dw = O.backward(h, w, x["labels"], ignore_index=wl.ignore_index, softcap_c=wl.softcap,
+                        reduction=wl.reduction, grad_logprob=x["grad_logprob"],
+                        grad_entropy=x["grad_entropy"], class_weight=cw)
     rows, cols = sample(wl)
-    N, H = wl.N, wl.H
-    lse = np.zeros(N)
-    lp = np.zeros(N)
-    ent = np.zeros(N)
-    dh_rows = np.zeros((rows.size, H))
-    dw_cols = np.zeros((H, cols.size))
-    row_pos = {int(r): i for i, r in enumerate(rows)}
-    for r0 in range(0, N, block):
-        idx = np.arange(r0, min(N, r0 + block))
-        idx = idx[valid[idx]]
-        if idx.size == 0:
-            continue
-        zc = O.logits(h[idx], w, wl.softcap)
-        l_, s_, e_, _ = O.row_stats(zc)
-        lse[idx] = l_
-        ent[idx] = e_
-        lp[idx] = zc[np.arange(idx.size), labels[idx]] - l_
-        dz = O.dlogits(zc, labels[idx], l_, s_, gb[idx], eb[idx], wl.softcap)
-        dw_cols += h[idx].astype(np.float64).T @ dz[:, cols]
-        for k, r in enumerate(idx):
-            if int(r) in row_pos:
-                dh_rows[row_pos[int(r)]] = dz[k] @ w.T
-        if (r0 // block) % 16 == 0:
-            print(f"  {name}: rows {r0}/{N}  {time.time() - t0:.0f}s", flush=True)
-    out = {"lse": lse.astype(np.float32), "logprob": lp.astype(np.float32),
-           "entropy": ent.astype(np.float32), "rows": rows, "cols": cols,
-           "dhidden_rows": dh_rows.astype(np.float32), "dweight_cols": dw_cols.astype(np.float32)}
+    out = {"lse": fw["lse"].astype(np.float32), "logprob": fw["logprob"].astype(np.float32),
+           "entropy": fw["entropy"].astype(np.float32), "rows": rows, "cols": cols,
+           "dhidden_rows": dh[rows].astype(np.float32),
+           "dweight_cols": dw[:, cols].astype(np.float32)}
     if wl.reduction == "mean":
-        om = O._token_weights(labels, valid, wl.reduction, cw)[valid]
-        ws = om.sum()
-        out["logprob_mean"] = np.array([(om * lp[valid]).sum() / ws if ws else 0.0])
-        out["entropy_mean"] = np.array([(om * ent[valid]).sum() / ws if ws else 0.0])
+        out["logprob_mean"] = np.array([fw["logprob_mean"]])
+        out["entropy_mean"] = np.array([fw["entropy_mean"]])
+    if project:
+        rh, rw = projections(wl)
+        out["dhidden_proj"] = (dh @ rh.astype(np.float64)).astype(np.float32)
+        out["dweight_proj"] = (rw.astype(np.float64).T @ dw).astype(np.float32)
+    return out
+
+
+def golden(name: str) -> str:
+    wl = W.WORKLOADS[WEIGHTED[name][0] if name in WEIGHTED else name]
+    t0 = time.time()
+    print(f"  {name}: N={wl.N} H={wl.H} V={wl.V}", flush=True)
+    out = expected(wl, W.make_inputs(wl), class_weights(name), project=name not in WEIGHTED)
     path = os.path.join(HERE, f"{name}.npz")
     np.savez_compressed(path, **out)
     print(f"wrote {path} in {time.time() - t0:.0f}s", flush=True)

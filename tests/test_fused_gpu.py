@@ -164,7 +164,7 @@ FULL = ["llama3_head", "gemma2_softcap", "rl_rollout"]
 def test_fused_full_size(name):
     """At the full sizes, in the configuration the benchmark times, against
     the stored oracle values (every token's statistics; sampled dHidden rows
-    and dWeight columns)."""
+    and dWeight columns; every row and column through the projections)."""
     path = os.path.join(HERE, "golden", f"{name}.npz")
     if not os.path.exists(path):
         pytest.skip(f"{path} not generated")
@@ -192,6 +192,8 @@ def test_fused_full_size(name):
     assert e <= G.GRAD_REL_L2, f"{name} grad_hidden rows rel L2 {e:.2e}"
     e = G.rel_l2(gw_cols, ref["dweight_cols"])
     assert e <= G.GRAD_REL_L2, f"{name} grad_weight cols rel L2 {e:.2e}"
+    G.check_projections(name, wl, out["grad_hidden"], out["grad_weight"], ref,
+                        x["labels"] != wl.ignore_index)
     ign = torch.from_numpy(x["labels"] == wl.ignore_index).to(G.dev())
     if bool(ign.any()):
         assert torch.count_nonzero(out["grad_hidden"][ign]).item() == 0

@@ -4,13 +4,21 @@ values (tests/golden/<workload>.npz, written by tests/golden/make_golden.py,
 which calls only the oracle):
 
   * every token's lse / logprob / entropy (and the means under "mean"),
-  * sampled rows of dHidden and sampled columns of dWeight.
+  * sampled rows of dHidden and sampled columns of dWeight,
+  * every row of dHidden @ R_h and every column of R_w^T @ dWeight, for seeded
+    Gaussian R_h, R_w [H, 8]: each row and column of both gradients enters
+    the comparison.
 
 The Gemma2-shaped head is also run with seeded class weights (their stored
 variant gemma2_softcap_weighted).
 
 Tolerances: statistics within 2e-3 absolute or 1e-3 relative; gradients
-within 1e-2 relative L2 error over the sampled rows / columns.
+within 1e-2 relative L2 error over the sampled rows / columns, over the whole
+projections and over each block of 256 rows of dHidden @ R_h and 256 columns
+of R_w^T @ dWeight (the tiles of the contractions), and within 0.1 for each
+single row and column: an 8-dimensional projection of a gradient row that
+meets 1e-2 stays within a few times that by chance (the ratio of two such
+projections' norms), while a misplaced row, column or tile is off by order 1.
 """
 import os
 
@@ -52,6 +60,8 @@ def test_parity_full_size(name):
     assert e <= G.GRAD_REL_L2, f"{name} grad_hidden rows rel L2 {e:.2e}"
     e = G.rel_l2(gw_cols, ref["dweight_cols"])
     assert e <= G.GRAD_REL_L2, f"{name} grad_weight cols rel L2 {e:.2e}"
+    G.check_projections(name, wl, got["grad_hidden"], got["grad_weight"], ref,
+                        x["labels"] != wl.ignore_index)
     ign = torch.from_numpy(x["labels"] == wl.ignore_index).to(G.dev())
     if bool(ign.any()):
         assert torch.count_nonzero(got["grad_hidden"][ign]).item() == 0
