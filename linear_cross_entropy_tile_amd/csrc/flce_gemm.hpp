@@ -429,6 +429,8 @@ struct MainloopIL {
     // LDS sees a steady stream rather than a burst per wave.
     __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 2 * kDmaBlocks, 0);
     interleave_reads<kReads>();
+    // The hook's stores, if any, count here too: the wait may then also cover
+    // part of the next stage's DMA, never less than this one.
     wait_vmcnt<2 * kDmaBlocks * (kStages - 2)>();
     wait_lgkmcnt0();
     block_barrier();
