@@ -608,23 +608,33 @@ struct MainloopPP {
     }
     block_barrier();
     fence();
-    if (leader) {
-      for (int kt = 0; kt < nk; kt += kStages) {
-        lead<0>(sa, sb, f, acc, kt, nk);
-        if (kt + 1 < nk) lead<1>(sa, sb, f, acc, kt + 1, nk);
-        if (kt + 2 < nk) lead<2>(sa, sb, f, acc, kt + 2, nk);
-        if (kt + 3 < nk) lead<3>(sa, sb, f, acc, kt + 3, nk);
-      }
-    } else {
-      for (int kt = 0; kt < nk; kt += kStages) {
-        follow<0>(sa, sb, f, acc, kt, nk);
-        if (kt + 1 < nk) follow<1>(sa, sb, f, acc, kt + 1, nk);
-        if (kt + 2 < nk) follow<2>(sa, sb, f, acc, kt + 2, nk);
-        if (kt + 3 < nk) follow<3>(sa, sb, f, acc, kt + 3, nk);
-      }
-    }
+    if (leader)
+      leader_loop(sa, sb, f, acc, nk);
+    else
+      follower_loop(sa, sb, f, acc, nk);
     wait_vmcnt<0>();
     block_barrier();
+  }
+
+  __device__ __forceinline__ void leader_loop(char* const (&sa)[kStages],
+                                              char* const (&sb)[kStages], Frags& f, Acc& acc,
+                                              int nk) {
+    for (int kt = 0; kt < nk; kt += kStages) {
+      lead<0>(sa, sb, f, acc, kt, nk);
+      if (kt + 1 < nk) lead<1>(sa, sb, f, acc, kt + 1, nk);
+      if (kt + 2 < nk) lead<2>(sa, sb, f, acc, kt + 2, nk);
+      if (kt + 3 < nk) lead<3>(sa, sb, f, acc, kt + 3, nk);
+    }
+  }
+  __device__ __forceinline__ void follower_loop(char* const (&sa)[kStages],
+                                                char* const (&sb)[kStages], Frags& f, Acc& acc,
+                                                int nk) {
+    for (int kt = 0; kt < nk; kt += kStages) {
+      follow<0>(sa, sb, f, acc, kt, nk);
+      if (kt + 1 < nk) follow<1>(sa, sb, f, acc, kt + 1, nk);
+      if (kt + 2 < nk) follow<2>(sa, sb, f, acc, kt + 2, nk);
+      if (kt + 3 < nk) follow<3>(sa, sb, f, acc, kt + 3, nk);
+    }
   }
 };
 
