@@ -889,7 +889,24 @@ struct DzCoef {
   float gbar;     // upstream logprob gradient (the label term)
   float k0;       // -gu / V (the uniform cross-entropy term)
   float cap, cap_k, inv_cap;
+  // Capped tile from raw logits (see dz_column): a1 = -2 c log2(e),
+  // b1 = c log2(e) + nl, a2 = -8 c ebar, b2 = 4 (c ebar + cS), k4 = 4 k0,
+  // gk4 = 4 (gbar + k0).
+  float a1, b1, a2, b2, k4, gk4;
 };
+
+// The per-token constants of token coefficients c for the cap constants of kc.
+__device__ __forceinline__ DzCoef dz_coef(const DzToken& c, const DzCoef& kc) {
+  const float nl = -c.lse * kLog2e;
+  const float cl = kc.cap * kLog2e;
+  return DzCoef{nl,        c.ebar,
+                c.cs,      c.gbar,
+                c.k0,      kc.cap,
+                kc.cap_k,  kc.inv_cap,
+                -2.f * cl, cl + nl,
+                -8.f * kc.cap * c.ebar, 4.f * fmaf(kc.cap, c.ebar, c.cs),
+                4.f * c.k0, 4.f * (c.gbar + c.k0)};
+}
 
 // The logit gradient of token column j of a wave's 128 x 32 block, rounded to
 // bf16, for both blocked images (see bwd_dlogits_kernel). The accumulators
@@ -911,16 +928,29 @@ __device__ __forceinline__ void dz_column(const Acc& acc, int j, const DzCoef& k
       for (int r3 = 0; r3 < 4; ++r3) {
         const int o = i * 32 + 8 * rq + r3;
         float z = acc[i][j][rq * 4 + r3];
-        if constexpr (CAP && RAW) z = softcap_apply(z, k.cap, k.cap_k);
-        const float p = fast_exp2(fmaf(z, kLog2e, k.nl));
         float v;
-        if constexpr (LABEL)
-          v = fmaf(-p, fmaf(k.ebar, z, k.cS), o == yl ? k.gbar + k.k0 : k.k0);
-        else
-          v = fmaf(-p, fmaf(k.ebar, z, k.cS), k.k0);
-        if constexpr (CAP) {
-          const float qz = z * k.inv_cap;
-          v *= fmaf(-qz, qz, 1.f);
+        if constexpr (CAP && RAW) {
+          // In terms of r = 1 / (1 + e^(2z/c)): z' = c (1 - 2r) and
+          // 1 - (z'/c)^2 = 4 r (1 - r), so with the per-token constants of
+          // DzCoef (the factor 4 folded in) the capped gradient is
+          // (K4 - p (b2 + a2 r)) (r - r^2), p = 2^(a1 r + b1).
+          const float r = fast_rcp(fast_exp2(z * k.cap_k) + 1.f);
+          const float p = fast_exp2(fmaf(k.a1, r, k.b1));
+          if constexpr (LABEL)
+            v = fmaf(-p, fmaf(k.a2, r, k.b2), o == yl ? k.gk4 : k.k4);
+          else
+            v = fmaf(-p, fmaf(k.a2, r, k.b2), k.k4);
+          v *= fmaf(-r, r, r);
+        } else {
+          const float p = fast_exp2(fmaf(z, kLog2e, k.nl));
+          if constexpr (LABEL)
+            v = fmaf(-p, fmaf(k.ebar, z, k.cS), o == yl ? k.gbar + k.k0 : k.k0);
+          else
+            v = fmaf(-p, fmaf(k.ebar, z, k.cS), k.k0);
+          if constexpr (CAP) {
+            const float qz = z * k.inv_cap;
+            v *= fmaf(-qz, qz, 1.f);
+          }
         }
         if constexpr (MASK) v = o < lim ? v : 0.f;
         d[r3] = v;
@@ -969,7 +999,7 @@ __device__ __forceinline__ void dlogits_epilogue(const Acc& acc, const DzToken* 
     // The label's row offset within this lane's rows, or -1.
     const int64_t yo = (int64_t)y - vg0 - wm * 128 - 4 * lh;
     const int yl = (y >= 0 && yo >= 0 && yo < 128) ? (int)yo : -1;
-    const DzCoef k{-c.lse * kLog2e, c.ebar, c.cs, c.gbar, c.k0, kc.cap, kc.cap_k, kc.inv_cap};
+    const DzCoef k = dz_coef(c, kc);
     // Wave-uniform choice of the variant: the label term is needed by few
     // waves, the row mask only in the last vocabulary tile.
     const bool any_label = __builtin_amdgcn_ballot_w64(yl >= 0) != 0;
@@ -1035,7 +1065,7 @@ bwd_dlogits_kernel(DlogitsArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) lds[i] = wm ? sb[i] : sa[i];
   dlogits_epilogue<CAP, true>(
-      acc, a.coef, a.lab, a.N, n0, vg0, a.V, DzCoef{0.f, 0.f, 0.f, 0.f, 0.f, a.cap, a.cap_k, a.inv_cap},
+      acc, a.coef, a.lab, a.N, n0, vg0, a.V, DzCoef{0.f, 0.f, 0.f, 0.f, 0.f, a.cap, a.cap_k, a.inv_cap, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f},
       wm, wn, lane,
       [&](int i, int n, int m0, u32x2_t v) {
         *reinterpret_cast<u32x2_t*>(lds[i] + blk_byte(n, m0 & 31)) = v;
@@ -1127,7 +1157,7 @@ __global__ void __launch_bounds__(kDzThreads) fused_dlogits_kernel(FusedDzArgs a
   }
   // Each lane rewrites only the pieces it read: no barrier between.
   dlogits_epilogue<CAP, false>(
-      acc, a.coef, a.lab, a.rows, n0, vg0, a.V, DzCoef{0.f, 0.f, 0.f, 0.f, 0.f, a.cap, 0.f, a.inv_cap},
+      acc, a.coef, a.lab, a.rows, n0, vg0, a.V, DzCoef{0.f, 0.f, 0.f, 0.f, 0.f, a.cap, 0.f, a.inv_cap, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f},
       wm, wn, lane,
       [&](int i, int n, int m0, u32x2_t v) { *reinterpret_cast<u32x2_t*>(lds + piece(i, n, m0)) = v; },
       rvt);
