@@ -4,12 +4,13 @@
 //           pack (hidden) -> fwd_tile -> fwd_combine (-> fwd_reduce)
 // Backward: bwd_prep (compaction, per-token gradient constants),
 //           zero_ignored_rows, pack (hidden, hidden^T) -> per vocabulary chunk
-//           { pack (weight chunk) -> bwd_dlogits -> bwd_dx (-> dx_finalize
-//             after the last chunk when dH is K-split) -> bwd_dw
-//             (-> dw_reduce) }
+//           { bwd_dlogits (also writing the weight chunk's image for dH) ->
+//             bwd_dx (-> dx_finalize after the last chunk when dH is
+//             K-split) -> bwd_dw (-> dw_reduce) }
 // Fused (gradient in the forward, when the upstream gradients are known
-// before the forward runs): fwd_prep, pack (hidden, hidden^T, weight) ->
-//           per chunk of tokens { fwd_tile storing z' - m (bf16) ->
+// before the forward runs): fwd_prep, pack (hidden, hidden^T) ->
+//           per chunk of tokens { fwd_tile storing z' - m (bf16; the first
+//             chunk also writes the weight's image for dH) ->
 //             fwd_combine (+ gradient constants) -> fused_dlogits ->
 //             bwd_dx (-> dx_finalize) -> bwd_dw (accumulating over chunks) }
 //           (-> fwd_reduce)
@@ -17,7 +18,8 @@
 // results are scattered back to the original token rows.
 //
 // GEMM operands are read in the blocked layout of flce_gemm.hpp (the pack
-// kernels below build it from the caller's row-major tensors, and the
+// kernels below build it from the caller's row-major hidden tensor, the
+// logit tiles copy the weight's image out of their own LDS stages, and the
 // logit-gradient epilogue writes its output directly in it), except the
 // weight as the vocabulary x H operand of the logit tiles, which is read
 // row-contiguous from the caller's [H,V] tensor.
