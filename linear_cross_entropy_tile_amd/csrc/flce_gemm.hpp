@@ -691,14 +691,13 @@ __device__ __forceinline__ u32x2_t quad_transpose_bf16(uint32_t p0, uint32_t p1)
   const uint32_t q0 = lo ? p0 : recv, q1 = lo ? recv : p1;
   const uint32_t o0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)q0, 0xB1, 0xF, 0xF, false);    // [1,0,3,2]
   const uint32_t o1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)q1, 0xB1, 0xF, 0xF, false);
+  // Odd lanes keep their high half and take the partner's high half below it,
+  // even lanes keep their low half and take the partner's low half above it:
+  // one byte permute of {o, q} each (bytes 0-3 of q, 4-7 of o), no branch.
+  const uint32_t bsel = (a & 1) ? 0x03020706u : 0x05040100u;
   u32x2_t r;
-  if (a & 1) {
-    r[0] = (o0 >> 16) | (q0 & 0xFFFF0000u);
-    r[1] = (o1 >> 16) | (q1 & 0xFFFF0000u);
-  } else {
-    r[0] = (q0 & 0xFFFFu) | (o0 << 16);
-    r[1] = (q1 & 0xFFFFu) | (o1 << 16);
-  }
+  r[0] = __builtin_amdgcn_perm(o0, q0, bsel);
+  r[1] = __builtin_amdgcn_perm(o1, q1, bsel);
   return r;
 }
 
