@@ -425,7 +425,7 @@ __device__ __forceinline__ void fwd_tile_body(const FwdTileArgs& a) {
   group_map(xcd_remap(blockIdx.x, tbv * a.VT), tbv, a.VT, a.group, tbl, vt);
   const int tb = a.tb0 + tbl;
   const int lane = threadIdx.x & 63, lh = lane >> 5;
-  const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
+  const int wave = wave_id(), wm = wave & 1, wn = wave >> 1;
   const int64_t n0 = (int64_t)tb * kTile;
 
   Acc acc;
@@ -461,10 +461,15 @@ __device__ __forceinline__ void fwd_tile_body(const FwdTileArgs& a) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     float z[64];
-    if (full)
+    if (full) {
       column_stats<CAP, false>(acc, j, a.cap, a.cap_k, lim, z, m[j], s[j], u[j], zs[j]);
-    else
-      column_stats<CAP, true>(acc, j, a.cap, a.cap_k, lim, z, m[j], s[j], u[j], zs[j]);
+    } else {
+      // lim passes through an empty asm here so that the row tests, needed
+      // by the last vocabulary tile only, are not hoisted into every tile.
+      int l = lim;
+      opaque(l);
+      column_stats<CAP, true>(acc, j, a.cap, a.cap_k, l, z, m[j], s[j], u[j], zs[j]);
+    }
 
     if constexpr (STORE) {
       // Rows m0 .. m0+3 (vocabulary) of token column n: one 8-byte piece.
@@ -1011,10 +1016,13 @@ __device__ __forceinline__ void dlogits_epilogue(const Acc& acc, const DzToken* 
       else
         dz_column<CAP, RAW, false, false>(acc, j, k, yl, lim, n, wm, wn, lane, out, rvt);
     } else {
+      // As in fwd_tile_body: the row tests stay in the last vocabulary tile.
+      int l = lim;
+      opaque(l);
       if (any_label)
-        dz_column<CAP, RAW, true, true>(acc, j, k, yl, lim, n, wm, wn, lane, out, rvt);
+        dz_column<CAP, RAW, true, true>(acc, j, k, yl, l, n, wm, wn, lane, out, rvt);
       else
-        dz_column<CAP, RAW, true, false>(acc, j, k, yl, lim, n, wm, wn, lane, out, rvt);
+        dz_column<CAP, RAW, true, false>(acc, j, k, yl, l, n, wm, wn, lane, out, rvt);
     }
     __builtin_amdgcn_sched_barrier(0);  // one token column at a time
   }
@@ -1037,7 +1045,7 @@ bwd_dlogits_kernel(DlogitsArgs a) {
   int tb, vt;
   group_map(xcd_remap(blockIdx.x, tbv * a.VTc), tbv, a.VTc, a.group, tb, vt);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
+  const int wave = wave_id(), wm = wave & 1, wn = wave >> 1;
   const int64_t n0 = (int64_t)tb * kTile;
   const int64_t vg0 = a.v0 + (int64_t)vt * kTile;  // first vocabulary column of the tile
 
