@@ -100,6 +100,10 @@ WORKLOADS = {
     "odd_vocab": Workload("odd_vocab", 300, 128, 1001, seed=209, weight_std=0.1,
                           ignore="fraction", ignore_fraction=0.1,
                           grad_logprob=("normal",), grad_entropy=("normal",)),
+    # Capped logits (std about 1.1 c) with a ragged last tile in every direction.
+    "odd_capped": Workload("odd_capped", 300, 192, 1001, seed=211, weight_std=0.4,
+                           softcap=5.0, ignore="fraction", ignore_fraction=0.1,
+                           grad_logprob=("normal",), grad_entropy=("normal",)),
     "odd_vocab_dw_split": Workload("odd_vocab_dw_split", 2048, 64, 1002, seed=210,
                                    weight_std=0.15, ignore="fraction", ignore_fraction=0.05,
                                    grad_logprob=("normal",), grad_entropy=("normal",)),

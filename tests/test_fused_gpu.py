@@ -34,6 +34,7 @@ CASES = [
     ("mean_ignore", "mean", 0.02, 1024),       # 4 chunks: dW accumulated in fp32
     ("dw_split", "none", 0.1, 256),            # 16 chunks of one token block each
     ("softcap_saturation", "none", 0.01, 256),  # capped logits near +-c, 2 chunks
+    ("odd_capped", "mean", 0.02, 256),         # capped logits, ragged N and V, 2 chunks
 ]
 
 

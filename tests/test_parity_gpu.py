@@ -17,7 +17,7 @@ from linear_cross_entropy_tile_amd import flce, workloads as W
 pytestmark = pytest.mark.gpu
 
 SMALL = ["tiny", "odd_tails", "all_ignored", "zero_weight", "dw_split", "softcap_saturation",
-         "mean_ignore"]
+         "odd_capped", "mean_ignore"]
 
 _ORACLE_CACHE = {}
 
