@@ -19,6 +19,9 @@ namespace {
 using namespace flce;
 
 // ---- kernel timing hooks --------------------------------------------------------
+// flce_profile_read reports per kind in this order. K_PACK_WEIGHT no longer
+// launches (the weight's dH image is written by the logit tiles themselves);
+// its slot stays so that the indices of the later kinds do not move.
 enum Kind {
   K_FWD_PREP, K_FWD_TILE, K_FWD_COMBINE, K_FWD_REDUCE, K_BWD_PREP, K_BWD_DLOGITS, K_BWD_DX,
   K_BWD_DW, K_DW_REDUCE, K_FILL, K_PACK_WEIGHT, K_PACK_HIDDEN, K_DX_FINALIZE, K_FUSED_TILE,
